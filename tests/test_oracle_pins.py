@@ -1,0 +1,338 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself:
+brute-force definitions on tiny inputs, a hand-worked example, closed forms
+of the layer in degenerate settings, textbook constants, and independent
+PyTorch re-expressions of the gate code the pages print.
+
+CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from mixture_experts_sparse_gate_amd import workloads
+from mixture_experts_sparse_gate_amd.inputs import make_inputs
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute_topk(l, k):
+    """rank(e) = #{e' : l[e'] > l[e] or (l[e'] == l[e] and e' < e)}; the
+    selected list is the experts ordered by rank, rank < k."""
+    N = len(l)
+    ranks = [sum(1 for f in range(N) if l[f] > l[e] or (l[f] == l[e] and f < e)) for e in range(N)]
+    out = [None] * k
+    for e in range(N):
+        if ranks[e] < k:
+            out[ranks[e]] = e
+    return out
+
+
+def brute_slots(idx):
+    """slot(t, j) = #{t' < t : idx[t, j] in idx[t']} (no running state)."""
+    T, k = idx.shape
+    return np.array([[sum(1 for u in range(t) if idx[t, j] in idx[u]) for j in range(k)]
+                     for t in range(T)])
+
+
+@settings(max_examples=60, deadline=None)
+@given(T=st.integers(1, 24), N=st.integers(1, 12), data=st.data())
+def test_topk_matches_rank_definition(T, N, data):
+    k = data.draw(st.integers(1, N))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 31)))
+    # small integer logits force many exact ties; sprinkle signed zeros
+    l = rng.integers(-2, 3, size=(T, N)).astype(np.float64)
+    l[l == 0] = np.where(rng.random((l == 0).sum()) < 0.5, -0.0, 0.0)
+    _, idx = O.top_k(l, k)
+    for t in range(T):
+        assert list(idx[t]) == brute_topk(list(l[t]), k)
+
+
+@settings(max_examples=60, deadline=None)
+@given(T=st.integers(1, 40), N=st.integers(1, 10), data=st.data())
+def test_slots_match_counting_definition(T, N, data):
+    k = data.draw(st.integers(1, N))
+    cf = data.draw(st.sampled_from([0.05, 0.5, 1.0, 1.2, N / k]))
+    rng = np.random.default_rng(data.draw(st.integers(0, 2 ** 31)))
+    idx = np.array([rng.permutation(N)[:k] for _ in range(T)])
+    C = O.capacity(T, k, N, cf)
+    count, kept, off, row_of, tor = O.assign_slots(idx, N, C)
+    slots = brute_slots(idx)
+    A = int(off[-1])
+    # counts, kept, offsets
+    assert list(count) == [int((idx == e).sum()) for e in range(N)]
+    assert all(kept[e] == min(count[e], C) <= C for e in range(N))
+    assert count.sum() == T * k
+    assert A + int((row_of < 0).sum()) == T * k
+    # rows: kept iff slot < C, row = off[e] + slot
+    for t in range(T):
+        for j in range(k):
+            e, s = idx[t, j], slots[t, j]
+            assert row_of[t * k + j] == (off[e] + s if s < C else -1)
+    # token_of_row inverts row_of on kept rows, and each expert segment lists
+    # tokens in strictly increasing order
+    assert sorted(tor.tolist()) == sorted(np.nonzero(row_of >= 0)[0].tolist())
+    for r in range(A):
+        assert row_of[tor[r]] == r
+    for e in range(N):
+        toks = [tor[r] // k for r in range(off[e], off[e + 1])]
+        assert toks == sorted(set(toks))
+
+
+# ---------------------------------------------------------------- hand-worked
+
+def test_hand_worked_routing():
+    g = _load("routing_hand_worked.json")
+    l = np.array(g["logits"], np.float64)
+    l[3, 0] = -0.0
+    assert O.capacity(g["T"], g["k"], g["N"], g["capacity_factor"]) == g["capacity"]
+    tkl, idx = O.top_k(l, g["k"])
+    assert idx.tolist() == g["topk_idx"]
+    assert brute_slots(idx).tolist() == g["slots"]
+    count, kept, off, row_of, tor = O.assign_slots(idx, g["N"], g["capacity"])
+    assert count.tolist() == g["count"]
+    assert kept.tolist() == g["kept"]
+    assert off.tolist() == g["off"]
+    assert row_of.tolist() == g["row_of"]
+    assert tor.tolist() == g["token_of_row"]
+    e = math.e
+    w = O.gate_weights(l, tkl, idx, renorm=True)
+    np.testing.assert_allclose(w[0], [e / (e + 1), 1 / (e + 1)], rtol=1e-15)
+    np.testing.assert_allclose(w[2], [0.5, 0.5], rtol=1e-15)
+    np.testing.assert_allclose(w[5], [1 / (1 + math.exp(-9)), math.exp(-9) / (1 + math.exp(-9))], rtol=1e-14)
+    w0 = O.gate_weights(l, tkl, idx, renorm=False)
+    np.testing.assert_allclose(w0[0], [e ** 2 / (e ** 2 + e + 1), e / (e ** 2 + e + 1)], rtol=1e-15)
+    np.testing.assert_allclose(w0[2], [1 / 3, 1 / 3], rtol=1e-15)
+    z = math.exp(5) + math.exp(-2) + math.exp(4)
+    np.testing.assert_allclose(w0[4], [math.exp(5) / z, math.exp(4) / z], rtol=1e-14)
+
+
+def test_capacity_of_workloads():
+    g = _load("capacity_workloads.json")
+    for name in workloads.WORKLOAD_ORDER:
+        s = workloads.get(name)
+        assert O.capacity(s.T, s.k, s.N, s.capacity_factor) == g[name], name
+
+
+# ---------------------------------------------------------------- closed forms
+
+def _small(gate="softmax", **kw):
+    base = dict(name="pin", T=37, d=24, h=40, N=5, k=2, capacity_factor=1.0, gate=gate,
+                renorm=False, dtype="f32", expert_bias=True)
+    if gate == "cosine":
+        base.update(proj_dim=16, temperature=0.07, zipf_s=1.1)
+    base.update(kw)
+    return workloads.MoESpec(**base)
+
+
+def _torch_ffn(x, W1, W2, b1, b2):
+    """Expert FFN with torch's own Linear/GELU (exact erf form), float64."""
+    x = torch.from_numpy(np.asarray(x, np.float64))
+    hdn = torch.nn.functional.linear(x, torch.from_numpy(W1.astype(np.float64)).T,
+                                     None if b1 is None else torch.from_numpy(b1.astype(np.float64)))
+    hdn = torch.nn.functional.gelu(hdn, approximate="none")
+    out = torch.nn.functional.linear(hdn, torch.from_numpy(W2.astype(np.float64)).T,
+                                     None if b2 is None else torch.from_numpy(b2.astype(np.float64)))
+    return out.numpy()
+
+
+@pytest.mark.parametrize("gate", ["softmax", "noisy", "cosine"])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_all_experts_unlimited_capacity_is_dense_softmax_mixture(gate, renorm):
+    """k = N and C = T: every token reaches every expert, so the layer is
+    sum_e softmax(l)_e FFN_e(x) whichever weight mode is used."""
+    s = _small(gate, k=5, N=5, capacity_factor=1.0, renorm=renorm)
+    inp = make_inputs(s, seed=11)
+    out = O.forward(s, inp)
+    assert out["capacity"] == s.T
+    p = O.softmax(out["logits"])
+    dense = sum(p[:, e:e + 1] * _torch_ffn(inp.x, inp.W1[e], inp.W2[e], inp.b1[e], inp.b2[e])
+                for e in range(s.N))
+    np.testing.assert_allclose(out["y"], dense, rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_one_ffn():
+    """N = 1, k = 1, cf >= 1: weight exactly 1, y = FFN_0(x)."""
+    s = _small("softmax", N=1, k=1, capacity_factor=1.0)
+    inp = make_inputs(s, seed=12)
+    out = O.forward(s, inp)
+    assert np.all(out["topk_w"] == 1.0)
+    np.testing.assert_allclose(out["y"], _torch_ffn(inp.x, inp.W1[0], inp.W2[0], inp.b1[0], inp.b2[0]),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_fully_dropped_tokens_output_zero():
+    s = _small("softmax", T=50, N=3, k=1, capacity_factor=0.2)
+    inp = make_inputs(s, seed=13)
+    out = O.forward(s, inp)
+    k = s.k
+    dropped = [t for t in range(s.T) if all(out["row_of"][t * k + j] < 0 for j in range(k))]
+    assert dropped, "capacity 0.2 must drop tokens"
+    assert np.all(out["y"][dropped] == 0.0)
+    kept_tokens = [t for t in range(s.T) if t not in dropped]
+    e = out["topk_idx"][kept_tokens, 0]
+    ref = np.stack([out["topk_w"][t, 0] * _torch_ffn(inp.x[t:t + 1], inp.W1[ee], inp.W2[ee], inp.b1[ee],
+                                                     inp.b2[ee])[0] for t, ee in zip(kept_tokens, e)])
+    np.testing.assert_allclose(out["y"][kept_tokens], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_sampled_token_outputs_agree_with_full_layer():
+    s = _small("noisy", T=40, N=6, k=3, capacity_factor=0.8, renorm=True)
+    inp = make_inputs(s, seed=14)
+    out = O.forward(s, inp)
+    toks = [0, 3, 17, 39]
+    np.testing.assert_allclose(O.token_outputs(s, inp, out, toks), out["y"][toks], rtol=1e-12, atol=1e-12)
+    rows = [0, 5, int(out["off"][-1]) - 1]
+    H, Y = O.row_outputs(inp, out, rows, s.k)
+    np.testing.assert_allclose(H, out["H"][rows], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Y, out["y_perm"][rows], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- the pages' own code, re-expressed
+
+def test_top1_layer_of_the_pages():
+    """The top-1 layer printed on the PyTorch-v2.6 page: gate Linear (with
+    bias) -> softmax -> max; each expert runs on its masked tokens; the output
+    is scaled by the top-1 probability. No capacity limit (cf = N/k)."""
+    s = _small("softmax", T=60, N=4, k=1, capacity_factor=4.0, expert_bias=True)
+    inp = make_inputs(s, seed=15)
+    gate_b = np.random.default_rng(0).standard_normal(s.N) * 0.3
+    inp.logit_bias = gate_b
+    out = O.forward(s, inp)
+
+    x = torch.from_numpy(inp.x.astype(np.float64))
+    gate_logits = torch.nn.functional.linear(x, torch.from_numpy(inp.w_gate.astype(np.float64)).T,
+                                             torch.from_numpy(gate_b))
+    weights = torch.softmax(gate_logits, dim=-1)
+    top1_w, top1_i = weights.max(dim=-1)
+    final = torch.zeros_like(x)
+    for i in range(s.N):
+        mask = top1_i == i
+        if mask.any():
+            final[mask] = torch.from_numpy(_torch_ffn(x[mask].numpy(), inp.W1[i], inp.W2[i], inp.b1[i], inp.b2[i]))
+    ref = (final * top1_w.unsqueeze(-1)).numpy()
+    assert out["topk_idx"][:, 0].tolist() == top1_i.tolist()
+    np.testing.assert_allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_noisy_topk_gating_of_the_pages():
+    """Noisy top-k gating as printed on the CANN page (section 2.1), with the
+    random normal tensor injected: sparse_gates = zeros.scatter(topk indices,
+    softmax(topk logits))."""
+    s = _small("noisy", T=33, N=7, k=3, renorm=True)
+    inp = make_inputs(s, seed=16)
+    x = torch.from_numpy(inp.x.astype(np.float64))
+    clean = x @ torch.from_numpy(inp.w_gate.astype(np.float64))
+    noise_l = x @ torch.from_numpy(inp.w_noise.astype(np.float64))
+    noisy = clean + torch.from_numpy(inp.noise.astype(np.float64)) * torch.nn.functional.softplus(noise_l)
+    tkl, tki = noisy.topk(s.k, dim=1)
+    ref = torch.zeros_like(noisy).scatter(1, tki, torch.softmax(tkl, dim=1)).numpy()
+    r = O.route(s, inp)
+    np.testing.assert_allclose(r["logits"], noisy.numpy(), rtol=1e-13, atol=1e-13)
+    assert r["topk_idx"].tolist() == tki.tolist()
+    np.testing.assert_allclose(O.sparse_gates(s.N, r["topk_idx"], r["topk_w"]), ref, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- gate pieces
+
+def test_noisy_with_zero_noise_is_plain_gate():
+    s = _small("noisy")
+    inp = make_inputs(s, seed=17)
+    inp.noise = np.zeros_like(inp.noise)
+    l_noisy = O.gate_logits("noisy", inp.x, inp.w_gate, inp.w_noise, inp.noise)
+    l_plain = O.gate_logits("softmax", inp.x, inp.w_gate)
+    assert np.array_equal(l_noisy, l_plain)
+
+
+def test_softplus_against_logaddexp_and_limits():
+    z = np.concatenate([np.linspace(-60, 60, 2001), [-1e4, 1e4, 0.0]])
+    sp = O.softplus(z)
+    np.testing.assert_allclose(sp, np.logaddexp(0.0, z), rtol=1e-15, atol=0)
+    assert np.all(sp[:2001] > 0)  # e^-60 is still representable; softplus(-1e4) underflows to 0
+    assert O.softplus(np.array([0.0]))[0] == pytest.approx(math.log(2.0), rel=1e-16)
+    assert O.softplus(np.array([1e4]))[0] == 1e4
+
+
+def test_cosine_logits_invariants():
+    s = _small("cosine", N=6)
+    inp = make_inputs(s, seed=18)
+    it = s.inv_temperature
+    l = O.cosine_logits(inp.x, inp.proj, inp.expert_emb, it)
+    it32 = float(np.float32(it))
+    assert np.all(np.abs(l) <= it32 * (1 + 1e-12))
+    scale_x = np.abs(np.random.default_rng(1).standard_normal((s.T, 1))) + 0.1
+    np.testing.assert_allclose(O.cosine_logits(inp.x * scale_x, inp.proj, inp.expert_emb, it), l, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.cosine_logits(inp.x, inp.proj, inp.expert_emb.astype(np.float64) * 3.5, it), l, rtol=1e-12, atol=1e-12)
+    # an expert embedding parallel to a token's projection scores exactly 1/tau
+    z0 = inp.x[0].astype(np.float64) @ inp.proj.astype(np.float64)
+    emb = inp.expert_emb.astype(np.float64).copy()
+    emb[2] = 2.0 * z0
+    assert O.cosine_logits(inp.x[:1], inp.proj, emb, it)[0, 2] == pytest.approx(it32, rel=1e-13)
+    # the bias is added after scaling
+    lb = O.gate_logits("cosine", inp.x, proj=inp.proj, expert_emb=inp.expert_emb, inv_temperature=it,
+                       logit_bias=inp.logit_bias)
+    np.testing.assert_allclose(lb - l, np.broadcast_to(inp.logit_bias.astype(np.float64), l.shape), atol=1e-12)
+
+
+def test_gelu_textbook_values():
+    u = np.array([0.0, 1.0, -1.0, 2.0, 40.0, -40.0])
+    g = O.gelu(u)
+    phi1 = 0.8413447460685429  # standard normal CDF at 1
+    phi2 = 0.9772498680518208  # at 2
+    assert g[0] == 0.0
+    assert g[1] == pytest.approx(phi1, rel=1e-15)
+    assert g[2] == pytest.approx(-(1 - phi1), rel=1e-14)
+    assert g[3] == pytest.approx(2 * phi2, rel=1e-15)
+    assert g[4] == 40.0 and abs(g[5]) < 1e-300
+    v = np.linspace(-8, 8, 1601)
+    np.testing.assert_allclose(O.gelu(v) - O.gelu(-v), v, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(O.gelu(v), [x * 0.5 * (1 + math.erf(x / math.sqrt(2))) for x in v], rtol=1e-14, atol=1e-15)
+
+
+def test_zipf_bias_shifts_selection_not_weights():
+    """Adding the same constant to every logit changes neither selection nor
+    softmax weights: the Zipf normalising constant is irrelevant."""
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal((20, 9))
+    a = O.top_k(l, 3)
+    b = O.top_k(l + 7.25, 3)
+    assert np.array_equal(a[1], b[1])
+    for renorm in (False, True):
+        np.testing.assert_allclose(O.gate_weights(l, a[0], a[1], renorm),
+                                   O.gate_weights(l + 7.25, b[0], b[1], renorm), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- inputs
+
+def test_inputs_are_deterministic_and_bf16_exact():
+    s = workloads.scaled(workloads.get("noisy_top2_bf16"), T=64, d=32, h=48)
+    a = make_inputs(s, seed=5)
+    b = make_inputs(s, seed=5)
+    c = make_inputs(s, seed=6)
+    for name in ("x", "w_gate", "w_noise", "noise", "W1", "W2"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+    assert not np.array_equal(a.x, c.x)
+    for name in ("x", "w_gate", "w_noise", "W1", "W2"):
+        bits = getattr(a, name).view(np.uint32)
+        assert np.all(bits & 0xFFFF == 0), name
+    assert not np.all(a.noise.view(np.uint32) & 0xFFFF == 0)  # eps stays fp32
+
+
+def test_bf16_rounding_is_nearest_even():
+    from mixture_experts_sparse_gate_amd.inputs import round_to_bf16
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even (1.0);
+    # 1 + 3*2^-8 is halfway between 1 + 2^-7 and 1 + 2^-6: ties to even (1 + 2^-6)
+    v = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -(1 + 2 ** -8)], np.float32)
+    r = round_to_bf16(v.copy())
+    assert r.tolist() == [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0]
