@@ -1,0 +1,223 @@
+"""Throughput of the sparse-gated MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole layer (gate, dispatch, expert FFN,
+combine) over one batch of seeded synthetic tokens, with every input already
+resident in HBM. The K timed steps are bracketed by torch.cuda.synchronize();
+HIP events recorded on the launch stream between the four stages give each
+stage's average duration inside the same timed region. The roofline object
+describes the expert FFN (the grouped-GEMM kernel, launched twice per step:
+GEMM1+GELU and GEMM2), against the bf16 MFMA peak, or against HBM bandwidth
+when few rows per expert make it weight-streaming bound.
+
+Prints one JSON line. The CPU oracle is timed afterwards on the host cores
+on a bounded sample of the same workload (kind "oracle").
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X published figures
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="noisy_top2_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON with measured HBM bytes per FFN step (from rocprofv3 --pmc)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); see the sharding notes in DESIGN.md", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from mixture_experts_sparse_gate_amd import api, workloads
+    from mixture_experts_sparse_gate_amd.inputs import make_inputs
+
+    spec = workloads.get(args.workload)
+    seed = workloads.WORKLOAD_SEED[args.workload]
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    inp = make_inputs(spec, seed)
+    dev = api.DeviceLayer(inp)
+    torch.cuda.synchronize()
+    log(f"[bench] {spec.name}: inputs ready in {time.perf_counter() - t_gen:.1f}s")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        api.route(dev.desc, **dev.gate_inputs(), logits=None, topk_idx=dev.topk_idx,
+                  topk_w=dev.topk_w, ws=dev.ws)
+        if ev:
+            ev[1].record(stream)
+        api.dispatch(dev.desc, dev.x, dev.topk_idx, dev.expert_count, dev.expert_off, dev.row_of,
+                     dev.token_of_row, dev.x_perm, ws=dev.ws)
+        if ev:
+            ev[2].record(stream)
+        api.expert_ffn(dev.desc, dev.x_perm, dev.expert_off, dev.W1, dev.b1, dev.W2, dev.b2, dev.H,
+                       dev.y_perm)
+        if ev:
+            ev[3].record(stream)
+        api.combine(dev.desc, dev.y_perm, dev.row_of, dev.topk_w, dev.y)
+        if ev:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / K
+    names = ["gate", "dispatch", "expert_ffn", "combine"]
+    stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(K)]))
+                for j, n in enumerate(names)}
+
+    # the whole layer through the single moe_forward entry point, same inputs
+    for _ in range(3):
+        dev.run_forward(inspect=False)
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    for _ in range(K):
+        dev.run_forward(inspect=False)
+    torch.cuda.synchronize()
+    forward_ms = (time.perf_counter() - tf0) * 1e3 / K
+
+    # algorithmic work of one step, from this step's routing
+    off = dev.expert_off.cpu().numpy().astype(np.int64)
+    kept = np.diff(off)
+    A = int(off[-1])
+    U = int((kept > 0).sum())
+    s = 2 if spec.dtype == "bf16" else 4
+    T, d, h, N, k = spec.T, spec.d, spec.h, spec.N, spec.k
+    ffn_flops = 4.0 * A * d * h
+    touched_weight_bytes = float(U) * 2 * d * h * s
+    ffn_s = stage_ms["expert_ffn"] * 1e-3
+    avg_rows = (T * k) / N
+    if avg_rows < 64:  # weight streaming: bound by HBM
+        roof = {"bound": "hbm", "achieved": touched_weight_bytes / ffn_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": ffn_flops / ffn_s / 1e12, "peak": MFMA_PEAK_TFLOPS[spec.dtype],
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["kernel"] = "grouped_gemm_kernel x2 (GEMM1+GELU, GEMM2) per step"
+    roof["traffic"] = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        if tr.get("workload") == spec.name:
+            roof["traffic"] = tr.get("ffn_hbm_bytes_per_step")
+
+    gate_bytes = T * d * s + (2 if spec.gate == "noisy" else 1) * d * N * s * (spec.gate != "cosine") \
+        + (d * spec.proj_dim * s if spec.gate == "cosine" else 0) + T * k * 8
+    disp_bytes = T * d * s + A * d * s + T * k * 8
+    comb_bytes = A * d * s + T * d * s + T * k * 8
+    stages = {
+        "gate": {"ms": stage_ms["gate"], "GB/s": gate_bytes / (stage_ms["gate"] * 1e-3) / 1e9},
+        "dispatch": {"ms": stage_ms["dispatch"], "GB/s": disp_bytes / (stage_ms["dispatch"] * 1e-3) / 1e9},
+        "expert_ffn": {"ms": stage_ms["expert_ffn"], "TFLOP/s": ffn_flops / ffn_s / 1e12,
+                       "touched_weight_GB/s": touched_weight_bytes / ffn_s / 1e9},
+        "combine": {"ms": stage_ms["combine"], "GB/s": comb_bytes / (stage_ms["combine"] * 1e-3) / 1e9},
+    }
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(spec, inp, args.cpu_seconds)
+
+    out = {
+        "metric": "MoE layer fwd tokens/s; expert GEMM % bf16 MFMA peak; dispatch/combine GB/s",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded normal inputs and random-init expert weights)",
+        "config": {"workload": spec.name, "T": T, "d": d, "h": h, "N": N, "k": k, "gate": spec.gate,
+                   "capacity_factor": spec.capacity_factor, "renorm": spec.renorm,
+                   "capacity": int(dev.C), "kept_rows": A, "experts_touched": U},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "moe_forward_ms": forward_ms,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(spec, inp, target_s: float):
+    """The oracle as it is, on the host cores, repeated over the workload (or a
+    token prefix of it when one full pass would take far longer than the target)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import moe_oracle as O
+
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    # estimate: fp64 BLAS at a few tens of GFLOP/s per core
+    T = spec.T
+    est_flops = 4.0 * T * spec.k * spec.d * spec.h
+    sub_T = T
+    if est_flops > 50e9 * blas_threads * target_s:
+        sub_T = max(1, int(T * 50e9 * blas_threads * target_s / est_flops))
+    sub = spec.with_(T=sub_T)
+    sub_inp = inp
+    if sub_T != T:
+        import copy
+        sub_inp = copy.copy(inp)
+        sub_inp.spec = sub
+        sub_inp.x = inp.x[:sub_T]
+        if inp.noise is not None:
+            sub_inp.noise = inp.noise[:sub_T]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.forward(sub, sub_inp)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el / reps * (reps + 1) > 3 * target_s:
+            break
+    what = (f"oracle forward over all {T} tokens" if sub_T == T else
+            f"oracle forward over the first {sub_T} of {T} tokens (same capacity factor)")
+    return {"value": sub_T * reps / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{what}, {reps} repetition(s), {el:.1f} s, fp64 NumPy"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

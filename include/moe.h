@@ -1,0 +1,212 @@
+/*
+ * moe.h — C ABI of the sparse-gated Mixture-of-Experts layer forward pass
+ * on one MI355X (gfx950).
+ *
+ * The layer maps tokens x[T, d] to y[T, d]:
+ *
+ *   1. gate      logits[T, N] from x (plain, noisy or cosine), softmax,
+ *                top-k experts per token and their weights g_i(x)
+ *   2. dispatch  capacity-limited slots in token order; the kept (token,
+ *                expert) pairs are copied into expert-contiguous rows
+ *   3. experts   per expert e, on its rows: GELU(x W1[e] + b1[e]) W2[e] + b2[e]
+ *   4. combine   y[t] = sum over the kept choices j of g_j(x_t) E_j(x_t)
+ *
+ * The layer's definition is the weighted sum of expert outputs on the page
+ * "MoE架构：突破单卡算力瓶颈的密钥" (§1.2); the gate follows the noisy top-k
+ * gating code on "MoE稀疏计算加速技术解析与应用实践" (§2.1) and
+ * "MoE架构：稀疏激活机制如何提升模型计算效率" (§2.1); grouping tokens by expert
+ * before one batched matmul per group follows the latter page's §3.1; the
+ * expert is the Linear-GELU-Linear block of the CANN page's §3.2; the
+ * capacity factor appears there and on the Tutel guide
+ * ("4大技术模块掌握Tutel MoE…", dynamic routing section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous arrays,
+ *    16-byte aligned. "X-dtype" arrays (x, w_gate, w_noise, proj, W1, b1, W2,
+ *    b2, x_perm, H, y_perm, y) hold desc->dtype elements (fp32 or bf16);
+ *    noise, expert_emb, logit_bias, logits and topk_w are always fp32; index
+ *    arrays are int32.
+ *  - The caller owns every buffer, including the workspace. The library
+ *    never allocates, frees or synchronises, and keeps no pointer after a
+ *    call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *    stream) and runs asynchronously; the call does not wait for it.
+ *  - All arguments are checked on the host before anything is enqueued; on
+ *    any error nothing is enqueued, the status says which class of error it
+ *    was and moe_last_error() gives a message (per thread).
+ *  - Results are deterministic: no floating-point atomics anywhere, and a
+ *    fixed summation order in every reduction.
+ *  - Sizes: 1 <= N <= 256, 1 <= k <= min(N, 32), T*k < 2^31, d and h
+ *    multiples of 8 (bf16) or 4 (fp32), cosine proj_dim a multiple of 8 and
+ *    at most 256.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* bad argument: null/misaligned pointer, size out of range */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes below moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* a HIP launch failed; moe_last_error() has the HIP message */
+} moe_status_t;
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum moe_gate {
+  /* logits = x w_gate (+ logit_bias) */
+  MOE_GATE_SOFTMAX = 0,
+  /* logits = x w_gate + noise * softplus(x w_noise) (+ logit_bias),
+     softplus(z) = max(z, 0) + log1p(exp(-|z|)); noise is the caller's
+     standard-normal [T, N] tensor (the pages draw it inside the gate) */
+  MOE_GATE_NOISY = 1,
+  /* z = x proj; logits_j = cos(z, expert_emb_j) * inv_temperature (+ logit_bias_j),
+     both norms clamped below at 1e-12 */
+  MOE_GATE_COSINE = 2
+} moe_gate_t;
+
+typedef struct moe_desc {
+  int64_t T;              /* tokens */
+  int32_t d;              /* model dim */
+  int32_t h;              /* expert hidden dim */
+  int32_t N;              /* experts */
+  int32_t k;              /* experts per token */
+  double capacity_factor; /* > 0; capacity C = min(T, ceil((cf * (T*k)) / N)) in IEEE double */
+  int32_t gate;           /* moe_gate_t */
+  int32_t renorm;         /* 1: weights = softmax over the k selected logits;
+                             0: weights = full softmax probability of each selected expert */
+  int32_t dtype;          /* moe_dtype_t of the X-dtype arrays */
+  int32_t proj_dim;       /* cosine gate: p (columns of proj); else 0 */
+  float inv_temperature;  /* cosine gate: 1/tau; else ignored */
+  int32_t reserved;       /* must be 0 */
+} moe_desc_t;
+
+/* Which entry point a workspace is sized for. */
+typedef enum moe_ws_kind {
+  MOE_WS_ROUTE = 0,
+  MOE_WS_DISPATCH = 1,
+  MOE_WS_FORWARD = 2
+} moe_ws_kind_t;
+
+/* Expert capacity C = min(T, ceil((capacity_factor * (T*k)) / N)), evaluated
+ * in IEEE double; -1 if desc is invalid. Host only. */
+MOE_API int64_t moe_capacity(const moe_desc_t* desc);
+
+/* Row bound R = min(T*k, N*C) of the expert-grouped buffers x_perm, H,
+ * y_perm and token_of_row; -1 if desc is invalid. Host only. */
+MOE_API int64_t moe_rows_bound(const moe_desc_t* desc);
+
+/* Bytes of device workspace `kind` needs (a multiple of 256). Host only. */
+MOE_API moe_status_t moe_workspace_size(const moe_desc_t* desc, moe_ws_kind_t kind, size_t* bytes);
+
+/* Gate: logits, top-k selection and weights.
+ *   x [T, d] X-dtype; w_gate [d, N] (SOFTMAX, NOISY); w_noise [d, N] and
+ *   noise [T, N] fp32 (NOISY); proj [d, p] X-dtype and expert_emb [N, p] fp32
+ *   (COSINE); logit_bias [N] fp32 or NULL (any gate).
+ * Outputs: logits [T, N] fp32 (the final gate logits, after noise and bias)
+ *   or NULL; topk_idx [T, k] int32, experts ordered by logit descending, equal
+ *   logits by ascending expert index (-0.0 equals +0.0); topk_w [T, k] fp32.
+ * Selection compares the fp32 logits; weights are computed in fp32 from them.
+ * ws: MOE_WS_ROUTE bytes (may be NULL when that size is 0). */
+MOE_API moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* w_gate,
+                       const void* w_noise, const float* noise, const void* proj,
+                       const float* expert_emb, const float* logit_bias, float* logits,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Capacity-limited dispatch in token order.
+ *   topk_idx [T, k] int32: each token's experts, distinct, in [0, N); an
+ *   out-of-range entry is treated as dropped.
+ * Outputs: expert_count [N] (demand: choices per expert before the capacity
+ *   limit); expert_off [N+1] (exclusive scan of kept = min(count, C);
+ *   expert_off[N] = A, the number of kept choices); row_of [T*k] (row of
+ *   choice (t, j) in the grouped buffers, or -1 if dropped: the choice is
+ *   kept iff fewer than C earlier tokens chose the same expert);
+ *   token_of_row [R] (t*k + j of each row < A; rows >= A untouched);
+ *   x_perm [R, d] X-dtype (x_perm[row_of[t*k+j]] = x[t] bitwise).
+ * ws: MOE_WS_DISPATCH bytes. */
+MOE_API moe_status_t moe_dispatch(const moe_desc_t* desc, const void* x, const int32_t* topk_idx,
+                          int32_t* expert_count, int32_t* expert_off, int32_t* row_of,
+                          int32_t* token_of_row, void* x_perm, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Grouped expert FFN on the expert-contiguous rows.
+ *   x_perm [R, d]; expert_off [N+1] (device); W1 [N, d, h]; b1 [N, h] or NULL;
+ *   W2 [N, h, d]; b2 [N, d] or NULL. All X-dtype except expert_off.
+ * For e < N and off[e] <= r < off[e+1]:
+ *   H[r]      = GELU(x_perm[r] W1[e] + b1[e])       fp32 accumulation, rounded once to X-dtype
+ *   y_perm[r] = H[r] W2[e] + b2[e]                   fp32 accumulation, rounded once
+ * with GELU(u) = u/2 (1 + erf(u / sqrt 2)). H [R, h] and y_perm [R, d] are
+ * outputs; rows >= expert_off[N] are not written. The grid is sized from R,
+ * so no host read of expert_off is needed. */
+MOE_API moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
+                            const void* W1, const void* b1, const void* W2, const void* b2,
+                            void* H, void* y_perm, void* stream);
+
+/* Gate-weighted combine: y[t] = sum over j with row_of[t*k+j] >= 0, in j order,
+ * of topk_w[t, j] * y_perm[row_of[t*k+j]], accumulated in fp32 and rounded once;
+ * a token with every choice dropped gets a zero row. y [T, d] X-dtype. */
+MOE_API moe_status_t moe_combine(const moe_desc_t* desc, const void* y_perm, const int32_t* row_of,
+                         const float* topk_w, void* y, void* stream);
+
+/* Every tensor of one layer call. Inputs as for moe_route and moe_expert_ffn;
+ * y is the output. The inspection outputs may each be NULL, in which case the
+ * value lives only in the workspace. */
+typedef struct moe_layer_tensors {
+  const void* x;
+  const void* w_gate;
+  const void* w_noise;
+  const float* noise;
+  const void* proj;
+  const float* expert_emb;
+  const float* logit_bias;
+  const void* W1;
+  const void* b1;
+  const void* W2;
+  const void* b2;
+  void* y;
+  /* optional inspection outputs */
+  float* logits;          /* [T, N] */
+  int32_t* topk_idx;      /* [T, k] */
+  float* topk_w;          /* [T, k] */
+  int32_t* expert_count;  /* [N]   */
+  int32_t* expert_off;    /* [N+1] */
+  int32_t* row_of;        /* [T*k] */
+  int32_t* token_of_row;  /* [R]   */
+} moe_layer_tensors_t;
+
+/* The whole layer: route, dispatch, expert FFN and combine, enqueued on one
+ * stream with no host synchronisation (so it can be captured in a HIP
+ * graph). ws: MOE_WS_FORWARD bytes; it holds x_perm, H, y_perm and every
+ * routing array the caller does not ask for. */
+MOE_API moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* tensors, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Static name of a status code. */
+MOE_API const char* moe_status_string(moe_status_t status);
+
+/* Message of this thread's last failed call ("" if none). */
+MOE_API const char* moe_last_error(void);
+
+/* Build identification, e.g. "moe gfx950 <date>". */
+MOE_API const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,188 @@
+"""Python binding of the C ABI in include/moe.h.
+
+Same entry points, same argument order. This module only marshals
+arguments: torch tensors supply device pointers, None becomes NULL, and work
+is enqueued on torch's current HIP stream. Every step of the layer runs in
+the HIP kernels of libmoe_gfx950.so; a status other than MOE_OK raises
+RuntimeError with the library's message.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MoeDesc, MoeLayerTensors
+from .workloads import MoESpec
+
+_GATES = {"softmax": _lib.MOE_GATE_SOFTMAX, "noisy": _lib.MOE_GATE_NOISY, "cosine": _lib.MOE_GATE_COSINE}
+_DTYPES = {"f32": _lib.MOE_F32, "bf16": _lib.MOE_BF16}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def desc_from_spec(spec: MoESpec) -> MoeDesc:
+    return MoeDesc(T=spec.T, d=spec.d, h=spec.h, N=spec.N, k=spec.k,
+                   capacity_factor=float(spec.capacity_factor), gate=_GATES[spec.gate],
+                   renorm=int(bool(spec.renorm)), dtype=_DTYPES[spec.dtype],
+                   proj_dim=int(spec.proj_dim), inv_temperature=float(spec.inv_temperature),
+                   reserved=0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch.Tensor or None, got {type(t)}")
+    if t.device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != _lib.MOE_OK:
+        lib = _lib.load()
+        raise RuntimeError(f"{what}: {lib.moe_status_string(status).decode()}: "
+                           f"{lib.moe_last_error().decode()}")
+
+
+def capacity(desc: MoeDesc) -> int:
+    return int(_lib.load().moe_capacity(ctypes.byref(desc)))
+
+
+def rows_bound(desc: MoeDesc) -> int:
+    return int(_lib.load().moe_rows_bound(ctypes.byref(desc)))
+
+
+def workspace_size(desc: MoeDesc, kind: int = _lib.MOE_WS_FORWARD) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.load().moe_workspace_size(ctypes.byref(desc), kind, ctypes.byref(n)), "moe_workspace_size")
+    return int(n.value)
+
+
+def workspace(desc: MoeDesc, kind: int = _lib.MOE_WS_FORWARD, device="cuda") -> torch.Tensor:
+    """A device buffer of moe_workspace_size bytes (torch's allocator aligns to 256 B or more)."""
+    return torch.empty(max(workspace_size(desc, kind), 1), dtype=torch.uint8, device=device)
+
+
+def route(desc, x, w_gate=None, w_noise=None, noise=None, proj=None, expert_emb=None,
+          logit_bias=None, logits=None, topk_idx=None, topk_w=None, ws=None, stream=None):
+    st = _lib.load().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_gate), _ptr(w_noise), _ptr(noise),
+                               _ptr(proj), _ptr(expert_emb), _ptr(logit_bias), _ptr(logits),
+                               _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_route")
+
+
+def dispatch(desc, x, topk_idx, expert_count, expert_off, row_of, token_of_row, x_perm, ws=None,
+             stream=None):
+    st = _lib.load().moe_dispatch(ctypes.byref(desc), _ptr(x), _ptr(topk_idx), _ptr(expert_count),
+                                  _ptr(expert_off), _ptr(row_of), _ptr(token_of_row), _ptr(x_perm),
+                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _check(st, "moe_dispatch")
+
+
+def expert_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, stream=None):
+    st = _lib.load().moe_expert_ffn(ctypes.byref(desc), _ptr(x_perm), _ptr(expert_off), _ptr(W1),
+                                    _ptr(b1), _ptr(W2), _ptr(b2), _ptr(H), _ptr(y_perm),
+                                    _stream(stream))
+    _check(st, "moe_expert_ffn")
+
+
+def combine(desc, y_perm, row_of, topk_w, y, stream=None):
+    st = _lib.load().moe_combine(ctypes.byref(desc), _ptr(y_perm), _ptr(row_of), _ptr(topk_w), _ptr(y),
+                                 _stream(stream))
+    _check(st, "moe_combine")
+
+
+def forward(desc, tensors: dict, ws: torch.Tensor, stream=None):
+    """tensors: the fields of moe_layer_tensors_t by name (missing = NULL)."""
+    unknown = set(tensors) - {f for f, _ in MoeLayerTensors._fields_}
+    if unknown:
+        raise KeyError(f"unknown tensor names {sorted(unknown)}")
+    lt = MoeLayerTensors(**{k: _ptr(v) for k, v in tensors.items() if v is not None})
+    st = _lib.load().moe_forward(ctypes.byref(desc), ctypes.byref(lt), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_forward")
+
+
+# ---------------------------------------------------------------- convenience
+
+class DeviceLayer:
+    """Device copies of one layer's inputs (from a MoEInputs) plus the
+    output buffers of every stage, ready to pass to the entry points."""
+
+    def __init__(self, inp, device="cuda"):
+        spec = inp.spec
+        self.spec = spec
+        self.desc = desc_from_spec(spec)
+        dt = TORCH_DTYPE[spec.dtype]
+
+        def up(a, dtype=dt):
+            if a is None:
+                return None
+            return torch.from_numpy(a).to(device=device).to(dtype).contiguous()
+
+        self.x = up(inp.x)
+        self.w_gate = up(inp.w_gate)
+        self.w_noise = up(inp.w_noise)
+        self.noise = up(inp.noise, torch.float32)
+        self.proj = up(inp.proj)
+        self.expert_emb = up(inp.expert_emb, torch.float32)
+        self.logit_bias = up(inp.logit_bias, torch.float32)
+        self.W1 = up(inp.W1)
+        self.W2 = up(inp.W2)
+        self.b1 = up(inp.b1)
+        self.b2 = up(inp.b2)
+        T, N, k, d, h = spec.T, spec.N, spec.k, spec.d, spec.h
+        R = rows_bound(self.desc)
+        self.R = R
+        self.C = capacity(self.desc)
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.logits = torch.empty(T, N, **f32)
+        self.topk_idx = torch.empty(T, k, **i32)
+        self.topk_w = torch.empty(T, k, **f32)
+        self.expert_count = torch.empty(N, **i32)
+        self.expert_off = torch.empty(N + 1, **i32)
+        self.row_of = torch.empty(T * k, **i32)
+        self.token_of_row = torch.full((max(R, 1),), -1, **i32)
+        self.x_perm = torch.zeros(max(R, 1), d, dtype=dt, device=device)
+        self.H = torch.zeros(max(R, 1), h, dtype=dt, device=device)
+        self.y_perm = torch.zeros(max(R, 1), d, dtype=dt, device=device)
+        self.y = torch.empty(T, d, dtype=dt, device=device)
+        self.ws = workspace(self.desc, _lib.MOE_WS_FORWARD, device)
+
+    def gate_inputs(self):
+        return dict(x=self.x, w_gate=self.w_gate, w_noise=self.w_noise, noise=self.noise, proj=self.proj,
+                    expert_emb=self.expert_emb, logit_bias=self.logit_bias)
+
+    def run_stages(self, stream=None):
+        route(self.desc, **self.gate_inputs(), logits=self.logits, topk_idx=self.topk_idx,
+              topk_w=self.topk_w, ws=self.ws, stream=stream)
+        dispatch(self.desc, self.x, self.topk_idx, self.expert_count, self.expert_off, self.row_of,
+                 self.token_of_row, self.x_perm, ws=self.ws, stream=stream)
+        expert_ffn(self.desc, self.x_perm, self.expert_off, self.W1, self.b1, self.W2, self.b2, self.H,
+                   self.y_perm, stream=stream)
+        combine(self.desc, self.y_perm, self.row_of, self.topk_w, self.y, stream=stream)
+
+    def layer_tensors(self, inspect: bool = True) -> dict:
+        t = dict(**self.gate_inputs(), W1=self.W1, b1=self.b1, W2=self.W2, b2=self.b2, y=self.y)
+        if inspect:
+            t.update(logits=self.logits, topk_idx=self.topk_idx, topk_w=self.topk_w,
+                     expert_count=self.expert_count, expert_off=self.expert_off, row_of=self.row_of,
+                     token_of_row=self.token_of_row)
+        return t
+
+    def run_forward(self, inspect: bool = True, stream=None):
+        forward(self.desc, self.layer_tensors(inspect), self.ws, stream=stream)

@@ -1,0 +1,441 @@
+// C ABI of the MoE layer (declared in include/moe.h): argument checks on the
+// host, workspace carve-up and the launch sequence. Nothing here allocates,
+// frees or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status_t hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return MOE_OK;
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int elem_bytes(const moe_desc_t* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
+int chunk_elems(const moe_desc_t* d) { return d->dtype == MOE_BF16 ? 8 : 4; }
+
+int64_t capacity_of(const moe_desc_t* d) {
+  const double c = ceil((d->capacity_factor * (double)(d->T * d->k)) / (double)d->N);
+  return c < (double)d->T ? (int64_t)c : d->T;
+}
+
+int64_t rows_bound_of(const moe_desc_t* d) {
+  const int64_t a = d->T * d->k, b = (int64_t)d->N * capacity_of(d);
+  return a < b ? a : b;
+}
+
+int ntiles_of(const moe_desc_t* d) {
+  return (int)((d->T + moe::kDispatchTile - 1) / moe::kDispatchTile);
+}
+
+moe_status_t check_desc(const moe_desc_t* d) {
+  if (!d) return fail(MOE_ERR_INVALID, "desc is NULL");
+  if (d->reserved != 0) return fail(MOE_ERR_INVALID, "desc->reserved must be 0");
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID, "dtype %d is not MOE_F32 or MOE_BF16", d->dtype);
+  if (d->gate < MOE_GATE_SOFTMAX || d->gate > MOE_GATE_COSINE)
+    return fail(MOE_ERR_INVALID, "gate %d is not a moe_gate_t", d->gate);
+  if (d->renorm != 0 && d->renorm != 1) return fail(MOE_ERR_INVALID, "renorm must be 0 or 1");
+  if (d->T < 1) return fail(MOE_ERR_INVALID, "T = %lld must be >= 1", (long long)d->T);
+  if (d->N < 1 || d->N > 256) return fail(MOE_ERR_INVALID, "N = %d must be in [1, 256]", d->N);
+  if (d->k < 1 || d->k > d->N || d->k > 32)
+    return fail(MOE_ERR_INVALID, "k = %d must be in [1, min(N, 32)]", d->k);
+  if (d->T * (int64_t)d->k >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_INVALID, "T*k must be below 2^31");
+  if (!(d->capacity_factor > 0.0) || !isfinite(d->capacity_factor))
+    return fail(MOE_ERR_INVALID, "capacity_factor must be finite and > 0");
+  const int ce = chunk_elems(d);
+  if (d->d < 1 || d->d % ce) return fail(MOE_ERR_INVALID, "d = %d must be a positive multiple of %d", d->d, ce);
+  if (d->h < 1 || d->h % ce) return fail(MOE_ERR_INVALID, "h = %d must be a positive multiple of %d", d->h, ce);
+  if (d->gate == MOE_GATE_COSINE) {
+    if (d->proj_dim < 8 || d->proj_dim > 256 || d->proj_dim % 8)
+      return fail(MOE_ERR_INVALID, "proj_dim = %d must be a multiple of 8 in [8, 256]", d->proj_dim);
+    if (!isfinite(d->inv_temperature))
+      return fail(MOE_ERR_INVALID, "inv_temperature must be finite");
+  }
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status_t need(const void* p, const char* name, size_t align) {
+  if (!p) return fail(MOE_ERR_INVALID, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(MOE_ERR_INVALID, "%s is not %zu-byte aligned", name, align);
+  return MOE_OK;
+}
+
+moe_status_t maybe(const void* p, const char* name, size_t align) {
+  if (p && !aligned(p, align)) return fail(MOE_ERR_INVALID, "%s is not %zu-byte aligned", name, align);
+  return MOE_OK;
+}
+
+#define TRY(expr)                       \
+  do {                                  \
+    moe_status_t st__ = (expr);         \
+    if (st__ != MOE_OK) return st__;    \
+  } while (0)
+
+// ---------------------------------------------------------------- workspace
+
+struct RouteWs {
+  size_t z, logits, bytes;
+};
+RouteWs route_ws(const moe_desc_t* d) {
+  RouteWs w{};
+  size_t o = 0;
+  w.z = o;
+  if (d->gate == MOE_GATE_COSINE) o += align_up((size_t)d->T * d->proj_dim * 4);
+  w.logits = o;
+  o += align_up((size_t)d->T * d->N * 4);
+  w.bytes = o;
+  return w;
+}
+
+struct DispatchWs {
+  size_t tile_counts, tile_base, bytes;
+};
+DispatchWs dispatch_ws(const moe_desc_t* d) {
+  DispatchWs w{};
+  const size_t t = (size_t)ntiles_of(d) * d->N * 4;
+  w.tile_counts = 0;
+  w.tile_base = align_up(t);
+  w.bytes = 2 * align_up(t);
+  return w;
+}
+
+struct ForwardWs {
+  size_t route, dispatch, topk_idx, topk_w, count, off, row_of, token_of_row, x_perm, H, y_perm,
+      bytes;
+};
+ForwardWs forward_ws(const moe_desc_t* d) {
+  ForwardWs w{};
+  const size_t Tk = (size_t)d->T * d->k, R = (size_t)rows_bound_of(d), s = elem_bytes(d);
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    const size_t at = o;
+    o += align_up(n);
+    return at;
+  };
+  w.route = take(route_ws(d).bytes);
+  w.dispatch = take(dispatch_ws(d).bytes);
+  w.topk_idx = take(Tk * 4);
+  w.topk_w = take(Tk * 4);
+  w.count = take((size_t)d->N * 4);
+  w.off = take((size_t)(d->N + 1) * 4);
+  w.row_of = take(Tk * 4);
+  w.token_of_row = take(R * 4);
+  w.x_perm = take(R * d->d * s);
+  w.H = take(R * d->h * s);
+  w.y_perm = take(R * d->d * s);
+  w.bytes = o;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// ---------------------------------------------------------------- stages (arguments checked)
+
+moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, const void* w_noise,
+                      const float* noise, const void* proj, const float* emb, const float* bias,
+                      float* logits, int32_t* idx, float* w, void* ws, hipStream_t s) {
+  const RouteWs rw = route_ws(d);
+  const bool bf = d->dtype == MOE_BF16;
+  if (d->gate == MOE_GATE_COSINE) {
+    float* z = at<float>(ws, rw.z);
+    moe::GemmParams g{};
+    g.A = x;
+    g.B = proj;
+    g.C = z;
+    g.lda = d->d;
+    g.ldc = d->proj_dim;
+    g.M = (int)d->T;
+    g.groups = 1;
+    g.K = d->d;
+    g.Ncols = d->proj_dim;
+    TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kProjF32, bf, (int)d->T, s),
+                   "cosine projection"));
+    moe::CosineParams c{};
+    c.z = z;
+    c.emb = emb;
+    c.logit_bias = bias;
+    c.inv_temperature = d->inv_temperature;
+    c.logits = logits;
+    c.topk_idx = idx;
+    c.topk_w = w;
+    c.T = (int)d->T;
+    c.p = d->proj_dim;
+    c.N = d->N;
+    c.k = d->k;
+    c.renorm = d->renorm;
+    return hip_status(moe::launch_cosine_select(c, s), "cosine gate");
+  }
+  moe::GateParams g{};
+  g.x = x;
+  g.w_gate = w_gate;
+  g.w_noise = w_noise;
+  g.noise = noise;
+  g.logit_bias = bias;
+  g.logits = logits ? logits : at<float>(ws, rw.logits);
+  g.topk_idx = idx;
+  g.topk_w = w;
+  g.T = (int)d->T;
+  g.d = d->d;
+  g.N = d->N;
+  g.k = d->k;
+  g.renorm = d->renorm;
+  return hip_status(moe::launch_gate_plain_noisy(g, bf, d->gate == MOE_GATE_NOISY, s), "gate");
+}
+
+moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx, int32_t* count,
+                         int32_t* off, int32_t* row_of, int32_t* token_of_row, void* x_perm,
+                         void* ws, hipStream_t s) {
+  const DispatchWs dw = dispatch_ws(d);
+  moe::DispatchParams p{};
+  p.x = x;
+  p.topk_idx = idx;
+  p.tile_counts = at<int32_t>(ws, dw.tile_counts);
+  p.tile_base = at<int32_t>(ws, dw.tile_base);
+  p.expert_count = count;
+  p.expert_off = off;
+  p.row_of = row_of;
+  p.token_of_row = token_of_row;
+  p.x_perm = x_perm;
+  p.T = (int)d->T;
+  p.d = d->d;
+  p.N = d->N;
+  p.k = d->k;
+  p.C = (int)capacity_of(d);
+  p.elem_bytes = elem_bytes(d);
+  return hip_status(moe::launch_dispatch(p, s), "dispatch");
+}
+
+moe_status_t do_ffn(const moe_desc_t* d, const void* x_perm, const int32_t* off, const void* W1,
+                    const void* b1, const void* W2, const void* b2, void* H, void* y_perm,
+                    hipStream_t s) {
+  const bool bf = d->dtype == MOE_BF16;
+  const int R = (int)rows_bound_of(d);
+  const int avg_rows = (int)((d->T * d->k) / d->N);
+  moe::GemmParams g{};
+  g.A = x_perm;
+  g.B = W1;
+  g.bias = b1;
+  g.C = H;
+  g.seg = off;
+  g.lda = d->d;
+  g.ldc = d->h;
+  g.strideB = (int64_t)d->d * d->h;
+  g.strideBias = d->h;
+  g.M = R;
+  g.groups = d->N;
+  g.K = d->d;
+  g.Ncols = d->h;
+  TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn1Gelu, bf, avg_rows, s),
+                 "expert GEMM1"));
+  g.A = H;
+  g.B = W2;
+  g.bias = b2;
+  g.C = y_perm;
+  g.lda = d->h;
+  g.ldc = d->d;
+  g.strideB = (int64_t)d->h * d->d;
+  g.strideBias = d->d;
+  g.K = d->h;
+  g.Ncols = d->d;
+  return hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn2, bf, avg_rows, s),
+                    "expert GEMM2");
+}
+
+moe_status_t do_combine(const moe_desc_t* d, const void* y_perm, const int32_t* row_of,
+                        const float* w, void* y, hipStream_t s) {
+  moe::CombineParams c{};
+  c.y_perm = y_perm;
+  c.row_of = row_of;
+  c.topk_w = w;
+  c.y = y;
+  c.T = (int)d->T;
+  c.d = d->d;
+  c.k = d->k;
+  c.R = (int)rows_bound_of(d);
+  return hip_status(moe::launch_combine(c, d->dtype == MOE_BF16, s), "combine");
+}
+
+moe_status_t check_gate_inputs(const moe_desc_t* d, const void* x, const void* w_gate,
+                               const void* w_noise, const float* noise, const void* proj,
+                               const float* emb, const float* bias) {
+  TRY(need(x, "x", 16));
+  if (d->gate == MOE_GATE_SOFTMAX || d->gate == MOE_GATE_NOISY) TRY(need(w_gate, "w_gate", 16));
+  if (d->gate == MOE_GATE_NOISY) {
+    TRY(need(w_noise, "w_noise", 16));
+    TRY(need(noise, "noise", 4));
+  }
+  if (d->gate == MOE_GATE_COSINE) {
+    TRY(need(proj, "proj", 16));
+    TRY(need(emb, "expert_emb", 4));
+  }
+  TRY(maybe(bias, "logit_bias", 4));
+  return MOE_OK;
+}
+
+moe_status_t check_ws(void* ws, size_t have, size_t want) {
+  if (want == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", want);
+  if (!aligned(ws, kAlign)) return fail(MOE_ERR_INVALID, "workspace is not %zu-byte aligned", kAlign);
+  if (have < want) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, want);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(const moe_desc_t* desc) {
+  if (check_desc(desc) != MOE_OK) return -1;
+  return capacity_of(desc);
+}
+
+int64_t moe_rows_bound(const moe_desc_t* desc) {
+  if (check_desc(desc) != MOE_OK) return -1;
+  return rows_bound_of(desc);
+}
+
+moe_status_t moe_workspace_size(const moe_desc_t* desc, moe_ws_kind_t kind, size_t* bytes) {
+  TRY(check_desc(desc));
+  if (!bytes) return fail(MOE_ERR_INVALID, "bytes is NULL");
+  switch (kind) {
+    case MOE_WS_ROUTE: *bytes = route_ws(desc).bytes; return MOE_OK;
+    case MOE_WS_DISPATCH: *bytes = dispatch_ws(desc).bytes; return MOE_OK;
+    case MOE_WS_FORWARD: *bytes = forward_ws(desc).bytes; return MOE_OK;
+  }
+  return fail(MOE_ERR_INVALID, "unknown workspace kind %d", (int)kind);
+}
+
+moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void* w_gate,
+                       const void* w_noise, const float* noise, const void* proj,
+                       const float* expert_emb, const float* logit_bias, float* logits,
+                       int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_desc(desc));
+  TRY(check_gate_inputs(desc, x, w_gate, w_noise, noise, proj, expert_emb, logit_bias));
+  TRY(maybe(logits, "logits", 4));
+  TRY(need(topk_idx, "topk_idx", 4));
+  TRY(need(topk_w, "topk_w", 4));
+  TRY(check_ws(ws, ws_bytes, route_ws(desc).bytes));
+  return do_route(desc, x, w_gate, w_noise, noise, proj, expert_emb, logit_bias, logits, topk_idx,
+                  topk_w, ws, (hipStream_t)stream);
+}
+
+moe_status_t moe_dispatch(const moe_desc_t* desc, const void* x, const int32_t* topk_idx,
+                          int32_t* expert_count, int32_t* expert_off, int32_t* row_of,
+                          int32_t* token_of_row, void* x_perm, void* ws, size_t ws_bytes,
+                          void* stream) {
+  TRY(check_desc(desc));
+  TRY(need(x, "x", 16));
+  TRY(need(topk_idx, "topk_idx", 4));
+  TRY(need(expert_count, "expert_count", 4));
+  TRY(need(expert_off, "expert_off", 4));
+  TRY(need(row_of, "row_of", 4));
+  TRY(need(token_of_row, "token_of_row", 4));
+  TRY(need(x_perm, "x_perm", 16));
+  TRY(check_ws(ws, ws_bytes, dispatch_ws(desc).bytes));
+  return do_dispatch(desc, x, topk_idx, expert_count, expert_off, row_of, token_of_row, x_perm, ws,
+                     (hipStream_t)stream);
+}
+
+moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
+                            const void* W1, const void* b1, const void* W2, const void* b2,
+                            void* H, void* y_perm, void* stream) {
+  TRY(check_desc(desc));
+  TRY(need(x_perm, "x_perm", 16));
+  TRY(need(expert_off, "expert_off", 4));
+  TRY(need(W1, "W1", 16));
+  TRY(need(W2, "W2", 16));
+  TRY(maybe(b1, "b1", 4));
+  TRY(maybe(b2, "b2", 4));
+  TRY(need(H, "H", 16));
+  TRY(need(y_perm, "y_perm", 16));
+  return do_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, (hipStream_t)stream);
+}
+
+moe_status_t moe_combine(const moe_desc_t* desc, const void* y_perm, const int32_t* row_of,
+                         const float* topk_w, void* y, void* stream) {
+  TRY(check_desc(desc));
+  TRY(need(y_perm, "y_perm", 16));
+  TRY(need(row_of, "row_of", 4));
+  TRY(need(topk_w, "topk_w", 4));
+  TRY(need(y, "y", 16));
+  return do_combine(desc, y_perm, row_of, topk_w, y, (hipStream_t)stream);
+}
+
+moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, void* ws,
+                         size_t ws_bytes, void* stream) {
+  TRY(check_desc(desc));
+  if (!t) return fail(MOE_ERR_INVALID, "tensors is NULL");
+  TRY(check_gate_inputs(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb,
+                        t->logit_bias));
+  TRY(need(t->W1, "W1", 16));
+  TRY(need(t->W2, "W2", 16));
+  TRY(maybe(t->b1, "b1", 4));
+  TRY(maybe(t->b2, "b2", 4));
+  TRY(need(t->y, "y", 16));
+  TRY(maybe(t->logits, "logits", 4));
+  TRY(maybe(t->topk_idx, "topk_idx", 4));
+  TRY(maybe(t->topk_w, "topk_w", 4));
+  TRY(maybe(t->expert_count, "expert_count", 4));
+  TRY(maybe(t->expert_off, "expert_off", 4));
+  TRY(maybe(t->row_of, "row_of", 4));
+  TRY(maybe(t->token_of_row, "token_of_row", 4));
+  const ForwardWs fw = forward_ws(desc);
+  TRY(check_ws(ws, ws_bytes, fw.bytes));
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* idx = t->topk_idx ? t->topk_idx : at<int32_t>(ws, fw.topk_idx);
+  float* w = t->topk_w ? t->topk_w : at<float>(ws, fw.topk_w);
+  int32_t* count = t->expert_count ? t->expert_count : at<int32_t>(ws, fw.count);
+  int32_t* off = t->expert_off ? t->expert_off : at<int32_t>(ws, fw.off);
+  int32_t* row_of = t->row_of ? t->row_of : at<int32_t>(ws, fw.row_of);
+  int32_t* tor = t->token_of_row ? t->token_of_row : at<int32_t>(ws, fw.token_of_row);
+  void* x_perm = at<char>(ws, fw.x_perm);
+  void* H = at<char>(ws, fw.H);
+  void* y_perm = at<char>(ws, fw.y_perm);
+  TRY(do_route(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb, t->logit_bias,
+               t->logits, idx, w, at<char>(ws, fw.route), s));
+  TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, x_perm, at<char>(ws, fw.dispatch), s));
+  TRY(do_ffn(desc, x_perm, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, s));
+  return do_combine(desc, y_perm, row_of, w, t->y, s);
+}
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return g_last_error; }
+
+const char* moe_version(void) { return "moe gfx950 " __DATE__; }
+
+}  // extern "C"

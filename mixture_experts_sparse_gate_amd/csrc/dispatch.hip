@@ -1,0 +1,190 @@
+// Dispatch: capacity-limited slots in token order and the permute into
+// expert-contiguous rows (grouping tokens by expert before one batched
+// matmul per group, as on "MoE架构：稀疏激活机制如何提升模型计算效率" §3.1;
+// capacity_factor on "MoE稀疏计算加速技术解析与应用实践" §3.2).
+//
+// A choice (t, j) of expert e takes slot #{t' < t : e in topk_idx[t']}; it
+// is kept iff that slot is below the capacity C, and then lands in row
+// off[e] + slot, off being the exclusive scan of kept = min(count, C).
+//
+// Three small index kernels compute this deterministically without any
+// global atomics:
+//   count  one block per tile of kDispatchTile tokens: per-expert histogram
+//          of the tile in LDS (integer adds, so order does not matter)
+//   scan   one block: per expert, exclusive scan of the tile counts over the
+//          tiles (the tile's starting slot), totals, kept, offsets
+//   slots  one block per tile: in each 64-token wave chunk a lane's rank
+//          among earlier lanes with the same expert is a popcount of an LDS
+//          bitmask; chunk prefixes come from the other waves' masks and a
+//          running per-expert count
+// and a fourth kernel, permute, copies each token's row of x once into its
+// kept rows with 16-byte loads and stores (one wave per token).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kWaves = kBlock / kWave;
+constexpr int kMaxN = 256;
+
+__global__ __launch_bounds__(kBlock) void count_kernel(DispatchParams p) {
+  __shared__ int hist[kMaxN];
+  const int N = p.N, k = p.k;
+  for (int e = threadIdx.x; e < N; e += kBlock) hist[e] = 0;
+  __syncthreads();
+  const int t_lo = blockIdx.x * kDispatchTile;
+  const int t_hi = min(p.T, t_lo + kDispatchTile);
+  for (int i = t_lo * k + threadIdx.x; i < t_hi * k; i += kBlock) {
+    const int e = p.topk_idx[i];
+    if ((unsigned)e < (unsigned)N) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += kBlock) p.tile_counts[blockIdx.x * N + e] = hist[e];
+}
+
+__global__ __launch_bounds__(kBlock) void scan_kernel(DispatchParams p, int ntiles) {
+  __shared__ int kept_s[kMaxN];
+  const int N = p.N;
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < N) {
+    for (int t = 0; t < ntiles; ++t) {
+      const int c = p.tile_counts[t * N + e];
+      p.tile_base[t * N + e] = total;
+      total += c;
+    }
+    p.expert_count[e] = total;
+    kept_s[e] = min(total, p.C);
+  }
+  __syncthreads();
+  // exclusive scan of kept over experts (N <= 256 values; wave 0 does it)
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int v[kMaxN / kWave];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxN / kWave; ++i) {
+      const int ee = lane * (kMaxN / kWave) + i;
+      v[i] = ee < N ? kept_s[ee] : 0;
+      sum += v[i];
+    }
+    // inclusive scan of the per-lane sums
+    int inc = sum;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int o = __shfl_up(inc, m, kWave);
+      if (lane >= m) inc += o;
+    }
+    int run = inc - sum;
+#pragma unroll
+    for (int i = 0; i < kMaxN / kWave; ++i) {
+      const int ee = lane * (kMaxN / kWave) + i;
+      if (ee < N) p.expert_off[ee] = run;
+      run += v[i];
+    }
+    if (lane == kWave - 1) p.expert_off[N] = inc;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void slots_kernel(DispatchParams p) {
+  __shared__ unsigned long long mask[kWaves][kMaxN];
+  __shared__ int running[kMaxN];
+  __shared__ int off_s[kMaxN];
+  const int N = p.N, k = p.k, C = p.C;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  for (int e = threadIdx.x; e < N; e += kBlock) {
+    running[e] = p.tile_base[blockIdx.x * N + e];
+    off_s[e] = p.expert_off[e];
+  }
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const int t_lo = blockIdx.x * kDispatchTile;
+  for (int r0 = t_lo; r0 < t_lo + kDispatchTile && r0 < p.T; r0 += kBlock) {
+    for (int i = threadIdx.x; i < kWaves * N; i += kBlock) mask[i / N][i % N] = 0ull;
+    __syncthreads();
+    const int t = r0 + threadIdx.x;
+    const bool live = t < p.T;
+    if (live) {
+      for (int j = 0; j < k; ++j) {
+        const int e = p.topk_idx[t * k + j];
+        if ((unsigned)e < (unsigned)N) atomicOr(&mask[wave][e], 1ull << lane);
+      }
+    }
+    __syncthreads();
+    if (live) {
+      for (int j = 0; j < k; ++j) {
+        const int e = p.topk_idx[t * k + j];
+        int row = -1;
+        if ((unsigned)e < (unsigned)N) {
+          int slot = running[e] + __popcll(mask[wave][e] & below);
+          for (int w = 0; w < wave; ++w) slot += __popcll(mask[w][e]);
+          if (slot < C) {
+            row = off_s[e] + slot;
+            p.token_of_row[row] = t * k + j;
+          }
+        }
+        p.row_of[t * k + j] = row;
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += kBlock) {
+      int c = 0;
+      for (int w = 0; w < kWaves; ++w) c += __popcll(mask[w][e]);
+      running[e] += c;
+    }
+    __syncthreads();
+  }
+}
+
+// One wave per token: the row of x is read once into registers (kUnroll
+// 16-byte chunks per lane at a time) and written to each kept row.
+constexpr int kUnroll = 8;
+__global__ __launch_bounds__(kBlock) void permute_kernel(DispatchParams p) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * kWaves + threadIdx.x / kWave;
+  if (t >= p.T) return;
+  const int k = p.k;
+  const int64_t row_bytes = (int64_t)p.d * p.elem_bytes;
+  const int nchunk = (int)(row_bytes / 16);
+  const char* src = static_cast<const char*>(p.x) + (int64_t)t * row_bytes;
+  char* dst = static_cast<char*>(p.x_perm);
+  for (int q0 = 0; q0 < nchunk; q0 += kWave * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = q0 + u * kWave + lane;
+      if (q < nchunk) v[u] = load16(src + (int64_t)q * 16);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int row = p.row_of[t * k + j];
+      if (row < 0) continue;
+      char* drow = dst + (int64_t)row * row_bytes;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int q = q0 + u * kWave + lane;
+        if (q < nchunk) store16(drow + (int64_t)q * 16, v[u]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {
+  const int ntiles = (p.T + kDispatchTile - 1) / kDispatchTile;
+  hipLaunchKernelGGL(count_kernel, dim3(ntiles), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kBlock), 0, s, p, ntiles);
+  hipLaunchKernelGGL(slots_kernel, dim3(ntiles), dim3(kBlock), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.x_perm == nullptr) return err;
+  return launch_permute(p, s);
+}
+
+hipError_t launch_permute(const DispatchParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(permute_kernel, dim3((p.T + kWaves - 1) / kWaves), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,81 @@
+// Host-side launchers of the MoE kernels (internal to the library).
+// Every launcher enqueues on `stream` and returns the launch status; shapes
+// have been validated by the C ABI layer before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- gate (gate.hip)
+struct GateParams {
+  const void* x;           // [T, d] X-dtype
+  const void* w_gate;      // [d, N]
+  const void* w_noise;     // [d, N] or null
+  const float* noise;      // [T, N] or null
+  const float* logit_bias; // [N] or null
+  float* logits;           // [T, N] (required when N exceeds one column block)
+  int32_t* topk_idx;       // [T, k]
+  float* topk_w;           // [T, k]
+  int T, d, N, k, renorm;
+};
+hipError_t launch_gate_plain_noisy(const GateParams& p, bool bf16, bool noisy, hipStream_t s);
+
+struct CosineParams {
+  const float* z;          // [T, p] fp32 projection x P
+  const float* emb;        // [N, p] fp32
+  const float* logit_bias; // [N] or null
+  float inv_temperature;
+  float* logits;           // [T, N] or null
+  int32_t* topk_idx;
+  float* topk_w;
+  int T, p, N, k, renorm;
+};
+hipError_t launch_cosine_select(const CosineParams& p, hipStream_t s);
+
+// ---- dispatch (dispatch.hip)
+constexpr int kDispatchTile = 1024;  // tokens per dispatch tile
+struct DispatchParams {
+  const void* x;            // [T, d]
+  const int32_t* topk_idx;  // [T, k]
+  int32_t* tile_counts;     // [nTiles, N] workspace
+  int32_t* tile_base;       // [nTiles, N] workspace
+  int32_t* expert_count;    // [N]
+  int32_t* expert_off;      // [N+1]
+  int32_t* row_of;          // [T*k]
+  int32_t* token_of_row;    // [R]
+  void* x_perm;             // [R, d] or null (skip the copy)
+  int T, d, N, k, C, elem_bytes;
+};
+hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
+hipError_t launch_permute(const DispatchParams& p, hipStream_t s);
+
+// ---- grouped GEMM (gemm.hip)
+// C[r, :] = epilogue(A[r, :] B_g + bias_g) for the rows r of group g.
+struct GemmParams {
+  const void* A;        // rows of length K, stride lda elements
+  const void* B;        // per group [K, Ncols] row-major, group stride strideB elements
+  const void* bias;     // per group [Ncols] (stride strideBias) or null
+  void* C;              // rows of length Ncols, stride ldc elements
+  const int32_t* seg;   // [groups+1] row offsets of each group (device); null = one group of M rows
+  int64_t lda, ldc, strideB, strideBias;
+  int M;                // rows when seg is null; else the row bound R
+  int groups, K, Ncols;
+};
+enum class GemmKind { kFfn1Gelu, kFfn2, kProjF32 };
+hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, int avg_rows,
+                               hipStream_t s);
+
+// ---- combine (combine.hip)
+struct CombineParams {
+  const void* y_perm;      // [R, d]
+  const int32_t* row_of;   // [T*k]
+  const float* topk_w;     // [T, k]
+  void* y;                 // [T, d]
+  int T, d, k;
+  int R;                   // rows of y_perm; row_of entries >= R count as dropped
+};
+hipError_t launch_combine(const CombineParams& p, bool bf16, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,177 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, sizes capacity and workspaces, and rejects bad arguments before
+anything is enqueued. No kernel runs here.
+
+Calls that pass fake device addresses are meant to fail validation; they are
+skipped when a GPU is visible so that a validation bug can never turn one
+into a launch on a real device."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+import torch
+
+from mixture_experts_sparse_gate_amd import _lib, workloads
+from mixture_experts_sparse_gate_amd.api import desc_from_spec
+from oracle import moe_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from mixture_experts_sparse_gate_amd.build import build
+        build(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_stage_entry_points():
+    names = declared_functions()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the ctypes signatures cover exactly the declared functions
+    assert sorted(_lib.SIGNATURES) == declared_functions()
+
+
+def test_struct_layout_matches_header(lib):
+    # T(8) d h N k(16) cf(8) gate renorm dtype proj_dim(16) inv_temp reserved(8) = 56 bytes
+    assert ctypes.sizeof(_lib.MoeDesc) == 56
+    assert ctypes.sizeof(_lib.MoeLayerTensors) == 19 * 8
+
+
+def test_capacity_and_rows_bound(lib):
+    with open(os.path.join(ROOT, "tests", "golden", "capacity_workloads.json")) as f:
+        g = json.load(f)
+    for name in workloads.WORKLOAD_ORDER:
+        s = workloads.get(name)
+        d = desc_from_spec(s)
+        C = lib.moe_capacity(ctypes.byref(d))
+        assert C == g[name] == O.capacity(s.T, s.k, s.N, s.capacity_factor)
+        assert lib.moe_rows_bound(ctypes.byref(d)) == min(s.T * s.k, s.N * C)
+
+
+@pytest.mark.parametrize("T,k,N,cf", [(1, 1, 1, 1.0), (7, 3, 5, 0.1), (1000, 2, 8, 1.2),
+                                      (999, 4, 64, 1.5), (64, 8, 128, 16.0), (50, 2, 3, 1e-9)])
+def test_capacity_matches_oracle_formula(lib, T, k, N, cf):
+    s = workloads.MoESpec("c", T=T, d=8, h=8, N=N, k=k, capacity_factor=cf, gate="softmax",
+                          renorm=False, dtype="bf16")
+    assert lib.moe_capacity(ctypes.byref(desc_from_spec(s))) == O.capacity(T, k, N, cf)
+
+
+def test_workspace_sizes(lib):
+    base = workloads.get("noisy_top2_bf16")
+    prev = 0
+    for T in (1, 100, 1024, 4096, 10000):
+        d = desc_from_spec(base.with_(T=T))
+        sizes = []
+        for kind in (_lib.MOE_WS_ROUTE, _lib.MOE_WS_DISPATCH, _lib.MOE_WS_FORWARD):
+            n = ctypes.c_size_t()
+            assert lib.moe_workspace_size(ctypes.byref(d), kind, ctypes.byref(n)) == _lib.MOE_OK
+            assert n.value % 256 == 0
+            sizes.append(n.value)
+        assert sizes[2] >= sizes[0] + sizes[1]
+        assert sizes[2] > prev
+        prev = sizes[2]
+
+
+def _bad(spec, **kw):
+    d = desc_from_spec(spec)
+    for k_, v in kw.items():
+        setattr(d, k_, v)
+    return d
+
+
+@pytest.mark.parametrize("field,value", [
+    ("N", 0), ("N", 257), ("k", 0), ("k", 9), ("T", 0), ("capacity_factor", 0.0),
+    ("capacity_factor", float("nan")), ("capacity_factor", float("inf")), ("d", 12), ("h", 1020),
+    ("gate", 3), ("dtype", 2), ("renorm", 2), ("reserved", 1),
+])
+def test_invalid_desc_is_rejected(lib, field, value):
+    d = _bad(workloads.get("decode_top8_bf16").with_(N=8), **{field: value})
+    assert lib.moe_capacity(ctypes.byref(d)) == -1
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(d), _lib.MOE_WS_FORWARD, ctypes.byref(n)) == _lib.MOE_ERR_INVALID
+    assert lib.moe_last_error()
+
+
+def test_cosine_proj_dim_is_checked(lib):
+    s = workloads.get("cosine_zipf_top4_bf16")
+    for p in (0, 4, 12, 264):
+        d = _bad(s, proj_dim=p)
+        n = ctypes.c_size_t()
+        assert lib.moe_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == _lib.MOE_ERR_INVALID
+
+
+def test_null_desc(lib):
+    assert lib.moe_capacity(None) == -1
+    assert lib.moe_route(None, *([None] * 10), None, 0, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_forward(None, None, None, 0, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_status_string(_lib.MOE_ERR_WORKSPACE) == b"MOE_ERR_WORKSPACE"
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="fake device addresses are only passed where no GPU exists")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@no_gpu
+def test_route_argument_checks(lib):
+    s = workloads.get("noisy_top2_bf16")
+    d = desc_from_spec(s)
+    P = [FAKE] * 10
+    ws_need = ctypes.c_size_t()
+    lib.moe_workspace_size(ctypes.byref(d), _lib.MOE_WS_ROUTE, ctypes.byref(ws_need))
+
+    def call(ptrs, ws=FAKE, ws_bytes=ws_need.value):
+        return lib.moe_route(ctypes.byref(d), *ptrs, ws, ws_bytes, None)
+
+    for i in (0, 1, 2, 3, 8, 9):  # x, w_gate, w_noise, noise, topk_idx, topk_w required
+        q = list(P)
+        q[i] = None
+        assert call(q) == _lib.MOE_ERR_INVALID, i
+    q = list(P)
+    q[0] = FAKE + 8  # x misaligned
+    assert call(q) == _lib.MOE_ERR_INVALID
+    assert b"x" in lib.moe_last_error()
+    assert call(P, ws_bytes=ws_need.value - 1) == _lib.MOE_ERR_WORKSPACE
+    assert call(P, ws=None) == _lib.MOE_ERR_WORKSPACE
+    assert call(P, ws=FAKE + 128) == _lib.MOE_ERR_INVALID  # workspace must be 256-byte aligned
+
+
+@no_gpu
+def test_forward_argument_checks(lib):
+    s = workloads.get("cosine_zipf_top4_bf16")
+    d = desc_from_spec(s)
+    t = _lib.MoeLayerTensors(x=FAKE, proj=FAKE, expert_emb=FAKE, W1=FAKE, W2=FAKE, y=FAKE)
+    need = ctypes.c_size_t()
+    lib.moe_workspace_size(ctypes.byref(d), _lib.MOE_WS_FORWARD, ctypes.byref(need))
+    assert lib.moe_forward(ctypes.byref(d), ctypes.byref(t), FAKE, need.value - 256, None) == _lib.MOE_ERR_WORKSPACE
+    t.proj = None
+    assert lib.moe_forward(ctypes.byref(d), ctypes.byref(t), FAKE, need.value, None) == _lib.MOE_ERR_INVALID
+    t.proj = FAKE
+    t.row_of = FAKE + 2
+    assert lib.moe_forward(ctypes.byref(d), ctypes.byref(t), FAKE, need.value, None) == _lib.MOE_ERR_INVALID
+
+
+@no_gpu
+def test_stage_argument_checks(lib):
+    d = desc_from_spec(workloads.get("large_expert_top2_bf16"))
+    assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 4, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_dispatch(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
