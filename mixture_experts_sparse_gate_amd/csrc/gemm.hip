@@ -168,32 +168,49 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   if (g < 0) return;
   const int row_lo = sched[1], row_hi = sched[2];
 
-  const E* A = static_cast<const E*>(p.A);
-  const E* B = static_cast<const E*>(p.B) + (int64_t)g * p.strideB;
   const int K = p.K, Ncols = p.Ncols;
+  const int lda = (int)p.lda;
+  // uniform 64-bit bases, per-thread 32-bit offsets that do not change over K
+  const E* At = static_cast<const E*>(p.A) + (int64_t)row_lo * p.lda;
+  const E* Bg = static_cast<const E*>(p.B) + (int64_t)g * p.strideB;
+  int a_off[C::A_PER_THREAD], a_k[C::A_PER_THREAD];
+  bool a_ok[C::A_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < C::A_PER_THREAD; ++i) {
+    const int idx = tid + i * C::THREADS;
+    const int r = idx / KC, c = idx % KC;
+    a_k[i] = c * CE;
+    a_off[i] = r * lda + c * CE;
+    a_ok[i] = idx < C::A_CHUNKS && row_lo + r < row_hi;
+  }
+  int b_off[C::B_PER_THREAD], b_k[C::B_PER_THREAD];
+  bool b_ok[C::B_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < C::B_PER_THREAD; ++i) {
+    const int idx = tid + i * C::THREADS;
+    const int kb = idx / (BN / CE), nb = idx % (BN / CE);
+    b_k[i] = kb * CE;
+    b_off[i] = kb * CE * Ncols + n0 + nb * CE;
+    b_ok[i] = idx < C::B_BLOCKS && n0 + nb * CE < Ncols;
+  }
 
   // ---- global -> register loads of one K-step
   u32x4 ra[C::A_PER_THREAD];
   u32x4 rb[C::B_PER_THREAD][CE];
   auto load_tiles = [&](int k0) {
+    const E* Ak = At + k0;
+    const E* Bk = Bg + (int64_t)k0 * Ncols;
 #pragma unroll
     for (int i = 0; i < C::A_PER_THREAD; ++i) {
-      const int idx = tid + i * C::THREADS;
-      const int r = idx / KC, c = idx % KC;
-      const int grow = row_lo + r;
-      const int kk = k0 + c * CE;
       ra[i] = u32x4{0, 0, 0, 0};
-      if (idx < C::A_CHUNKS && grow < row_hi && kk < K) ra[i] = load16(A + grow * p.lda + kk);
+      if (a_ok[i] && k0 + a_k[i] < K) ra[i] = load16(Ak + a_off[i]);
     }
 #pragma unroll
     for (int i = 0; i < C::B_PER_THREAD; ++i) {
-      const int idx = tid + i * C::THREADS;
-      const int kb = idx / (BN / CE), nb = idx % (BN / CE);
-      const int kk = k0 + kb * CE, nn = n0 + nb * CE;
-      const bool ok = idx < C::B_BLOCKS && kk < K && nn < Ncols;
+      const bool ok = b_ok[i] && k0 + b_k[i] < K;
 #pragma unroll
       for (int r = 0; r < CE; ++r)
-        rb[i][r] = ok ? load16(B + (int64_t)(kk + r) * Ncols + nn) : u32x4{0, 0, 0, 0};
+        rb[i][r] = ok ? load16(Bk + b_off[i] + r * Ncols) : u32x4{0, 0, 0, 0};
     }
   };
   auto store_tiles = [&](int stage) {
@@ -236,29 +253,35 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   store_tiles(0);
   __syncthreads();
   const int lrow = lane & 31, lhalf = lane >> 5;
+  // operand fragments of one k-substep (16 bf16 / 8 fp32 of K), double-buffered
+  // so that the LDS reads of substep s+1 are in flight during the MFMAs of s
+  u32x4 fa[2][C::FN], fb[2][C::FM];
+  auto load_frags = [&](const u32x4* as, const u32x4* bs, int s, int buf) {
+    const int c = 2 * s + lhalf;
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i) {
+      const int n = wn * C::WTN + i * 32 + lrow;
+      fa[buf][i] = bs[n * KC + (c ^ swz(n))];
+    }
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) {
+      const int m = wm * C::WTM + j * 32 + lrow;
+      fb[buf][j] = as[m * KC + (c ^ swz(m))];
+    }
+  };
   for (int kt = 0; kt < nk; ++kt) {
     const int stage = kt & 1;
     if (kt + 1 < nk) load_tiles((kt + 1) * BK);
     const u32x4* as = As + stage * C::A_CHUNKS;
     const u32x4* bs = Bs + stage * C::B_CHUNKS;
+    load_frags(as, bs, 0, 0);
 #pragma unroll
     for (int s = 0; s < KC / 2; ++s) {
-      const int c = 2 * s + lhalf;
-      u32x4 fa[C::FN], fb[C::FM];
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i) {
-        const int n = wn * C::WTN + i * 32 + lrow;
-        fa[i] = bs[n * KC + (c ^ swz(n))];
-      }
-#pragma unroll
-      for (int j = 0; j < C::FM; ++j) {
-        const int m = wm * C::WTM + j * 32 + lrow;
-        fb[j] = as[m * KC + (c ^ swz(m))];
-      }
+      if (s + 1 < KC / 2) load_frags(as, bs, s + 1, (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FM; ++j) Mfma<E>::step(acc[i][j], fa[i], fb[j]);
+        for (int j = 0; j < C::FM; ++j) Mfma<E>::step(acc[i][j], fa[s & 1][i], fb[s & 1][j]);
     }
     if (kt + 1 < nk) store_tiles(stage ^ 1);
     __syncthreads();
@@ -303,11 +326,21 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile shapes: BM x BN with WM x WN waves.
+constexpr int kNumCUs = 256;
+
+// Tile shapes (BM x BN with WM x WN waves): the largest tile that still gives
+// every CU a block, judged from the row bound M (the routing itself is only
+// known on the device). Few rows per expert (decode) take thin row tiles that
+// stream the weights.
 template <typename E, typename O, bool G>
 hipError_t launch_dtype(const GemmParams& p, int avg_rows, hipStream_t s) {
-  if (avg_rows < 64)  // few rows per expert (decode): stream the weights with thin row tiles
-    return launch_cfg<Cfg<E, O, 32, 256, 1, 4, G>>(p, s);
+  if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, G>>(p, s);
+  const int groups = p.seg ? p.groups : 0;
+  auto tiles = [&](int bm, int bn) {
+    return (int64_t)(p.M / bm + groups) * ((p.Ncols + bn - 1) / bn);
+  };
+  if (tiles(256, 256) >= kNumCUs) return launch_cfg<Cfg<E, O, 256, 256, 2, 2, G>>(p, s);
+  if (tiles(256, 128) >= kNumCUs) return launch_cfg<Cfg<E, O, 256, 128, 2, 2, G>>(p, s);
   return launch_cfg<Cfg<E, O, 128, 128, 2, 2, G>>(p, s);
 }
 

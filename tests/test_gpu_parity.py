@@ -105,6 +105,13 @@ def test_full_size_forward(name):
     say(f"   tokens routed differently from fp64 logits: {differ} of {spec.T}")
     assert differ <= max(1, spec.T // 1000)
     A = int(r["off"][-1])
+    # moe_forward keeps x_perm in its workspace: rebuild it with moe_dispatch
+    # on the same routing, which must reproduce forward's row maps exactly
+    row_of_fwd, tor_fwd = dev.row_of.clone(), dev.token_of_row.clone()
+    api.dispatch(dev.desc, dev.x, dev.topk_idx, dev.expert_count, dev.expert_off, dev.row_of,
+                 dev.token_of_row, dev.x_perm, ws=dev.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.row_of, row_of_fwd) and torch.equal(dev.token_of_row[:A], tor_fwd[:A])
     rng = np.random.default_rng(1)
     rows = np.unique(np.concatenate([[0, A - 1], rng.choice(A, size=min(A, 64), replace=False)]))
     check_x_perm(spec, inp, dev, r, rows)
