@@ -17,6 +17,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_gfx950.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
@@ -26,7 +27,7 @@ SOURCES = ["gate.hip", "dispatch.hip", "gemm.hip", "combine.hip", "capi.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
-    "-fvisibility=hidden",
+    "-fvisibility=hidden", f"-I{INCLUDE}",
     # packed fp32 instructions stay off: the compiler emits plain v_fma/v_add
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

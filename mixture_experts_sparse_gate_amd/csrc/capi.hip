@@ -6,7 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.hpp"
 
 namespace {

@@ -13,15 +13,19 @@
 //    transposed sense, D = B^T A^T: the weight tile is the MFMA's first
 //    operand and the activation rows its second, so each lane ends up with
 //    4 consecutive output columns of one row (8- or 16-byte stores).
-//  - Both operands are K-contiguous 16-byte chunks in LDS. A rows are
-//    K-contiguous already. B is N-contiguous in memory, so each thread loads
-//    an 8x8 (bf16) or 4x4 (fp32) block of it with 16-byte row loads and
-//    transposes it in registers before the LDS store.
-//  - LDS rows are BK elements = 8 chunks; chunk c of row r is stored at
-//    c ^ ((r ^ r>>3) & 7), which keeps both the transposed stores and the
-//    MFMA operand reads free of bank conflicts.
+//  - Both tiles go to LDS as they lie in memory: activation rows
+//    K-contiguous, weight rows N-contiguous, copied with 16-byte loads and
+//    stores. The MFMA needs 8 consecutive K values of one weight column per
+//    lane; gfx950's LDS transpose read (ds_read_b64_tr_b16) delivers exactly
+//    that from the N-contiguous tile (two reads per 16-K fragment), so the
+//    weights are never transposed in registers or in memory. The fp32 build
+//    reads single elements instead (its MFMA takes one K value per lane).
+//  - LDS rows are padded (activation rows by 16 bytes, weight rows by 32) so
+//    that every fragment read is free of bank conflicts and every fragment
+//    address is one per-lane base plus compile-time offsets.
 //  - Two LDS stages: the next K-step's global loads are in flight while the
-//    current one feeds the MFMAs.
+//    current one feeds the MFMAs; within a step the fragment reads of
+//    substep s+1 overlap the MFMAs of substep s.
 //  - Ragged groups: the grid's x dimension is an upper bound on the number
 //    of row tiles; each block finds its (group, row range) from seg on the
 //    device, so no host synchronisation is needed. Blocks past the last tile
@@ -51,93 +55,111 @@ template <> struct Mfma<float> {
   }
 };
 
-// Transposes a CE x CE block held as CE rows of one 16-byte chunk each:
-// in[r] = row r (CE consecutive columns), out[c] = column c (CE consecutive rows).
-template <typename E> struct Transpose;
-template <> struct Transpose<bf16> {
-  __device__ static inline void run(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = in[2 * q][c >> 1], hi = in[2 * q + 1][c >> 1];
-        out[c][q] = (c & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u)
-                            : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-      }
-  }
-};
-template <> struct Transpose<float> {
-  __device__ static inline void run(const u32x4 (&in)[4], u32x4 (&out)[4]) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) out[c][r] = in[r][c];
-  }
-};
-
 __device__ inline float gelu_erf(float u) { return 0.5f * u * (1.f + erff(u * 0.70710678118654752f)); }
 
-template <typename E, typename O, int BM_, int BN_, int WM_, int WN_, bool GELU_>
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
+// Raw buffer descriptor (gfx9 family: word 3 = 0x00020000) over [base, base + bytes).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from the buffer at byte offset voff straight into LDS:
+// lane l writes dst + 16 l (dst is wave-uniform). Out-of-range reads write zeros.
+__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+// s_waitcnt that waits for at most n outstanding vector-memory operations
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at max).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr int kNumXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
+constexpr int kGroupN = 4;   // n-tiles per run of the tile order
+
+template <typename E, typename O, int BM_, int BN_, int WM_, int WN_, int KC_, int S_, bool GELU_>
 struct Cfg {
   using Elem = E;
   using Out = O;
-  static constexpr int CE = ElemTraits<E>::kPerChunk;
-  static constexpr int KC = 8;  // chunks per LDS row: BK = 8 * CE elements
-  static constexpr int BK = KC * CE;
+  static constexpr int ES = sizeof(E);
+  static constexpr int CE = ElemTraits<E>::kPerChunk;   // elements per 16-byte chunk
+  static constexpr int KC = KC_;                         // 16-byte chunks of K per activation row per stage
+  static constexpr int BK = KC * CE;                     // K per stage
+  static constexpr int S = S_;                           // LDS stages
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int THREADS = kWave * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr bool GELU = GELU_;
-  static constexpr int A_CHUNKS = BM * KC;              // per stage
-  static constexpr int B_CHUNKS = BN * KC;
-  static constexpr int A_PER_THREAD = (A_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int B_BLOCKS = KC * (BN / CE);       // CE x CE blocks per stage
-  static constexpr int B_PER_THREAD = (B_BLOCKS + THREADS - 1) / THREADS;
-  static constexpr int LDS_BYTES = 2 * (A_CHUNKS + B_CHUNKS) * 16;
+  static constexpr int B_CPR = BN * ES / 16;             // 16-byte chunks per weight row
+  static constexpr int A_STAGE = BM * KC * 16;           // activation tile, K-contiguous rows
+  static constexpr int B_STAGE = BK * B_CPR * 16;        // weight tile, N-contiguous rows
+  static constexpr int A_INST = BM * KC / THREADS;       // 16-byte loads per thread per stage
+  static constexpr int B_INST = BK * B_CPR / THREADS;
+  static constexpr int LOADS = A_INST + B_INST;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
-  static_assert(BN % CE == 0, "");
+  static_assert(KC == 4 || KC == 8, "activation rows of 4 or 8 chunks");
+  static_assert(BM * KC % THREADS == 0 && BK * B_CPR % THREADS == 0, "loads must divide evenly");
+  static_assert(B_CPR >= 8 && WTN % 64 == 0, "weight rows of at least 128 bytes, wave tiles of 64 columns");
+  static_assert(S >= 2 && S <= 4 && S * (A_STAGE + B_STAGE) <= 160 * 1024, "LDS budget");
+  static_assert(LOADS * (S - 2) < 64, "vmcnt range");
 };
 
-__device__ inline int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// Chunk swizzles. Activation rows hold KC chunks: chunk c of row r sits at
+// c ^ fa(r), so that the 8 rows one MFMA fragment read touches at a time
+// land in distinct banks. Weight rows: chunk c of row k sits at c ^ 2(k%4),
+// so that the 4 rows one transpose read touches land in distinct 32-byte
+// bank windows.
+template <int KC> __device__ inline int swz_a(int r) { return KC == 8 ? (r & 7) : ((r >> 1) & 3); }
+__device__ inline int swz_b(int k) { return 2 * (k & 3); }
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) {
   using E = typename C::Elem;
   using O = typename C::Out;
-  constexpr int CE = C::CE, KC = C::KC, BK = C::BK, BM = C::BM, BN = C::BN;
-  __shared__ u32x4 smem[C::LDS_BYTES / 16];
-  __shared__ int sched[3];
-  u32x4* As = smem;                      // [2][BM * KC]
-  u32x4* Bs = smem + 2 * C::A_CHUNKS;    // [2][BN * KC]
+  constexpr int CE = C::CE, KC = C::KC, BK = C::BK, BM = C::BM, BN = C::BN, ES = C::ES, S = C::S;
+  // one LDS object per stage, so that the compiler can tell a stage being
+  // filled by the asynchronous loads from the one being read
+  // (activation tile at offset 0, weight tile at A_STAGE)
+  constexpr int ST = C::A_STAGE + C::B_STAGE;
+  __shared__ __attribute__((aligned(1024))) char st0[ST];
+  __shared__ __attribute__((aligned(1024))) char st1[ST];
+  __shared__ __attribute__((aligned(1024))) char st2[S > 2 ? ST : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? ST : 16];
+  __shared__ int sched[4];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  const int mt = blockIdx.x;
-  const int n0 = blockIdx.y * BN;
-
-  // ---- find this block's (group, rows)
-  if (p.seg == nullptr) {
-    if (tid == 0) {
-      const int lo = mt * BM;
-      sched[0] = lo < p.M ? 0 : -1;
-      sched[1] = lo;
-      sched[2] = p.M;
-    }
-  } else if (wave == 0) {
+  // ---- tile schedule. Tiles are ordered group by group; within a group,
+  // n-tiles in runs of kGroupN, row tiles fastest within a run. The
+  // hardware hands blocks to the XCDs round-robin (block b -> XCD b % 8), so
+  // block b is given tile (b % 8) * per + b / 8: each XCD works through one
+  // contiguous stretch of that order, and the ~32 blocks it runs at a time
+  // share their weight slabs and activation rows in its own L2.
+  if (wave == 0) {
     constexpr int GPL = 4;  // groups per lane (groups <= 256)
     int cnt[GPL];
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
-      const int g = lane * GPL + i;
+      const int gi = lane * GPL + i;
       cnt[i] = 0;
-      if (g < p.groups) {
+      if (p.seg == nullptr) {
+        if (gi == 0) cnt[i] = (p.M + BM - 1) / BM;
+      } else if (gi < p.groups) {
         // rows are clamped to [0, M] so that no offset table can address
         // outside the row buffers
-        const int lo = min(max(p.seg[g], 0), p.M), hi = min(max(p.seg[g + 1], lo), p.M);
+        const int lo = min(max(p.seg[gi], 0), p.M), hi = min(max(p.seg[gi + 1], lo), p.M);
         cnt[i] = (hi - lo + BM - 1) / BM;
       }
       sum += cnt[i];
@@ -148,96 +170,85 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
       const int o = __shfl_up(inc, m, kWave);
       if (lane >= m) inc += o;
     }
-    const int total = __shfl(inc, kWave - 1, kWave);
-    if (lane == 0 && mt >= total) sched[0] = -1;
+    const int NT = (p.Ncols + BN - 1) / BN;
+    const int total = __shfl(inc, kWave - 1, kWave) * NT;
+    const int per = (total + kNumXcds - 1) / kNumXcds;
+    const int b = blockIdx.x, local = b / kNumXcds;
+    const int tile = (b % kNumXcds) * per + local;
+    const bool live = local < per && tile < total;
+    if (lane == 0 && !live) sched[0] = -1;
+    const int q = tile / NT;  // row tile in the concatenated order of all groups
     int start = inc - sum;
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
-      if (mt >= start && mt < start + cnt[i]) {
-        const int g = lane * GPL + i;
-        const int lo = min(max(p.seg[g], 0), p.M), hi = min(max(p.seg[g + 1], lo), p.M);
-        sched[0] = g;
-        sched[1] = lo + (mt - start) * BM;
+      if (live && q >= start && q < start + cnt[i]) {
+        const int gi = lane * GPL + i;
+        int lo = 0, hi = p.M;
+        if (p.seg != nullptr) {
+          lo = min(max(p.seg[gi], 0), p.M);
+          hi = min(max(p.seg[gi + 1], lo), p.M);
+        }
+        const int t = tile - start * NT;       // tile within the group
+        const int run = cnt[i] * kGroupN;      // tiles per run of kGroupN n-tiles
+        const int ng = t / run, r = t % run;
+        const int gn = min(kGroupN, NT - ng * kGroupN);
+        sched[0] = gi;
+        sched[1] = lo + (r / gn) * BM;
         sched[2] = hi;
+        sched[3] = (ng * kGroupN + r % gn) * BN;
       }
       start += cnt[i];
     }
   }
   __syncthreads();
-  const int g = sched[0];
+  // block-uniform: keep them in scalar registers so that the buffer
+  // descriptors built from them are uniform too
+  const int g = __builtin_amdgcn_readfirstlane(sched[0]);
   if (g < 0) return;
-  const int row_lo = sched[1], row_hi = sched[2];
-
+  const int row_lo = __builtin_amdgcn_readfirstlane(sched[1]);
+  const int row_hi = __builtin_amdgcn_readfirstlane(sched[2]);
+  const int n0 = __builtin_amdgcn_readfirstlane(sched[3]);
   const int K = p.K, Ncols = p.Ncols;
   const int lda = (int)p.lda;
-  // uniform 64-bit bases, per-thread 32-bit offsets that do not change over K
-  const E* At = static_cast<const E*>(p.A) + (int64_t)row_lo * p.lda;
-  const E* Bg = static_cast<const E*>(p.B) + (int64_t)g * p.strideB;
-  int a_off[C::A_PER_THREAD], a_k[C::A_PER_THREAD];
-  bool a_ok[C::A_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < C::A_PER_THREAD; ++i) {
-    const int idx = tid + i * C::THREADS;
-    const int r = idx / KC, c = idx % KC;
-    a_k[i] = c * CE;
-    a_off[i] = r * lda + c * CE;
-    a_ok[i] = idx < C::A_CHUNKS && row_lo + r < row_hi;
-  }
-  int b_off[C::B_PER_THREAD], b_k[C::B_PER_THREAD];
-  bool b_ok[C::B_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < C::B_PER_THREAD; ++i) {
-    const int idx = tid + i * C::THREADS;
-    const int kb = idx / (BN / CE), nb = idx % (BN / CE);
-    b_k[i] = kb * CE;
-    b_off[i] = kb * CE * Ncols + n0 + nb * CE;
-    b_ok[i] = idx < C::B_BLOCKS && n0 + nb * CE < Ncols;
-  }
+  const int rows = row_hi - row_lo;
+  const char* At = static_cast<const char*>(p.A) + (int64_t)row_lo * p.lda * ES;
+  const char* Bt = static_cast<const char*>(p.B) + ((int64_t)g * p.strideB + n0) * ES;
+  const int64_t a_bytes = (int64_t)rows * lda * ES;
+  const int64_t b_bytes = (int64_t)K * Ncols * ES - (int64_t)n0 * ES;
 
-  // ---- global -> register loads of one K-step
-  u32x4 ra[C::A_PER_THREAD];
-  u32x4 rb[C::B_PER_THREAD][CE];
-  auto load_tiles = [&](int k0) {
-    const E* Ak = At + k0;
-    const E* Bk = Bg + (int64_t)k0 * Ncols;
+  // ---- asynchronous global -> LDS loads. Each 16-byte load of a wave lands
+  // at (wave's slot base + lane) * 16 in the stage; the lane fetches whichever
+  // chunk the swizzle puts in that slot. Offsets are fixed over K; each
+  // K-step moves the descriptor base to k0 and shrinks its extent to what
+  // remains (zero past K), so the hardware range check supplies zeros for
+  // rows past the group and for K past the end. (Activation rows are exactly
+  // K long: a load past K in one row reads the next row, which meets zero
+  // weights.) Columns past Ncols read neighbouring data and only feed
+  // outputs that are never stored.
+  int a_off[C::A_INST], b_off[C::B_INST];
 #pragma unroll
-    for (int i = 0; i < C::A_PER_THREAD; ++i) {
-      ra[i] = u32x4{0, 0, 0, 0};
-      if (a_ok[i] && k0 + a_k[i] < K) ra[i] = load16(Ak + a_off[i]);
-    }
+  for (int i = 0; i < C::A_INST; ++i) {
+    const int slot = i * C::THREADS + tid;
+    const int r = slot / KC, c = (slot % KC) ^ swz_a<KC>(r);
+    a_off[i] = (r * lda + c * CE) * ES;
+  }
 #pragma unroll
-    for (int i = 0; i < C::B_PER_THREAD; ++i) {
-      const bool ok = b_ok[i] && k0 + b_k[i] < K;
+  for (int i = 0; i < C::B_INST; ++i) {
+    const int slot = i * C::THREADS + tid;
+    const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_b(k);
+    b_off[i] = (k * Ncols + c * CE) * ES;
+  }
+  auto issue = [&](char* sa, char* sb, int k0) {
+    const int64_t ab = a_bytes - (int64_t)k0 * ES;
+    const int64_t bb = b_bytes - (int64_t)k0 * Ncols * ES;
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(At + (int64_t)k0 * ES, (uint32_t)(ab > 0 ? ab : 0));
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(Bt + (int64_t)k0 * Ncols * ES, (uint32_t)(bb > 0 ? bb : 0));
 #pragma unroll
-      for (int r = 0; r < CE; ++r)
-        rb[i][r] = ok ? load16(Bk + b_off[i] + r * Ncols) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tiles = [&](int stage) {
-    u32x4* as = As + stage * C::A_CHUNKS;
-    u32x4* bs = Bs + stage * C::B_CHUNKS;
+    for (int i = 0; i < C::A_INST; ++i)
+      lds_load16(ar, (lds_void*)(sa + (i * C::THREADS + wave * kWave) * 16), a_off[i]);
 #pragma unroll
-    for (int i = 0; i < C::A_PER_THREAD; ++i) {
-      const int idx = tid + i * C::THREADS;
-      if (idx < C::A_CHUNKS) {
-        const int r = idx / KC, c = idx % KC;
-        as[r * KC + (c ^ swz(r))] = ra[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_THREAD; ++i) {
-      const int idx = tid + i * C::THREADS;
-      if (idx < C::B_BLOCKS) {
-        const int kb = idx / (BN / CE), nb = idx % (BN / CE);
-        u32x4 t[CE];
-        Transpose<E>::run(rb[i], t);
-#pragma unroll
-        for (int c = 0; c < CE; ++c) {
-          const int n = nb * CE + c;
-          bs[n * KC + (kb ^ swz(n))] = t[c];
-        }
-      }
-    }
+    for (int i = 0; i < C::B_INST; ++i)
+      lds_load16(br, (lds_void*)(sb + (i * C::THREADS + wave * kWave) * 16), b_off[i]);
   };
 
   f32x16 acc[C::FN][C::FM];
@@ -248,44 +259,90 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = (K + BK - 1) / BK;
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
+  // ---- per-lane fragment offsets within a stage
   const int lrow = lane & 31, lhalf = lane >> 5;
-  // operand fragments of one k-substep (16 bf16 / 8 fp32 of K), double-buffered
-  // so that the LDS reads of substep s+1 are in flight during the MFMAs of s
+  // activation fragment (MFMA second operand): row wm*WTM + 32j + lane%32,
+  // chunk 2s + lane/32 (swizzled); one offset per substep
+  int fa_off[KC / 2];
+#pragma unroll
+  for (int ss = 0; ss < KC / 2; ++ss)
+    fa_off[ss] = (wm * C::WTM + lrow) * KC * 16 + (((2 * ss + lhalf) ^ swz_a<KC>(lrow)) * 16);
+  // weight fragment, bf16: 16-lane group q, lane r in it: rows 16s + 8(q/2) + 4p + r/4,
+  // columns wn*WTN + 32i + 16(q%2) + 4(r%4) .. +3 (chunk XOR 2(r/4) flips bit 2 for odd i)
+  const int q16 = lane >> 4, r16 = lane & 15;
+  const int zc = (2 * (q16 & 1) + ((r16 & 3) >> 1)) ^ swz_b(r16 >> 2);
+  const int fw_row = (8 * (q16 >> 1) + (r16 >> 2)) * C::B_CPR * 16 + (wn * C::WTN / 64) * 128 + 8 * (r16 & 1);
+  const int fw_even = fw_row + zc * 16, fw_odd = fw_row + (zc ^ 4) * 16;
+  // weight fragment, fp32: row 8s + 4(lane/32) + e, column wn*WTN + 32i + lane%32
+  int fw32[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    fw32[e] = (4 * lhalf + e) * C::B_CPR * 16 + (wn * C::WTN / 4 + ((lrow >> 2) ^ swz_b(e))) * 16 + (lrow & 3) * 4;
+
   u32x4 fa[2][C::FN], fb[2][C::FM];
-  auto load_frags = [&](const u32x4* as, const u32x4* bs, int s, int buf) {
-    const int c = 2 * s + lhalf;
+  auto load_frags = [&](const char* sa, const char* sb, int ss, int buf) {
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i) {
-      const int n = wn * C::WTN + i * 32 + lrow;
-      fa[buf][i] = bs[n * KC + (c ^ swz(n))];
-    }
+    for (int j = 0; j < C::FM; ++j)
+      fb[buf][j] = *(lds_u32x4*)(sa + fa_off[ss] + j * 32 * KC * 16);
+    if constexpr (ES == 2) {
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) {
-      const int m = wm * C::WTM + j * 32 + lrow;
-      fb[buf][j] = as[m * KC + (c ^ swz(m))];
-    }
-  };
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-    const u32x4* as = As + stage * C::A_CHUNKS;
-    const u32x4* bs = Bs + stage * C::B_CHUNKS;
-    load_frags(as, bs, 0, 0);
-#pragma unroll
-    for (int s = 0; s < KC / 2; ++s) {
-      if (s + 1 < KC / 2) load_frags(as, bs, s + 1, (s + 1) & 1);
+      for (int i = 0; i < C::FN; ++i) {
+        const char* w = sb + ((i & 1) ? fw_odd : fw_even) + (i >> 1) * 128;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + (16 * ss) * C::B_CPR * 16));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + (16 * ss + 4) * C::B_CPR * 16));
+        const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+        fa[buf][i] = u32x4{x[0], x[1], y[0], y[1]};
+      }
+    } else {
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-        for (int j = 0; j < C::FM; ++j) Mfma<E>::step(acc[i][j], fa[s & 1][i], fb[s & 1][j]);
+        for (int e = 0; e < 4; ++e)
+          fa[buf][i][e] = *(lds_u32*)(sb + fw32[e] + (8 * ss) * C::B_CPR * 16 + i * 128);
     }
-    if (kt + 1 < nk) store_tiles(stage ^ 1);
-    __syncthreads();
+  };
+  auto compute = [&](const char* sa, const char* sb) {
+    load_frags(sa, sb, 0, 0);
+#pragma unroll
+    for (int ss = 0; ss < KC / 2; ++ss) {
+      if (ss + 1 < KC / 2) load_frags(sa, sb, ss + 1, (ss + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) Mfma<E>::step(acc[i][j], fa[ss & 1][i], fb[ss & 1][j]);
+    }
+  };
+
+  // ---- S-stage pipeline, one barrier per K-step: wait until this step's
+  // loads have landed (later steps' loads may still be in flight), barrier
+  // (everyone's loads visible; everyone done with the previous stage), start
+  // the loads S-1 steps ahead into the stage just freed, compute.
+  const int nk = (K + BK - 1) / BK;
+  issue(st0, st0 + C::A_STAGE, 0);
+  if constexpr (S > 2) issue(st1, st1 + C::A_STAGE, BK);
+  if constexpr (S > 3) issue(st2, st2 + C::A_STAGE, 2 * BK);
+  auto step = [&](auto st, int kt) {
+    constexpr int cur = decltype(st)::value;
+    constexpr int nxt = (cur + S - 1) % S;
+    wait_vmcnt<C::LOADS * (S - 2)>();
+    __builtin_amdgcn_s_barrier();
+    const int kn = (kt + S - 1) * BK;
+    if constexpr (nxt == 0) issue(st0, st0 + C::A_STAGE, kn);
+    else if constexpr (nxt == 1) issue(st1, st1 + C::A_STAGE, kn);
+    else if constexpr (nxt == 2) issue(st2, st2 + C::A_STAGE, kn);
+    else issue(st3, st3 + C::A_STAGE, kn);
+    if constexpr (cur == 0) compute(st0, st0 + C::A_STAGE);
+    else if constexpr (cur == 1) compute(st1, st1 + C::A_STAGE);
+    else if constexpr (cur == 2) compute(st2, st2 + C::A_STAGE);
+    else compute(st3, st3 + C::A_STAGE);
+  };
+  for (int kt = 0; kt < nk; kt += S) {
+    step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (S > 2) if (kt + 2 < nk) step(std::integral_constant<int, 2 % S>{}, kt + 2);
+    if constexpr (S > 3) if (kt + 3 < nk) step(std::integral_constant<int, 3 % S>{}, kt + 3);
   }
+  wait_vmcnt<0>();
 
   // ---- epilogue: lane holds row m = .. + lane%32, columns n = .. + 8*(r/4) + 4*(lane/32) + r%4
   O* Cp = static_cast<O*>(p.C);
@@ -322,26 +379,27 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
     mtiles = p.M / C::BM + p.groups + 1;  // >= sum over groups of ceil(rows_g / BM)
   const int ntiles = (p.Ncols + C::BN - 1) / C::BN;
   if (mtiles <= 0 || ntiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3(mtiles, ntiles), dim3(C::THREADS), 0, s, p);
+  // a multiple of the XCD count, so that every XCD has room for its share
+  const int64_t blocks = ((int64_t)mtiles * ntiles + kNumXcds - 1) / kNumXcds * kNumXcds;
+  hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 constexpr int kNumCUs = 256;
 
-// Tile shapes (BM x BN with WM x WN waves): the largest tile that still gives
-// every CU a block, judged from the row bound M (the routing itself is only
-// known on the device). Few rows per expert (decode) take thin row tiles that
-// stream the weights.
+// Tile shapes: the largest tile that still gives every CU a block, judged
+// from the row bound M (the routing itself is only known on the device).
+// Few rows per expert (decode) take thin row tiles that stream the weights
+// with deep prefetch. Cfg<elem, out, BM, BN, waves M x N, K chunks/stage, stages>.
 template <typename E, typename O, bool G>
 hipError_t launch_dtype(const GemmParams& p, int avg_rows, hipStream_t s) {
-  if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, G>>(p, s);
+  if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, 8, 4, G>>(p, s);
   const int groups = p.seg ? p.groups : 0;
   auto tiles = [&](int bm, int bn) {
     return (int64_t)(p.M / bm + groups) * ((p.Ncols + bn - 1) / bn);
   };
-  if (tiles(256, 256) >= kNumCUs) return launch_cfg<Cfg<E, O, 256, 256, 2, 2, G>>(p, s);
-  if (tiles(256, 128) >= kNumCUs) return launch_cfg<Cfg<E, O, 256, 128, 2, 2, G>>(p, s);
-  return launch_cfg<Cfg<E, O, 128, 128, 2, 2, G>>(p, s);
+  if (tiles(256, 256) >= kNumCUs) return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s);
+  return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s);
 }
 
 }  // namespace
