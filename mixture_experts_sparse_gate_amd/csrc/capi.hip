@@ -173,7 +173,7 @@ moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, co
     g.groups = 1;
     g.K = d->d;
     g.Ncols = d->proj_dim;
-    TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kProjF32, bf, (int)d->T, s),
+    TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kProjF32, bf, (int)d->T, (int)d->T, s),
                    "cosine projection"));
     moe::CosineParams c{};
     c.z = z;
@@ -236,6 +236,7 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* x_perm, const int32_t* off,
   const bool bf = d->dtype == MOE_BF16;
   const int R = (int)rows_bound_of(d);
   const int avg_rows = (int)((d->T * d->k) / d->N);
+  const int max_rows = (int)capacity_of(d);
   moe::GemmParams g{};
   g.A = x_perm;
   g.B = W1;
@@ -250,7 +251,7 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* x_perm, const int32_t* off,
   g.groups = d->N;
   g.K = d->d;
   g.Ncols = d->h;
-  TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn1Gelu, bf, avg_rows, s),
+  TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s),
                  "expert GEMM1"));
   g.A = H;
   g.B = W2;
@@ -262,7 +263,7 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* x_perm, const int32_t* off,
   g.strideBias = d->d;
   g.K = d->h;
   g.Ncols = d->d;
-  return hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn2, bf, avg_rows, s),
+  return hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn2, bf, avg_rows, max_rows, s),
                     "expert GEMM2");
 }
 

@@ -77,6 +77,81 @@ __device__ void select_token(const float* lg, int N, int k, int renorm, int32_t*
   }
 }
 
+// Top-k selection and weights for TW tokens at once (same rules as
+// select_token); the TW reductions are independent, so their shuffles
+// interleave instead of running back to back. lg[t] holds token t's N
+// logits in LDS; tokens at or past `valid` are skipped.
+template <int TW>
+__device__ void select_tokens(const float (*lg)[kWave * kMaxExpertsPerLane], int valid, int N, int k,
+                              int renorm, int32_t* idx_out, float* w_out) {
+  const int lane = lane_id();
+  float v[TW][kMaxExpertsPerLane];
+  uint32_t taken[TW];
+  int my_e[TW];
+  float my_l[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    taken[t] = 0;
+    my_e[t] = 0;
+    my_l[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+      const int e = lane + kWave * i;
+      v[t][i] = e < N ? lg[t][e] : 0.f;
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    uint64_t best[TW];
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      best[t] = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+        const uint32_t e = lane + kWave * i;
+        if (e < (uint32_t)N && !((taken[t] >> i) & 1u)) {
+          const uint64_t key = ((uint64_t)float_order_key(v[t][i]) << 32) | (0xFFFFFFFFu - e);
+          best[t] = key > best[t] ? key : best[t];
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+      for (int t = 0; t < TW; ++t) {
+        const uint64_t o = shfl_xor_u64(best[t], m);
+        best[t] = o > best[t] ? o : best[t];
+      }
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const int e = (int)(0xFFFFFFFFu - (uint32_t)best[t]);
+      if ((e & (kWave - 1)) == lane) taken[t] |= 1u << (e / kWave);
+      if (lane == j) {
+        my_e[t] = e;
+        my_l[t] = lg[t][e];
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    if (t >= valid) break;
+    const float m = __shfl(my_l[t], 0, kWave);
+    float s;
+    if (renorm) {
+      s = wave_sum(lane < k ? expf(my_l[t] - m) : 0.f);
+    } else {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < kMaxExpertsPerLane; ++i)
+        if (lane + kWave * i < N) part += expf(v[t][i] - m);
+      s = wave_sum(part);
+    }
+    if (lane < k) {
+      idx_out[t * k + lane] = my_e[t];
+      w_out[t * k + lane] = expf(my_l[t] - m) / s;
+    }
+  }
+}
+
 // In-place butterfly reduce-scatter over the 64 lanes: afterwards each lane
 // holds max(V/64, 1) fully reduced values. Returns the index (in 0..V) of
 // v[0]; v[i] is index + i. When V < 64, 64/V lanes hold each value.
@@ -230,57 +305,93 @@ __global__ __launch_bounds__(kBlock) void gate_select_kernel(const float* __rest
     select_token(lg[wave], N, k, renorm, topk_idx + (int64_t)tok * k, topk_w + (int64_t)tok * k);
 }
 
-// Cosine gate from the projection z = x P (fp32, [T, p], p <= 256). A block
-// works on batches of kCosTok tokens; experts are staged through LDS in
-// groups of 64 (one per lane) with a padded row stride so that lanes
-// reading different rows hit different banks.
-constexpr int kCosTW = 8;                              // tokens per wave
-constexpr int kCosTok = kCosTW * kWavesPerBlock;       // tokens per batch
+// Cosine gate from the projection z = x P (fp32, [T, p], p <= 256). Experts
+// are staged through LDS in groups of 64 (one per lane) with a padded row
+// stride so that lanes reading different rows hit different banks; with
+// N <= 64 (one group) the table and its norms are staged once per block and
+// each wave then walks its own token batches without block barriers.
+constexpr int kCosTW = 8;                              // tokens per wave per batch
 constexpr int kCosMaxP = 256;
 constexpr int kCosPad = 4;
 
 __global__ __launch_bounds__(kBlock) void cosine_select_kernel(CosineParams p) {
-  __shared__ __attribute__((aligned(16))) float zs[kCosTok][kCosMaxP];
+  __shared__ __attribute__((aligned(16))) float zs[kWavesPerBlock][kCosTW][kCosMaxP];
   __shared__ __attribute__((aligned(16))) float es[kWave][kCosMaxP + kCosPad];
-  __shared__ float lg[kCosTok][kWave * kMaxExpertsPerLane];
-  __shared__ float znorm[kCosTok];
+  __shared__ float lg[kWavesPerBlock][kCosTW][kWave * kMaxExpertsPerLane];
   __shared__ float enorm[kWave];
 
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int P = p.p, N = p.N, T = p.T;
   const int groups = (N + kWave - 1) / kWave;
-  const int nbatch = (T + kCosTok - 1) / kCosTok;
+  const int nbatch = (T + kCosTW - 1) / kCosTW;
 
-  for (int b = blockIdx.x; b < nbatch; b += gridDim.x) {
-    const int tb = b * kCosTok;
-    // stage z rows and their norms (each wave its own kCosTW tokens)
-    for (int t = 0; t < kCosTW; ++t) {
-      const int tl = wave * kCosTW + t, tok = tb + tl;
-      float ss = 0.f;
-      for (int c = lane; c < P; c += kWave) {
-        const float v = tok < T ? p.z[(int64_t)tok * P + c] : 0.f;
-        zs[tl][c] = v;
-        ss += v * v;
-      }
-      ss = wave_sum(ss);
-      if (lane == 0) znorm[tl] = fmaxf(sqrtf(ss), 1e-12f);
+  auto stage_group = [&](int g) {
+    // 16-byte copies of the group's rows (P is a multiple of 8)
+    const int q4 = P / 4;
+    for (int i = threadIdx.x; i < kWave * q4; i += kBlock) {
+      const int r = i / q4, c = (i % q4) * 4, e = g * kWave + r;
+      *reinterpret_cast<f32x4*>(&es[r][c]) =
+          e < N ? *reinterpret_cast<const f32x4*>(p.emb + (int64_t)e * P + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // norms: each wave takes 16 rows, lanes split the row
+    for (int r = wave * (kWave / kWavesPerBlock); r < (wave + 1) * (kWave / kWavesPerBlock); ++r) {
+      const int e = g * kWave + r;
+      float ss = 0.f;
+      if (e < N)
+        for (int c = lane; c < P; c += kWave) {
+          const float v = p.emb[(int64_t)e * P + c];
+          ss += v * v;
+        }
+      ss = wave_sum(ss);
+      if (lane == 0) enorm[r] = fmaxf(sqrtf(ss), 1e-12f);
+    }
+    __syncthreads();
+  };
+  if (groups == 1) stage_group(0);
+
+  // each wave takes batches wave-major over the whole grid; with several
+  // expert groups the block moves in step (the table is re-staged per group)
+  const int wstride = gridDim.x * kWavesPerBlock;
+  const int nb_iter = groups == 1 ? nbatch : (nbatch + wstride - 1) / wstride * wstride;
+  for (int b = blockIdx.x * kWavesPerBlock + wave; b < nb_iter; b += wstride) {
+    const int t0 = b * kCosTW;
+    const bool live = b < nbatch;
+    float (*z)[kCosMaxP] = zs[wave];
+    // this wave's z rows and their norms (read only by this wave): all loads
+    // first, so that they are in flight together
+    constexpr int ZPL = kCosMaxP / kWave;
+    float zv[kCosTW][ZPL];
+#pragma unroll
+    for (int t = 0; t < kCosTW; ++t)
+#pragma unroll
+      for (int i = 0; i < ZPL; ++i) {
+        const int tok = t0 + t, c = lane + kWave * i;
+        zv[t][i] = (live && tok < T && c < P) ? p.z[(int64_t)tok * P + c] : 0.f;
+      }
+    float zn[kCosTW];
+#pragma unroll
+    for (int t = 0; t < kCosTW; ++t) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < ZPL; ++i) {
+        z[t][lane + kWave * i] = zv[t][i];
+        ss += zv[t][i] * zv[t][i];
+      }
+      zn[t] = ss;
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+#pragma unroll
+      for (int t = 0; t < kCosTW; ++t) zn[t] += __shfl_xor(zn[t], m, kWave);
+#pragma unroll
+    for (int t = 0; t < kCosTW; ++t) zn[t] = fmaxf(sqrtf(zn[t]), 1e-12f);
     for (int g = 0; g < groups; ++g) {
-      __syncthreads();  // es is about to be overwritten
-      // stage expert group g
-      for (int i = threadIdx.x; i < kWave * P; i += kBlock) {
-        const int r = i / P, c = i % P, e = g * kWave + r;
-        es[r][c] = e < N ? p.emb[(int64_t)e * P + c] : 0.f;
+      if (groups > 1) {
+        __syncthreads();  // everyone done with the previous group
+        stage_group(g);
       }
-      __syncthreads();
-      if (wave == 0) {
-        float ss = 0.f;
-        for (int c = 0; c < P; ++c) ss += es[lane][c] * es[lane][c];
-        enorm[lane] = fmaxf(sqrtf(ss), 1e-12f);
-      }
-      __syncthreads();
-      // lane = expert of the group; kCosTW tokens per wave
+      // lane = expert of the group
       float acc[kCosTW];
 #pragma unroll
       for (int t = 0; t < kCosTW; ++t) acc[t] = 0.f;
@@ -288,7 +399,7 @@ __global__ __launch_bounds__(kBlock) void cosine_select_kernel(CosineParams p) {
         const f32x4 ev = *reinterpret_cast<const f32x4*>(&es[lane][c]);
 #pragma unroll
         for (int t = 0; t < kCosTW; ++t) {
-          const f32x4 zv = *reinterpret_cast<const f32x4*>(&zs[wave * kCosTW + t][c]);
+          const f32x4 zv = *reinterpret_cast<const f32x4*>(&z[t][c]);
           acc[t] += zv[0] * ev[0] + zv[1] * ev[1] + zv[2] * ev[2] + zv[3] * ev[3];
         }
       }
@@ -297,23 +408,17 @@ __global__ __launch_bounds__(kBlock) void cosine_select_kernel(CosineParams p) {
         const float en = enorm[lane];
         const float bias = p.logit_bias ? p.logit_bias[e] : 0.f;
 #pragma unroll
-        for (int t = 0; t < kCosTW; ++t) {
-          const int tl = wave * kCosTW + t;
-          const float cosv = acc[t] / (znorm[tl] * en);
-          lg[tl][e] = cosv * p.inv_temperature + bias;
-        }
+        for (int t = 0; t < kCosTW; ++t) lg[wave][t][e] = acc[t] / (zn[t] * en) * p.inv_temperature + bias;
       }
     }
-    __syncthreads();
-    for (int t = 0; t < kCosTW; ++t) {
-      const int tl = wave * kCosTW + t, tok = tb + tl;
-      if (tok >= T) break;
-      if (p.logits)
-        for (int e = lane; e < N; e += kWave) p.logits[(int64_t)tok * N + e] = lg[tl][e];
-      select_token(lg[tl], N, p.k, p.renorm, p.topk_idx + (int64_t)tok * p.k,
-                   p.topk_w + (int64_t)tok * p.k);
-    }
-    __syncthreads();  // zs / lg reuse by the next batch
+    if (!live) continue;
+    __builtin_amdgcn_wave_barrier();
+    const int valid = min(kCosTW, T - t0);
+    if (p.logits)
+      for (int t = 0; t < valid; ++t)
+        for (int e = lane; e < N; e += kWave) p.logits[(int64_t)(t0 + t) * N + e] = lg[wave][t][e];
+    select_tokens<kCosTW>(lg[wave], valid, N, p.k, p.renorm, p.topk_idx + (int64_t)t0 * p.k,
+                          p.topk_w + (int64_t)t0 * p.k);
   }
 }
 
@@ -353,8 +458,9 @@ hipError_t launch_gate_plain_noisy(const GateParams& p, bool bf16_, bool noisy, 
 }
 
 hipError_t launch_cosine_select(const CosineParams& p, hipStream_t s) {
-  const int nbatch = (p.T + kCosTok - 1) / kCosTok;
-  const int grid = nbatch < 1024 ? nbatch : 1024;
+  const int nbatch = (p.T + kCosTW - 1) / kCosTW;
+  const int want = (nbatch + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int grid = want < 256 ? want : 256;  // persistent: one block per CU stages the table once
   hipLaunchKernelGGL(cosine_select_kernel, dim3(grid), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }

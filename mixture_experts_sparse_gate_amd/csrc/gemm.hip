@@ -387,35 +387,38 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
 
 constexpr int kNumCUs = 256;
 
-// Tile shapes: the largest tile that still gives every CU a block, judged
-// from the row bound M (the routing itself is only known on the device).
-// Few rows per expert (decode) take thin row tiles that stream the weights
-// with deep prefetch. Cfg<elem, out, BM, BN, waves M x N, K chunks/stage, stages>.
+// Tile shapes, judged from the rows a group can hold (the routing itself is
+// only known on the device): avg_rows = T*k/N, max_rows = the capacity.
+// 256 x 256 tiles (8 waves of 128 x 64) when groups can reach ~1536 rows,
+// so that the partly filled last row tile of each group wastes little, and
+// there are enough tiles to give every CU a block; otherwise 128 x 128
+// (2 blocks per CU). Few rows per group on average (decode) take thin row
+// tiles that stream the weights with deep prefetch.
+// Cfg<elem, out, BM, BN, waves M x N, K chunks per stage, stages, GELU>.
 template <typename E, typename O, bool G>
-hipError_t launch_dtype(const GemmParams& p, int avg_rows, hipStream_t s) {
+hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStream_t s) {
   if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, 8, 4, G>>(p, s);
   const int groups = p.seg ? p.groups : 0;
-  auto tiles = [&](int bm, int bn) {
-    return (int64_t)(p.M / bm + groups) * ((p.Ncols + bn - 1) / bn);
-  };
-  if (tiles(256, 256) >= kNumCUs) return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s);
+  const int64_t tiles256 = (int64_t)(p.M / 256 + groups) * ((p.Ncols + 255) / 256);
+  if (max_rows >= 1536 && tiles256 >= kNumCUs)
+    return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s);
   return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16_, int avg_rows,
-                               hipStream_t s) {
+                               int max_rows, hipStream_t s) {
   switch (kind) {
     case GemmKind::kFfn1Gelu:
-      return bf16_ ? launch_dtype<bf16, bf16, true>(p, avg_rows, s)
-                   : launch_dtype<float, float, true>(p, avg_rows, s);
+      return bf16_ ? launch_dtype<bf16, bf16, true>(p, avg_rows, max_rows, s)
+                   : launch_dtype<float, float, true>(p, avg_rows, max_rows, s);
     case GemmKind::kFfn2:
-      return bf16_ ? launch_dtype<bf16, bf16, false>(p, avg_rows, s)
-                   : launch_dtype<float, float, false>(p, avg_rows, s);
+      return bf16_ ? launch_dtype<bf16, bf16, false>(p, avg_rows, max_rows, s)
+                   : launch_dtype<float, float, false>(p, avg_rows, max_rows, s);
     case GemmKind::kProjF32:
-      return bf16_ ? launch_dtype<bf16, float, false>(p, avg_rows, s)
-                   : launch_dtype<float, float, false>(p, avg_rows, s);
+      return bf16_ ? launch_dtype<bf16, float, false>(p, avg_rows, max_rows, s)
+                   : launch_dtype<float, float, false>(p, avg_rows, max_rows, s);
   }
   return hipErrorInvalidValue;
 }

@@ -64,8 +64,9 @@ struct GemmParams {
   int groups, K, Ncols;
 };
 enum class GemmKind { kFfn1Gelu, kFfn2, kProjF32 };
+// avg_rows / max_rows: expected and largest rows per group (tile choice only)
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, int avg_rows,
-                               hipStream_t s);
+                               int max_rows, hipStream_t s);
 
 // ---- combine (combine.hip)
 struct CombineParams {
