@@ -13,12 +13,24 @@ when few rows per expert make it weight-streaming bound.
 
 Prints one JSON line. The CPU oracle is timed afterwards on the host cores
 on a bounded sample of the same workload (kind "oracle").
+
+The measured HBM traffic of the expert FFN comes from two rocprofv3 --pmc
+runs of this script (FETCH_SIZE, then WRITE_SIZE, with --calib-copy-mib so
+that a device copy of known size calibrates both counters), condensed by
+
+    python bench.py --summarize <results.db> --kind traffic --workload W --out profiles/...
+
+into profiles/grouped_gemm_<workload>_traffic.txt. That figure is used only
+while the file's hash of the GEMM source matches the current source.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
+import sqlite3
 import sys
 import time
 
@@ -32,8 +44,37 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X published figures
 
 
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_sparse_gate_amd", "csrc", "gemm.hip")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"grouped_gemm_{workload}_traffic.txt")
+
+
+def read_traffic(workload: str):
+    """HBM bytes per FFN step from the committed PMC summary, if it was taken
+    on the current GEMM source."""
+    path = traffic_path(workload)
+    if not os.path.exists(path):
+        return None, "no summary"
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            m = re.match(r"^(\w+):\s*(\S+)", line)
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None, "GEMM source changed since the counters were taken"
+    return float(fields["ffn_hbm_bytes_per_step"]), path
 
 
 def main() -> int:
@@ -44,9 +85,18 @@ def main() -> int:
     ap.add_argument("--workload", default="noisy_top2_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON with measured HBM bytes per FFN step (from rocprofv3 --pmc)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--summarize", default=None, help="rocprofv3 results.db to condense (no GPU)")
+    ap.add_argument("--kind", choices=["stats", "traffic"], default="stats")
+    ap.add_argument("--fetch-db", default=None, help="with --kind traffic: the FETCH_SIZE results.db")
+    ap.add_argument("--write-db", default=None, help="with --kind traffic: the WRITE_SIZE results.db")
+    ap.add_argument("--command", default="", help="command line recorded in the summary")
+    ap.add_argument("--out", default=None)
     args = ap.parse_args()
+
+    if args.summarize or args.kind == "traffic" and args.fetch_db:
+        return summarize(args)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -68,6 +118,14 @@ def main() -> int:
     log(f"[bench] {spec.name}: inputs ready in {time.perf_counter() - t_gen:.1f}s")
 
     stream = torch.cuda.current_stream()
+    if args.calib_copy_mib > 0:
+        # a plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read
+        # for it calibrates the counters (the only 1-byte-element copy here)
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev=None):
         if ev:
@@ -133,13 +191,11 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": ffn_flops / ffn_s / 1e12, "peak": MFMA_PEAK_TFLOPS[spec.dtype],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "grouped_gemm_kernel x2 (GEMM1+GELU, GEMM2) per step"
-    roof["traffic"] = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        if tr.get("workload") == spec.name:
-            roof["traffic"] = tr.get("ffn_hbm_bytes_per_step")
+    roof["kernel"] = "grouped_gemm_kernel, launched twice per step (GEMM1+GELU, GEMM2); duration from HIP events around moe_expert_ffn"
+    roof["algorithmic"] = {"flops": ffn_flops, "touched_weight_bytes": touched_weight_bytes}
+    traffic, tsrc = read_traffic(spec.name)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = tsrc
 
     gate_bytes = T * d * s + (2 if spec.gate == "noisy" else 1) * d * N * s * (spec.gate != "cosine") \
         + (d * spec.proj_dim * s if spec.gate == "cosine" else 0) + T * k * 8
@@ -217,6 +273,82 @@ def cpu_baseline(spec, inp, target_s: float):
             f"oracle forward over the first {sub_T} of {T} tokens (same capacity factor)")
     return {"value": sub_T * reps / el, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{what}, {reps} repetition(s), {el:.1f} s, fp64 NumPy"}
+
+
+# ---------------------------------------------------------------- summaries
+
+def _kernel_rows(db):
+    c = sqlite3.connect(db)
+    return list(c.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
+
+
+def _short(name: str) -> str:
+    m = re.search(r"grouped_gemm_kernel.*?Cfg<([^>]*)>", name)
+    if m:
+        return "grouped_gemm_kernel<" + m.group(1) + ">"
+    m = re.search(r"CfgI(\w+?)EEEEEvNS_10GemmParamsE", name)
+    if m:
+        return "grouped_gemm_kernel<" + m.group(1) + ">"
+    for key in ("gate_logits_kernel", "gate_select_kernel", "cosine_select_kernel", "count_kernel",
+                "scan_kernel", "slots_kernel", "permute_kernel", "combine_kernel"):
+        if key in name:
+            return key
+    return name[:70]
+
+
+def _pmc_per_kernel(db, counter):
+    c = sqlite3.connect(db)
+    rows = c.execute("select dispatch_id, kernel_name, grid_size, sum(value) from counters_collection "
+                     "where counter_name = ? group by dispatch_id", (counter,))
+    return [(d, n, g, v) for d, n, g, v in rows]
+
+
+def summarize(args):
+    lines = [f"command: {args.command}"] if args.command else []
+    if args.kind == "stats":
+        lines.append(f"source: rocprofv3 --kernel-trace --stats (top_kernels of {os.path.basename(args.summarize)})")
+        lines.append(f"{'kernel':70s} {'calls':>6s} {'total_us':>12s} {'avg_us':>10s} {'%':>7s}")
+        for n, calls, tot, avg, pct in _kernel_rows(args.summarize):
+            lines.append(f"{_short(n):70s} {calls:6d} {tot:12.1f} {avg:10.2f} {pct:7.2f}")
+    else:
+        out = {}
+        for tag, db, counter in (("fetch", args.fetch_db, "FETCH_SIZE"), ("write", args.write_db, "WRITE_SIZE")):
+            rows = _pmc_per_kernel(db, counter)
+            copies = [v for d, n, g, v in rows if "copy" in n.lower() and "bfloat16" not in n.lower()]
+            calib_kib = max(copies) if copies else None
+            # expert-FFN launches only (GEMM1, GEMM2 alternate); the cosine
+            # gate's projection (bf16 in, fp32 out: "DF16bf" in the name) is not
+            gemm = [v for d, n, g, v in rows if "grouped_gemm_kernel" in n and "DF16bfLi" not in n]
+            out[tag] = dict(calib_kib=calib_kib, gemm_kib=gemm)
+        mib = None
+        if args.command:
+            m = re.search(r"--calib-copy-mib\s+(\d+)", args.command)
+            mib = int(m.group(1)) if m else None
+        known_kib = (mib or 0) * 1024
+        lines.append("source: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch)")
+        res = {}
+        for tag in ("fetch", "write"):
+            o = out[tag]
+            fac = known_kib / o["calib_kib"] if o["calib_kib"] and known_kib else float("nan")
+            g = o["gemm_kib"]
+            per_step = [g[i] + g[i + 1] for i in range(0, len(g) - 1, 2)]
+            steady = per_step[len(per_step) // 2:] or per_step
+            kib = sum(steady) / max(len(steady), 1)
+            res[tag] = kib * fac * 1024
+            lines.append(f"{tag}_calib_copy_kib: {o['calib_kib']}")
+            lines.append(f"{tag}_scale_factor: {fac:.4f}")
+            lines.append(f"{tag}_ffn_kib_per_step_raw: {kib:.1f}")
+        lines.append(f"workload: {args.workload}")
+        lines.append(f"ffn_hbm_bytes_per_step: {res['fetch'] + res['write']:.0f}")
+        lines.append(f"ffn_hbm_read_bytes_per_step: {res['fetch']:.0f}")
+        lines.append(f"ffn_hbm_write_bytes_per_step: {res['write']:.0f}")
+        lines.append(f"gemm_source_sha256_16: {gemm_source_hash()}")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
 
 
 if __name__ == "__main__":
