@@ -99,18 +99,26 @@ struct Cfg {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 32, FN = WTN / 32;
   static constexpr bool GELU = GELU_;
+  // With 64-byte activation rows per K-step (KC = 4) one stage would use
+  // half of each 128-byte cache line, and the other half, needed one step
+  // later, has usually left the L1 by then. Such configurations load the
+  // activation tile for two K-steps at once (AP = 2) into two buffers of
+  // 128-byte rows, while the weight tile keeps its ring of S stages.
+  static constexpr int AP = (KC == 4 && S == 4) ? 2 : 1;  // K-steps per activation stage
+  static constexpr int KCA = KC * AP;                    // 16-byte chunks per activation row per stage
   static constexpr int B_CPR = BN * ES / 16;             // 16-byte chunks per weight row
-  static constexpr int A_STAGE = BM * KC * 16;           // activation tile, K-contiguous rows
+  static constexpr int A_STAGE = BM * KCA * 16;          // activation tile, K-contiguous rows
   static constexpr int B_STAGE = BK * B_CPR * 16;        // weight tile, N-contiguous rows
-  static constexpr int A_INST = BM * KC / THREADS;       // 16-byte loads per thread per stage
-  static constexpr int B_INST = BK * B_CPR / THREADS;
+  static constexpr int A_INST = BM * KCA / THREADS;      // 16-byte loads per thread per activation stage
+  static constexpr int B_INST = BK * B_CPR / THREADS;    // ... per weight stage
   static constexpr int LOADS = A_INST + B_INST;
+  static constexpr int LDS_BYTES = AP == 1 ? S * (A_STAGE + B_STAGE) : 2 * A_STAGE + S * B_STAGE;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(KC == 4 || KC == 8, "activation rows of 4 or 8 chunks");
-  static_assert(BM * KC % THREADS == 0 && BK * B_CPR % THREADS == 0, "loads must divide evenly");
+  static_assert(BM * KCA % THREADS == 0 && BK * B_CPR % THREADS == 0, "loads must divide evenly");
   static_assert(B_CPR >= (ES == 2 ? 16 : 8) && WTN % 64 == 0, "weight rows of at least 256 (bf16) or 128 (fp32) bytes, wave tiles of 64 columns");
-  static_assert(S >= 2 && S <= 4 && S * (A_STAGE + B_STAGE) <= 160 * 1024, "LDS budget");
-  static_assert(LOADS * (S - 2) < 64, "vmcnt range");
+  static_assert(S >= 2 && S <= 4 && LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(LOADS * (S - 2) < 64 && A_INST + 2 * B_INST < 64, "vmcnt range");
 };
 
 // Chunk swizzles, for gfx950's LDS as measured with bank-conflict counters:
@@ -138,14 +146,20 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   using E = typename C::Elem;
   using O = typename C::Out;
   constexpr int CE = C::CE, KC = C::KC, BK = C::BK, BM = C::BM, BN = C::BN, ES = C::ES, S = C::S;
+  constexpr int AP = C::AP, KCA = C::KCA;
   // one LDS object per stage, so that the compiler can tell a stage being
-  // filled by the asynchronous loads from the one being read
-  // (activation tile at offset 0, weight tile at A_STAGE)
-  constexpr int ST = C::A_STAGE + C::B_STAGE;
+  // filled by the asynchronous loads from the one being read. AP == 1: stage
+  // i holds the activation tile at offset 0 and the weight tile at A_STAGE.
+  // AP == 2: st0..st3 hold weight tiles only; sa0/sa1 hold activation tiles
+  // for K-step pairs (0,1) and (2,3) of each group of four.
+  constexpr int ST = AP == 1 ? C::A_STAGE + C::B_STAGE : C::B_STAGE;
+  constexpr int SA = AP == 1 ? 16 : C::A_STAGE;
   __shared__ __attribute__((aligned(1024))) char st0[ST];
   __shared__ __attribute__((aligned(1024))) char st1[ST];
   __shared__ __attribute__((aligned(1024))) char st2[S > 2 ? ST : 16];
   __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? ST : 16];
+  __shared__ __attribute__((aligned(1024))) char sa0[SA];
+  __shared__ __attribute__((aligned(1024))) char sa1[SA];
   __shared__ int sched[4];
 
   const int tid = threadIdx.x;
@@ -241,7 +255,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
 #pragma unroll
   for (int i = 0; i < C::A_INST; ++i) {
     const int slot = i * C::THREADS + tid;
-    const int r = slot / KC, c = (slot % KC) ^ swz_a<KC>(r);
+    const int r = slot / KCA, c = (slot % KCA) ^ swz_a<KCA>(r);
     a_off[i] = (r * lda + c * CE) * ES;
   }
 #pragma unroll
@@ -250,17 +264,30 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_b<ES>(k);
     b_off[i] = (k * Ncols + c * CE) * ES;
   }
-  auto issue = [&](char* sa, char* sb, int k0) {
+  auto issue_a = [&](char* sa, int k0) {
     const int64_t ab = a_bytes - (int64_t)k0 * ES;
-    const int64_t bb = b_bytes - (int64_t)k0 * Ncols * ES;
     const __amdgpu_buffer_rsrc_t ar = make_rsrc(At + (int64_t)k0 * ES, (uint32_t)(ab > 0 ? ab : 0));
-    const __amdgpu_buffer_rsrc_t br = make_rsrc(Bt + (int64_t)k0 * Ncols * ES, (uint32_t)(bb > 0 ? bb : 0));
 #pragma unroll
     for (int i = 0; i < C::A_INST; ++i)
       lds_load16(ar, (lds_void*)(sa + (i * C::THREADS + wave * kWave) * 16), a_off[i]);
+  };
+  auto issue_b = [&](char* sb, int k0) {
+    const int64_t bb = b_bytes - (int64_t)k0 * Ncols * ES;
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(Bt + (int64_t)k0 * Ncols * ES, (uint32_t)(bb > 0 ? bb : 0));
 #pragma unroll
     for (int i = 0; i < C::B_INST; ++i)
       lds_load16(br, (lds_void*)(sb + (i * C::THREADS + wave * kWave) * 16), b_off[i]);
+  };
+  // stage i's buffers (i constant, so that each access names its LDS object)
+  auto a_stage = [&](auto i) -> char* {
+    constexpr int v = decltype(i)::value;
+    if constexpr (AP == 2) return (v / 2) % 2 == 0 ? sa0 : sa1;
+    else return v == 0 ? st0 : v == 1 ? st1 : v == 2 ? st2 : st3;
+  };
+  auto b_stage = [&](auto i) -> char* {
+    constexpr int v = decltype(i)::value;
+    char* const base = v == 0 ? st0 : v == 1 ? st1 : v == 2 ? st2 : st3;
+    return AP == 2 ? base : base + C::A_STAGE;
   };
 
   f32x16 acc[C::FN][C::FM];
@@ -275,10 +302,12 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   const int lrow = lane & 31, lhalf = lane >> 5;
   // activation fragment (MFMA second operand): row wm*WTM + 32j + lane%32,
   // chunk 2s + lane/32 (swizzled); one offset per substep
+  // (AP == 2: the first K-step of a pair; the second reads chunk + KC, and as
+  // the swizzle only permutes the low three chunk bits, that is offset ^ 64)
   int fa_off[KC / 2];
 #pragma unroll
   for (int ss = 0; ss < KC / 2; ++ss)
-    fa_off[ss] = (wm * C::WTM + lrow) * KC * 16 + (((2 * ss + lhalf) ^ swz_a<KC>(lrow)) * 16);
+    fa_off[ss] = (wm * C::WTM + lrow) * KCA * 16 + (((2 * ss + lhalf) ^ swz_a<KCA>(lrow)) * 16);
   // weight fragment, bf16: 16-lane group q, lane r in it: rows 16s + 8(q/2) + 4p + r/4,
   // columns wn*WTN + 32i + 16(q%2) + 4(r%4) .. +3; the row's swizzle depends on r/4 only
   const int q16 = lane >> 4, r16 = lane & 15;
@@ -295,10 +324,10 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     fw32[e] = (4 * lhalf + e) * C::B_CPR * 16 + (wn * C::WTN / 4 + ((lrow >> 2) ^ swz_b<ES>(e))) * 16 + (lrow & 3) * 4;
 
   u32x4 fa[2][C::FN], fb[2][C::FM];
-  auto load_frags = [&](const char* sa, const char* sb, int ss, int buf) {
+  auto load_frags = [&](const char* sa, const char* sb, int ss, int buf, int hi) {
 #pragma unroll
     for (int j = 0; j < C::FM; ++j)
-      fb[buf][j] = *(lds_u32x4*)(sa + fa_off[ss] + j * 32 * KC * 16);
+      fb[buf][j] = *(lds_u32x4*)(sa + (fa_off[ss] ^ hi) + j * 32 * KCA * 16);
     if constexpr (ES == 2) {
 #pragma unroll
       for (int i = 0; i < C::FN; ++i) {
@@ -316,11 +345,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
           fa[buf][i][e] = *(lds_u32*)(sb + fw32[e] + (8 * ss) * C::B_CPR * 16 + i * 128);
     }
   };
-  auto compute = [&](const char* sa, const char* sb) {
-    load_frags(sa, sb, 0, 0);
+  auto compute = [&](const char* sa, const char* sb, int hi) {
+    load_frags(sa, sb, 0, 0, hi);
 #pragma unroll
     for (int ss = 0; ss < KC / 2; ++ss) {
-      if (ss + 1 < KC / 2) load_frags(sa, sb, ss + 1, (ss + 1) & 1);
+      if (ss + 1 < KC / 2) load_frags(sa, sb, ss + 1, (ss + 1) & 1, hi);
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -332,24 +361,37 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   // loads have landed (later steps' loads may still be in flight), barrier
   // (everyone's loads visible; everyone done with the previous stage), start
   // the loads S-1 steps ahead into the stage just freed, compute.
+  // AP == 2 (S == 4): even steps also start the activation pair two steps
+  // ahead, before their weight loads, into the buffer the previous pair
+  // used. At an even step the pair's loads and this step's weights sit
+  // behind two steps of weight loads; at an odd step this step's weights
+  // sit behind two weight loads and one activation pair.
   const int nk = (K + BK - 1) / BK;
-  issue(st0, st0 + C::A_STAGE, 0);
-  if constexpr (S > 2) issue(st1, st1 + C::A_STAGE, BK);
-  if constexpr (S > 3) issue(st2, st2 + C::A_STAGE, 2 * BK);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  issue_a(a_stage(I0{}), 0);
+  issue_b(b_stage(I0{}), 0);
+  if constexpr (S > 2) {
+    if constexpr (AP == 1) issue_a(a_stage(I1{}), BK);
+    issue_b(b_stage(I1{}), BK);
+  }
+  if constexpr (S > 3) {
+    if constexpr (AP == 1) issue_a(a_stage(I2{}), 2 * BK);
+    issue_b(b_stage(I2{}), 2 * BK);
+  }
   auto step = [&](auto st, int kt) {
     constexpr int cur = decltype(st)::value;
     constexpr int nxt = (cur + S - 1) % S;
-    wait_vmcnt<C::LOADS * (S - 2)>();
+    if constexpr (AP == 1) wait_vmcnt<C::LOADS * (S - 2)>();
+    else if constexpr (cur % 2 == 0) wait_vmcnt<2 * C::B_INST>();
+    else wait_vmcnt<C::A_INST + 2 * C::B_INST>();
     __builtin_amdgcn_s_barrier();
     const int kn = (kt + S - 1) * BK;
-    if constexpr (nxt == 0) issue(st0, st0 + C::A_STAGE, kn);
-    else if constexpr (nxt == 1) issue(st1, st1 + C::A_STAGE, kn);
-    else if constexpr (nxt == 2) issue(st2, st2 + C::A_STAGE, kn);
-    else issue(st3, st3 + C::A_STAGE, kn);
-    if constexpr (cur == 0) compute(st0, st0 + C::A_STAGE);
-    else if constexpr (cur == 1) compute(st1, st1 + C::A_STAGE);
-    else if constexpr (cur == 2) compute(st2, st2 + C::A_STAGE);
-    else compute(st3, st3 + C::A_STAGE);
+    if constexpr (AP == 1) issue_a(a_stage(std::integral_constant<int, nxt>{}), kn);
+    else if constexpr (cur % 2 == 0) issue_a(a_stage(std::integral_constant<int, (cur + 2) % 4>{}), (kt + 2) * BK);
+    issue_b(b_stage(std::integral_constant<int, nxt>{}), kn);
+    compute(a_stage(st), b_stage(st), (AP == 2 && (cur & 1)) ? 64 : 0);
   };
   // whole groups of S steps run as one straight-line loop body: steps guarded
   // by a branch inside the body make the compiler merge its load tracking at
