@@ -362,10 +362,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   // (everyone's loads visible; everyone done with the previous stage), start
   // the loads S-1 steps ahead into the stage just freed, compute.
   // AP == 2 (S == 4): even steps also start the activation pair two steps
-  // ahead, before their weight loads, into the buffer the previous pair
-  // used. At an even step the pair's loads and this step's weights sit
-  // behind two steps of weight loads; at an odd step this step's weights
-  // sit behind two weight loads and one activation pair.
+  // ahead into the buffer the previous pair used. The counts hold whatever
+  // order the compiler gives the loads within a step: an even step waits for
+  // everything but the previous step's weight loads (this step's pair was
+  // started two steps back), an odd step for everything but the last two
+  // steps' loads (its weights were started three steps back, by an even step).
   const int nk = (K + BK - 1) / BK;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -384,7 +385,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     constexpr int cur = decltype(st)::value;
     constexpr int nxt = (cur + S - 1) % S;
     if constexpr (AP == 1) wait_vmcnt<C::LOADS * (S - 2)>();
-    else if constexpr (cur % 2 == 0) wait_vmcnt<2 * C::B_INST>();
+    else if constexpr (cur % 2 == 0) wait_vmcnt<C::B_INST>();
     else wait_vmcnt<C::A_INST + 2 * C::B_INST>();
     __builtin_amdgcn_s_barrier();
     const int kn = (kt + S - 1) * BK;
@@ -392,6 +393,24 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     else if constexpr (cur % 2 == 0) issue_a(a_stage(std::integral_constant<int, (cur + 2) % 4>{}), (kt + 2) * BK);
     issue_b(b_stage(std::integral_constant<int, nxt>{}), kn);
     compute(a_stage(st), b_stage(st), (AP == 2 && (cur & 1)) ? 64 : 0);
+    if constexpr (ES == 2 && C::THREADS == 512) {
+      // (8-wave tiles) instruction order for the step: the first substep's LDS reads, then
+      // each MFMA followed by one of the next substep's LDS reads and, after
+      // every second MFMA, one of the step's global->LDS loads, so that the
+      // loads reach the address unit evenly spread over the step
+      constexpr int DSR = C::FM + 2 * C::FN;
+      constexpr int MF = C::FM * C::FN;
+      constexpr int VM = (AP == 1 || cur % 2 == 0) ? C::LOADS : C::B_INST;
+      __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);
+#pragma unroll
+      for (int ss = 0; ss < KC / 2; ++ss)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ss + 1 < KC / 2 && m < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if ((ss * MF + m) % 2 == 1 && (ss * MF + m) / 2 < VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
+    }
   };
   // whole groups of S steps run as one straight-line loop body: steps guarded
   // by a branch inside the body make the compiler merge its load tracking at
