@@ -96,7 +96,7 @@ moe_status_t maybe(const void* p, const char* name, size_t align) {
 // ---------------------------------------------------------------- workspace
 
 struct RouteWs {
-  size_t z, logits, bytes;
+  size_t z, logits, partial, bytes;
 };
 RouteWs route_ws(const moe_desc_t* d) {
   RouteWs w{};
@@ -105,6 +105,9 @@ RouteWs route_ws(const moe_desc_t* d) {
   if (d->gate == MOE_GATE_COSINE) o += align_up((size_t)d->T * d->proj_dim * 4);
   w.logits = o;
   o += align_up((size_t)d->T * d->N * 4);
+  w.partial = o;
+  if (d->gate != MOE_GATE_COSINE && d->dtype == MOE_BF16)
+    o += align_up(moe::gate_partial_bytes(d->T, d->d, d->N, d->gate == MOE_GATE_NOISY));
   w.bytes = o;
   return w;
 }
@@ -199,6 +202,7 @@ moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, co
   g.logits = logits ? logits : at<float>(ws, rw.logits);
   g.topk_idx = idx;
   g.topk_w = w;
+  g.partial = at<float>(ws, rw.partial);
   g.T = (int)d->T;
   g.d = d->d;
   g.N = d->N;

@@ -63,6 +63,18 @@ template <> struct Store<bf16> {
   }
 };
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+
+// Raw buffer descriptor (gfx9 family: word 3 = 0x00020000) over [base, base + bytes):
+// loads outside the range return zeros.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ inline u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ inline void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 

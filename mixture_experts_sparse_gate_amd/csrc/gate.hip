@@ -12,10 +12,17 @@
 // Weights: softmax over the k selected logits (renormalised) or over all N
 // (full probabilities), in fp32.
 //
-// The plain/noisy logits are a skinny product (N or 2N columns against
-// d-long rows of x): bound by reading x from HBM, so they run on the vector
-// ALUs with each wave's 64 lanes splitting d and a butterfly
-// reduce-scatter across lanes, not on MFMA.
+// The plain/noisy logits are the product x [W_g | W_n], skinny (N or 2N
+// columns against d-long rows of x) and bound by reading x. In bf16 it runs
+// on MFMA (32x32x16): blocks of four waves take 32 tokens and 32 columns over
+// a K slice, each wave a quarter of it, with the gate matrices' slice staged
+// in LDS and read back transposed (ds_read_b64_tr_b16); the waves' sums add
+// up in LDS and K slices (only as many as it takes to fill the chip) add up
+// in fixed order in the selection kernel, so the logits are deterministic.
+// The fp32 build keeps a vector-ALU kernel: each wave's 64 lanes split d and
+// a butterfly reduce-scatter across lanes sums them.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -74,6 +81,64 @@ __device__ void select_token(const float* lg, int N, int k, int renorm, int32_t*
   if (lane < k) {
     idx_out[lane] = my_e;
     w_out[lane] = expf(my_l - m) / s;
+  }
+}
+
+// Top-k selection and weights for one token by a single lane, for N <= 32
+// (same rules and the same (logit, index) key as select_token). The k
+// winners are found twice, once for the indices and the softmax
+// denominator, once for the weights, so that nothing is indexed by j.
+struct Pick {
+  uint32_t taken;  // experts taken so far, bit e
+  int e;           // the winner
+  float l;         // its logit
+};
+
+// The largest logit among the first N of v not yet taken, ties to the lower
+// index: candidates in ascending index, replaced only by a strictly larger
+// order key (the same order as select_token's (logit, -index) key).
+template <int NM>
+__device__ __forceinline__ Pick pick_next(const float (&v)[NM], int N, uint32_t taken) {
+  uint32_t best = 0;
+  int be = -1;
+  float bl = 0.f;
+#pragma unroll
+  for (int e = 0; e < NM; ++e) {
+    const uint32_t key = float_order_key(v[e]);
+    const bool better = e < N && !((taken >> e) & 1u) && (be < 0 || key > best);
+    best = better ? key : best;
+    be = better ? e : be;
+    bl = better ? v[e] : bl;
+  }
+  return Pick{taken | (1u << be), be, bl};
+}
+
+// Top-k selection and weights for one token by a single lane, N <= NM <= 32.
+// The k winners are found twice, once for the indices and the softmax
+// denominator, once for the weights, so that nothing is indexed by j.
+template <int NM>
+__device__ __forceinline__ void select_lane(const float* lg, int N, int k, int renorm, int32_t* idx_out,
+                                            float* w_out) {
+  float v[NM];
+#pragma unroll
+  for (int e = 0; e < NM; ++e) v[e] = e < N ? lg[e] : 0.f;
+  uint32_t taken = 0;
+  float m = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const Pick pk = pick_next(v, N, taken);
+    taken = pk.taken;
+    idx_out[j] = pk.e;
+    if (j == 0) m = pk.l;  // the largest logit
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < NM; ++e)
+    if (e < N && (!renorm || ((taken >> e) & 1u))) s += expf(v[e] - m);
+  uint32_t again = 0;
+  for (int j = 0; j < k; ++j) {
+    const Pick pk = pick_next(v, N, again);
+    again = pk.taken;
+    w_out[j] = expf(pk.l - m) / s;
   }
 }
 
@@ -422,6 +487,330 @@ __global__ __launch_bounds__(kBlock) void cosine_select_kernel(CosineParams p) {
   }
 }
 
+// ---- bf16 plain / noisy gate product on MFMA
+constexpr int kGtTok = 32;          // tokens per block (one MFMA tile)
+constexpr int kGtCols = 32;         // columns per chunk
+constexpr int kGtWaves = 4;         // waves per block, splitting the block's K slice
+constexpr int kGtMaxKr = 1024;      // K per slice at most: LDS rows of 64 bytes -> 64 KiB
+constexpr int kGtTargetBlocks = 256;
+
+struct GatePartialParams {
+  const bf16* x;
+  const bf16* wg;
+  const bf16* wn;
+  float* partial;  // [ks][T][ncc * 32]
+  int T, d, N, NC, ncp, kr;
+  bool vec;        // N % 8 == 0: 8 consecutive columns lie in one matrix, 16-byte aligned
+};
+
+// partial[z][t][c0 + c] = sum over k in slice z of x[t][k] * Wc[k][c0 + c],
+// Wc = [W_g | W_n] (columns past NC read as zeros). Grid: (token tiles,
+// column chunks, K slices); wave w covers quarter w of the slice.
+__global__ __launch_bounds__(kGtWaves * kWave) void gate_partial_kernel(GatePartialParams p) {
+  __shared__ __attribute__((aligned(1024))) char wl[kGtMaxKr * kGtCols * 2];
+  __shared__ __attribute__((aligned(16))) float red[kGtWaves][kGtTok][kGtCols];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * kGtTok;
+  const int c0 = blockIdx.y * kGtCols;
+  const int k_lo = blockIdx.z * p.kr;
+  const int nk = min(p.kr, p.d - k_lo);  // > 0: every slice starts inside d
+  const int krw = p.kr / kGtWaves;       // multiple of 16
+
+  // stage the slice's gate rows: row kk (k = k_lo + kk) as 32 bf16 columns,
+  // 64 bytes, zeros past d and past NC
+  for (int gi = threadIdx.x; gi < p.kr * 4; gi += kGtWaves * kWave) {
+    const int kk = gi >> 2, col = c0 + 8 * (gi & 3);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (kk < nk && col < p.NC) {
+      const int64_t k = k_lo + kk;
+      if (p.vec) {
+        v = col < p.N ? load16(p.wg + k * p.N + col) : load16(p.wn + k * p.N + (col - p.N));
+      } else {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = col + e;
+          const bf16* src = c < p.N ? p.wg + k * p.N + c : p.wn + k * p.N + (c - p.N);
+          h[e] = c < p.NC ? (uint32_t)__builtin_bit_cast(uint16_t, *src) : 0u;
+        }
+        v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      }
+    }
+    store16(wl + gi * 16, v);
+  }
+  __syncthreads();
+
+  // this wave: rows [wave * krw, wave * krw + krw) of the slice
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int q16 = lane >> 4, r16 = lane & 15;
+  // x fragment: token t0 + lrow, 8 K values from k_lo + kk + 8 lhalf; rows past T
+  // read zeros through the descriptor's range, K past d is masked below
+  const int rows = min(kGtTok, p.T - t0);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x + (int64_t)t0 * p.d, (uint32_t)((int64_t)rows * p.d * 2));
+  const int xoff = (lrow * p.d + k_lo + 8 * lhalf) * 2;
+  // gate fragment (transposing read): 16-lane group q, lane r: rows 8(q/2) + 4j + r/4
+  // of the 16-K step, columns 16(q%2) + 4(r%4) .. +3
+  const int woff = (8 * (q16 >> 1) + (r16 >> 2)) * 64 + 32 * (q16 & 1) + 8 * (r16 & 3);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int kw0 = wave * krw, kw1 = min(kw0 + krw, nk);
+  constexpr int U = 4;
+  for (int kk = kw0; kk < kw1; kk += 16 * U) {
+    u32x4 xv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kk + 16 * u;
+      // a 16-K step past the wave's rows, or the half of one past d, reads nothing
+      xv[u] = (k + 8 * lhalf < kw1) ? __builtin_amdgcn_raw_buffer_load_b128(xr, xoff + k * 2, 0, 0)
+                                     : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kk + 16 * u;
+      if (k >= kw1) break;
+      const char* w = wl + k * 64 + woff;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)w);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + 4 * 64));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      const u32x4 wf = u32x4{a[0], a[1], b[0], b[1]};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf),
+                                                    __builtin_bit_cast(bf16x8, xv[u]), acc, 0, 0, 0);
+    }
+  }
+  // lane holds token lrow, columns 8(r/4) + 4 lhalf + r%4
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<f32x4*>(&red[wave][lrow][8 * g + 4 * lhalf]) =
+        f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+  __syncthreads();
+  // the four quarters, added in order; 256 threads x 4 columns
+  const int tt = threadIdx.x >> 3, cc = (threadIdx.x & 7) * 4;
+  if (t0 + tt < p.T) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(&red[0][tt][cc]);
+#pragma unroll
+    for (int w = 1; w < kGtWaves; ++w) v += *reinterpret_cast<const f32x4*>(&red[w][tt][cc]);
+    *reinterpret_cast<f32x4*>(p.partial + ((int64_t)blockIdx.z * p.T + t0 + tt) * p.ncp + c0 + cc) = v;
+  }
+}
+
+// Logits from the K slices' partial products (added in slice order), then
+// selection; one wave per token, lanes over the columns.
+template <bool NOISY>
+__global__ __launch_bounds__(kBlock) void gate_finish_kernel(const float* __restrict__ partial, int ks,
+                                                             int ncp, GateParams p) {
+  __shared__ float lg[kWavesPerBlock][kWave * kMaxExpertsPerLane];
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int tok = blockIdx.x * kWavesPerBlock + wave;
+  if (tok >= p.T) return;  // no block barrier below
+  const int N = p.N;
+  const int64_t slice = (int64_t)p.T * ncp;
+  const float* src = partial + (int64_t)tok * ncp;
+  // slices added in order, eight loads in flight at a time
+  auto sum_slices = [&](int c) {
+    float l = src[c];
+    int z = 1;
+    for (; z + 8 <= ks; z += 8) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t[i] = src[(z + i) * slice + c];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) l += t[i];
+    }
+    for (; z < ks; ++z) l += src[z * slice + c];
+    return l;
+  };
+  for (int c = lane; c < N; c += kWave) {
+    float l = sum_slices(c);
+    if (NOISY) l += p.noise[(int64_t)tok * N + c] * softplusf(sum_slices(N + c));
+    if (p.logit_bias) l += p.logit_bias[c];
+    if (p.logits) p.logits[(int64_t)tok * N + c] = l;
+    lg[wave][c] = l;
+  }
+  // the wave reads back what its own lanes wrote: LDS keeps one wave's
+  // operations in order, the compiler keeps their program order
+  select_token(lg[wave], N, p.k, p.renorm, p.topk_idx + (int64_t)tok * p.k, p.topk_w + (int64_t)tok * p.k);
+}
+
+// One kernel for gates of at most 32 logit columns (N <= 32 plain, N <= 16
+// noisy): 32 tokens per block, the 8 waves splitting d. Each wave stages its
+// own gate rows (128 at a time) in its own LDS region and runs them through
+// the MFMA; the waves' sums add up in LDS in wave order, then the block
+// forms the logits and selects for its 32 tokens.
+constexpr int kGfWaves = 8;
+constexpr int kGfRows = 128;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // past any descriptor's range
+
+template <bool NOISY>
+__global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartialParams q, int krw,
+                                                                       GateParams p) {
+  __shared__ __attribute__((aligned(1024))) char wl[kGfWaves][kGfRows * kGtCols * 2];
+  __shared__ __attribute__((aligned(16))) float red[kGfWaves][kGtTok][kGtCols];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * kGtTok;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int q16 = lane >> 4, r16 = lane & 15;
+  const int rows = min(kGtTok, q.T - t0);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(q.x + (int64_t)t0 * q.d, (uint32_t)((int64_t)rows * q.d * 2));
+  const int xoff = (lrow * q.d + 8 * lhalf) * 2;
+  const int woff = (8 * (q16 >> 1) + (r16 >> 2)) * 64 + 32 * (q16 & 1) + 8 * (r16 & 3);
+  char* const mine = wl[wave];
+  const uint32_t wbytes = (uint32_t)((int64_t)q.d * q.N * 2);
+  const __amdgpu_buffer_rsrc_t wgr = make_rsrc(q.wg, wbytes);
+  const __amdgpu_buffer_rsrc_t wnr = make_rsrc(q.wn, wbytes);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int kw0 = wave * krw, kw1 = min(kw0 + krw, q.d);
+  constexpr int U = kGfRows / 16;         // 16-K steps per chunk
+  constexpr int G = kGfRows * 4 / kWave;  // 16-byte gate granules per lane per chunk
+  // one chunk's x fragments and gate rows; an offset past a descriptor's
+  // range reads zeros (x past the wave's rows; gate granules of the other
+  // matrix, past NC or past the wave's rows), so chunks past the end load
+  // nothing but zeros
+  auto load_chunk = [&](int kc, u32x4 (&xd)[U], u32x4 (&wd)[G]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = kc + 16 * u;
+      xd[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, (k + 8 * lhalf < kw1) ? xoff + k * 2 : (int)kOutOfRange, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int gi = i * kWave + lane;
+      const int kk = gi >> 2, col = 8 * (gi & 3);
+      const bool row_ok = kc + kk < kw1;
+      const uint32_t row = (uint32_t)(kc + kk) * q.N;
+      const uint32_t og = (row_ok && col < q.N) ? (row + col) * 2u : kOutOfRange;
+      const uint32_t on = (row_ok && col >= q.N && col < q.NC) ? (row + col - q.N) * 2u : kOutOfRange;
+      wd[i] = __builtin_amdgcn_raw_buffer_load_b128(wgr, (int)og, 0, 0);
+      if (NOISY) wd[i] |= __builtin_amdgcn_raw_buffer_load_b128(wnr, (int)on, 0, 0);
+    }
+  };
+  auto mfma_chunk = [&](const u32x4 (&xd)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const char* w = mine + 16 * u * 64 + woff;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)w);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + 4 * 64));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      const u32x4 wf = u32x4{a[0], a[1], b[0], b[1]};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf),
+                                                    __builtin_bit_cast(bf16x8, xd[u]), acc, 0, 0, 0);
+    }
+  };
+  if (q.vec) {
+    // steps past the wave's rows meet zero rows and zero x: they add nothing
+    u32x4 xv[U], wv[G];
+    load_chunk(kw0, xv, wv);
+    for (int kc = kw0; kc < kw1; kc += kGfRows) {
+      u32x4 xn[U], wn[G];
+      load_chunk(kc + kGfRows, xn, wn);  // in flight while this chunk computes
+#pragma unroll
+      for (int i = 0; i < G; ++i) store16(mine + (i * kWave + lane) * 16, wv[i]);
+      mfma_chunk(xv);
+#pragma unroll
+      for (int u = 0; u < U; ++u) xv[u] = xn[u];
+#pragma unroll
+      for (int i = 0; i < G; ++i) wv[i] = wn[i];
+    }
+  } else {
+    for (int kc = kw0; kc < kw1; kc += kGfRows) {
+      u32x4 xv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = kc + 16 * u;
+        xv[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, (k + 8 * lhalf < kw1) ? xoff + k * 2 : (int)kOutOfRange, 0, 0);
+      }
+      for (int gi = lane; gi < kGfRows * 4; gi += kWave) {
+        const int kk = gi >> 2, col = 8 * (gi & 3);
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = col + e;
+          const int64_t k = kc + kk;
+          const bf16* src = c < q.N ? q.wg + k * q.N + c : q.wn + k * q.N + (c - q.N);
+          h[e] = (kc + kk < kw1 && c < q.NC) ? (uint32_t)__builtin_bit_cast(uint16_t, *src) : 0u;
+        }
+        store16(mine + gi * 16,
+                u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
+      }
+      mfma_chunk(xv);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<f32x4*>(&red[wave][lrow][8 * g + 4 * lhalf]) =
+        f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+  __syncthreads();
+  // logits of the block's tokens (waves' sums in wave order), into LDS rows
+  // of 256 floats for the selection (the gate-row area is free now)
+  float (*lg)[kWave * kMaxExpertsPerLane] = reinterpret_cast<float (*)[kWave * kMaxExpertsPerLane]>(&wl[0][0]);
+  const int N = p.N;
+  for (int i = threadIdx.x; i < kGtTok * N; i += kGfWaves * kWave) {
+    const int t = i / N, c = i % N, tok = t0 + t;
+    if (tok >= p.T) continue;
+    float l = red[0][t][c];
+#pragma unroll
+    for (int w = 1; w < kGfWaves; ++w) l += red[w][t][c];
+    if (NOISY) {
+      float u = red[0][t][N + c];
+#pragma unroll
+      for (int w = 1; w < kGfWaves; ++w) u += red[w][t][N + c];
+      l += p.noise[(int64_t)tok * N + c] * softplusf(u);
+    }
+    if (p.logit_bias) l += p.logit_bias[c];
+    if (p.logits) p.logits[(int64_t)tok * N + c] = l;
+    lg[t][c] = l;
+  }
+  __syncthreads();
+  // selection: one lane per token
+  const int t = threadIdx.x;
+  if (t < kGtTok && t0 + t < p.T) {
+    int32_t* io = p.topk_idx + (int64_t)(t0 + t) * p.k;
+    float* wo = p.topk_w + (int64_t)(t0 + t) * p.k;
+    if (N <= 8) select_lane<8>(lg[t], N, p.k, p.renorm, io, wo);
+    else if (N <= 16) select_lane<16>(lg[t], N, p.k, p.renorm, io, wo);
+    else select_lane<32>(lg[t], N, p.k, p.renorm, io, wo);
+  }
+}
+
+hipError_t launch_gate_bf16(const GateParams& p, bool noisy, hipStream_t s) {
+  GatePartialParams g{};
+  g.x = static_cast<const bf16*>(p.x);
+  g.wg = static_cast<const bf16*>(p.w_gate);
+  g.wn = static_cast<const bf16*>(noisy ? p.w_noise : p.w_gate);
+  g.partial = p.partial;
+  g.T = p.T;
+  g.d = p.d;
+  g.N = p.N;
+  g.NC = noisy ? 2 * p.N : p.N;
+  g.vec = p.N % 8 == 0;
+  if (g.NC <= kGtCols) {
+    // one kernel: each wave takes a multiple of 16 of d
+    const int krw = ((p.d + kGfWaves - 1) / kGfWaves + 15) / 16 * 16;
+    const dim3 grid((p.T + kGtTok - 1) / kGtTok);
+    if (noisy)
+      hipLaunchKernelGGL((gate_fused_kernel<true>), grid, dim3(kGfWaves * kWave), 0, s, g, krw, p);
+    else
+      hipLaunchKernelGGL((gate_fused_kernel<false>), grid, dim3(kGfWaves * kWave), 0, s, g, krw, p);
+    return hipGetLastError();
+  }
+  const GateSplit sp = gate_split(p.T, p.d, p.N, noisy);
+  g.ncp = sp.ncc * kGtCols;
+  g.kr = sp.kr;
+  const dim3 grid((p.T + kGtTok - 1) / kGtTok, sp.ncc, sp.ks);
+  hipLaunchKernelGGL(gate_partial_kernel, grid, dim3(kGtWaves * kWave), 0, s, g);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const dim3 g2((p.T + kWavesPerBlock - 1) / kWavesPerBlock);
+  if (noisy)
+    hipLaunchKernelGGL((gate_finish_kernel<true>), g2, dim3(kBlock), 0, s, p.partial, sp.ks, g.ncp, p);
+  else
+    hipLaunchKernelGGL((gate_finish_kernel<false>), g2, dim3(kBlock), 0, s, p.partial, sp.ks, g.ncp, p);
+  return hipGetLastError();
+}
+
 template <typename E, int TW, bool NOISY>
 hipError_t launch_tw(const GateParams& p, hipStream_t s) {
   int ncb = 8;
@@ -452,8 +841,28 @@ hipError_t launch_e(const GateParams& p, hipStream_t s) {
 
 }  // namespace
 
+GateSplit gate_split(int64_t T, int d, int N, bool noisy) {
+  GateSplit sp{};
+  const int NC = noisy ? 2 * N : N;
+  sp.ncc = (NC + kGtCols - 1) / kGtCols;
+  const int64_t tiles = (T + kGtTok - 1) / kGtTok;
+  // as many K slices as it takes to reach ~kGtTargetBlocks blocks, each at
+  // least 64 deep and at most kGtMaxKr
+  const int64_t want = (kGtTargetBlocks + tiles * sp.ncc - 1) / (tiles * sp.ncc);
+  const int lo = (d + kGtMaxKr - 1) / kGtMaxKr, hi = (d + 63) / 64;
+  const int ks = (int)std::min<int64_t>(std::max<int64_t>(want, lo), hi);
+  sp.kr = ((d + ks - 1) / ks + 63) / 64 * 64;
+  sp.ks = (d + sp.kr - 1) / sp.kr;
+  return sp;
+}
+
+size_t gate_partial_bytes(int64_t T, int d, int N, bool noisy) {
+  const GateSplit sp = gate_split(T, d, N, noisy);
+  return (size_t)sp.ks * (size_t)T * sp.ncc * kGtCols * sizeof(float);
+}
+
 hipError_t launch_gate_plain_noisy(const GateParams& p, bool bf16_, bool noisy, hipStream_t s) {
-  if (bf16_) return noisy ? launch_e<bf16, true>(p, s) : launch_e<bf16, false>(p, s);
+  if (bf16_) return launch_gate_bf16(p, noisy, s);
   return noisy ? launch_e<float, true>(p, s) : launch_e<float, false>(p, s);
 }
 

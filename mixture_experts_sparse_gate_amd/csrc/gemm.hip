@@ -57,17 +57,6 @@ template <> struct Mfma<float> {
 
 __device__ inline float gelu_erf(float u) { return 0.5f * u * (1.f + erff(u * 0.70710678118654752f)); }
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-typedef __attribute__((address_space(3))) const uint32_t lds_u32;
-
-// Raw buffer descriptor (gfx9 family: word 3 = 0x00020000) over [base, base + bytes).
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // 16 bytes per lane from the buffer at byte offset voff straight into LDS:
 // lane l writes dst + 16 l (dst is wave-uniform). Out-of-range reads write zeros.
 __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void* dst, int voff) {

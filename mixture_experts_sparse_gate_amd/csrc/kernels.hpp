@@ -18,9 +18,18 @@ struct GateParams {
   float* logits;           // [T, N] (required when N exceeds one column block)
   int32_t* topk_idx;       // [T, k]
   float* topk_w;           // [T, k]
+  float* partial;          // bf16 only: gate_partial_bytes() of scratch for the split product
   int T, d, N, k, renorm;
 };
 hipError_t launch_gate_plain_noisy(const GateParams& p, bool bf16, bool noisy, hipStream_t s);
+
+// How the bf16 plain/noisy gate product x [W_g | W_n] is split: column
+// chunks of 32, K slices, and K per slice (a multiple of 64).
+struct GateSplit {
+  int ncc, ks, kr;
+};
+GateSplit gate_split(int64_t T, int d, int N, bool noisy);
+size_t gate_partial_bytes(int64_t T, int d, int N, bool noisy);
 
 struct CosineParams {
   const float* z;          // [T, p] fp32 projection x P
