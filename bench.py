@@ -3,13 +3,23 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step is one pass of the whole layer (gate, dispatch, expert FFN,
-combine) over one batch of seeded synthetic tokens, with every input already
-resident in HBM. The K timed steps are bracketed by torch.cuda.synchronize();
-HIP events recorded on the launch stream between the four stages give each
-stage's average duration inside the same timed region. The roofline object
-describes the expert FFN (the grouped-GEMM kernel, launched twice per step:
-GEMM1+GELU and GEMM2), against the bf16 MFMA peak, or against HBM bandwidth
-when few rows per expert make it weight-streaming bound.
+combine) over one batch of seeded synthetic tokens, through the single
+moe_forward entry point, with every input already resident in HBM. W warmup
+steps, then exactly K timed steps bracketed by torch.cuda.synchronize(); the
+headline value is T tokens over the mean step time.
+
+Besides the headline:
+  - stages: the same layer through the four stage entry points, with HIP
+    events recorded on the launch stream between them; their averages give
+    each stage's duration (and the expert FFN's for the roofline object);
+  - graph_ms_per_step: moe_forward captured once in a HIP graph and replayed
+    (no host launch cost per kernel);
+  - cold: each step timed alone by events after writing a 512 MiB buffer
+    (twice the last-level cache), median / p10 / p90.
+The roofline object describes the expert FFN (the grouped-GEMM kernel,
+launched twice per step: GEMM1+GELU and GEMM2), against the bf16 MFMA peak,
+or against HBM bandwidth when few rows per expert make it weight-streaming
+bound.
 
 Prints one JSON line. The CPU oracle is timed afterwards on the host cores
 on a bounded sample of the same workload (kind "oracle").
@@ -127,6 +137,9 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    def forward():
+        dev.run_forward(inspect=False)
+
     def step(ev=None):
         if ev:
             ev[0].record(stream)
@@ -146,32 +159,71 @@ def main() -> int:
         if ev:
             ev[4].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     K = args.steps
+    # ---- headline: K steps of moe_forward
+    for _ in range(args.warmup):
+        forward()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        forward()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+
+    # ---- stage breakdown through the four stage entry points
+    for _ in range(3):
+        step()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(events[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / K
+    staged_ms = (time.perf_counter() - t0) * 1e3 / K
     names = ["gate", "dispatch", "expert_ffn", "combine"]
     stage_ms = {n: float(np.mean([events[i][j].elapsed_time(events[i][j + 1]) for i in range(K)]))
                 for j, n in enumerate(names)}
 
-    # the whole layer through the single moe_forward entry point, same inputs
-    for _ in range(3):
-        dev.run_forward(inspect=False)
-    torch.cuda.synchronize()
-    tf0 = time.perf_counter()
-    for _ in range(K):
-        dev.run_forward(inspect=False)
-    torch.cuda.synchronize()
-    forward_ms = (time.perf_counter() - tf0) * 1e3 / K
+    # ---- moe_forward replayed from a HIP graph
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            forward()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            forward()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / K
+        del graph
+    except RuntimeError as e:  # capture unavailable: report the eager figures only
+        log(f"[bench] graph capture skipped: {e}")
+
+    # ---- cold caches: each step alone after a 512 MiB write
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(min(K, 20)):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        forward()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    cold.sort()
+    cold_ms = {"median_ms": cold[len(cold) // 2], "p10_ms": cold[len(cold) // 10],
+               "p90_ms": cold[(9 * len(cold)) // 10], "reps": len(cold)}
+    cold_ms["tokens_per_s"] = spec.T / (cold_ms["median_ms"] * 1e-3)
 
     # algorithmic work of one step, from this step's routing
     off = dev.expert_off.cpu().numpy().astype(np.int64)
@@ -232,7 +284,9 @@ def main() -> int:
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages": stages,
-        "moe_forward_ms": forward_ms,
+        "staged_ms_per_step": staged_ms,
+        "graph_ms_per_step": graph_ms,
+        "cold": cold_ms,
     }
     print(json.dumps(out), flush=True)
     return 0
