@@ -113,14 +113,13 @@ RouteWs route_ws(const moe_desc_t* d) {
 }
 
 struct DispatchWs {
-  size_t tile_counts, tile_base, bytes;
+  size_t tile_counts, bytes;
 };
 DispatchWs dispatch_ws(const moe_desc_t* d) {
   DispatchWs w{};
   const size_t t = (size_t)ntiles_of(d) * d->N * 4;
   w.tile_counts = 0;
-  w.tile_base = align_up(t);
-  w.bytes = 2 * align_up(t);
+  w.bytes = align_up(t);
   return w;
 }
 
@@ -219,7 +218,6 @@ moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx,
   p.x = x;
   p.topk_idx = idx;
   p.tile_counts = at<int32_t>(ws, dw.tile_counts);
-  p.tile_base = at<int32_t>(ws, dw.tile_base);
   p.expert_count = count;
   p.expert_off = off;
   p.row_of = row_of;

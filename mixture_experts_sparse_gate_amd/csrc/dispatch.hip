@@ -7,17 +7,18 @@
 // is kept iff that slot is below the capacity C, and then lands in row
 // off[e] + slot, off being the exclusive scan of kept = min(count, C).
 //
-// Three small index kernels compute this deterministically without any
+// Two small index kernels compute this deterministically without any
 // global atomics:
 //   count  one block per tile of kDispatchTile tokens: per-expert histogram
 //          of the tile in LDS (integer adds, so order does not matter)
-//   scan   one block: per expert, exclusive scan of the tile counts over the
-//          tiles (the tile's starting slot), totals, kept, offsets
-//   slots  one block per tile: in each 64-token wave chunk a lane's rank
-//          among earlier lanes with the same expert is a popcount of an LDS
-//          bitmask; chunk prefixes come from the other waves' masks and a
-//          running per-expert count
-// and a fourth kernel, permute, copies each token's row of x once into its
+//   rows   one block per tile, one token per thread: from all tiles' counts
+//          the block forms, per expert, the tile's starting slot (counts of
+//          the tiles before it), the totals, kept and the offsets (each
+//          block repeats this small scan instead of waiting for another);
+//          then in each 64-token wave a lane's rank among earlier lanes with
+//          the same expert is a popcount of an LDS bitmask, and the earlier
+//          waves' masks give the wave's own starting slot
+// and a third kernel, permute, copies each token's row of x once into its
 // kept rows with 16-byte loads and stores (one wave per token).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -44,24 +45,44 @@ __global__ __launch_bounds__(kBlock) void count_kernel(DispatchParams p) {
   for (int e = threadIdx.x; e < N; e += kBlock) p.tile_counts[blockIdx.x * N + e] = hist[e];
 }
 
-__global__ __launch_bounds__(kBlock) void scan_kernel(DispatchParams p, int ntiles) {
+static_assert(kDispatchTile == kBlock, "rows_kernel: one token per thread");
+
+__global__ __launch_bounds__(kBlock) void rows_kernel(DispatchParams p, int ntiles) {
+  __shared__ unsigned long long mask[kWaves][kMaxN];
+  __shared__ int start_s[kMaxN];
   __shared__ int kept_s[kMaxN];
-  const int N = p.N;
-  const int e = threadIdx.x;
-  int total = 0;
-  if (e < N) {
-    for (int t = 0; t < ntiles; ++t) {
+  __shared__ int off_s[kMaxN];
+  const int N = p.N, k = p.k, C = p.C;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int tile = blockIdx.x;
+  // per expert: slots taken by earlier tiles, total, kept
+  for (int e = threadIdx.x; e < N; e += kBlock) {
+    int before = 0, total = 0;
+    int t = 0;
+    for (; t + 8 <= ntiles; t += 8) {  // eight loads in flight
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = p.tile_counts[(t + i) * N + e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        before += t + i < tile ? c[i] : 0;
+        total += c[i];
+      }
+    }
+    for (; t < ntiles; ++t) {
       const int c = p.tile_counts[t * N + e];
-      p.tile_base[t * N + e] = total;
+      before += t < tile ? c : 0;
       total += c;
     }
-    p.expert_count[e] = total;
-    kept_s[e] = min(total, p.C);
+    start_s[e] = before;
+    kept_s[e] = min(total, C);
+    if (tile == 0) p.expert_count[e] = total;
   }
+  for (int i = threadIdx.x; i < kWaves * N; i += kBlock) mask[i / N][i % N] = 0ull;
   __syncthreads();
   // exclusive scan of kept over experts (N <= 256 values; wave 0 does it)
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
+  if (wave == 0) {
     int v[kMaxN / kWave];
     int sum = 0;
 #pragma unroll
@@ -70,7 +91,6 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(DispatchParams p, int ntil
       v[i] = ee < N ? kept_s[ee] : 0;
       sum += v[i];
     }
-    // inclusive scan of the per-lane sums
     int inc = sum;
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) {
@@ -81,60 +101,39 @@ __global__ __launch_bounds__(kBlock) void scan_kernel(DispatchParams p, int ntil
 #pragma unroll
     for (int i = 0; i < kMaxN / kWave; ++i) {
       const int ee = lane * (kMaxN / kWave) + i;
-      if (ee < N) p.expert_off[ee] = run;
+      if (ee < N) {
+        off_s[ee] = run;
+        if (tile == 0) p.expert_off[ee] = run;
+      }
       run += v[i];
     }
-    if (lane == kWave - 1) p.expert_off[N] = inc;
+    if (tile == 0 && lane == kWave - 1) p.expert_off[N] = inc;
   }
-}
-
-__global__ __launch_bounds__(kBlock) void slots_kernel(DispatchParams p) {
-  __shared__ unsigned long long mask[kWaves][kMaxN];
-  __shared__ int running[kMaxN];
-  __shared__ int off_s[kMaxN];
-  const int N = p.N, k = p.k, C = p.C;
-  const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
-  for (int e = threadIdx.x; e < N; e += kBlock) {
-    running[e] = p.tile_base[blockIdx.x * N + e];
-    off_s[e] = p.expert_off[e];
-  }
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  const int t_lo = blockIdx.x * kDispatchTile;
-  for (int r0 = t_lo; r0 < t_lo + kDispatchTile && r0 < p.T; r0 += kBlock) {
-    for (int i = threadIdx.x; i < kWaves * N; i += kBlock) mask[i / N][i % N] = 0ull;
-    __syncthreads();
-    const int t = r0 + threadIdx.x;
-    const bool live = t < p.T;
-    if (live) {
-      for (int j = 0; j < k; ++j) {
-        const int e = p.topk_idx[t * k + j];
-        if ((unsigned)e < (unsigned)N) atomicOr(&mask[wave][e], 1ull << lane);
-      }
+  // this tile's choices, as per-wave bitmasks per expert
+  const int t = tile * kDispatchTile + threadIdx.x;
+  const bool live = t < p.T;
+  if (live) {
+    for (int j = 0; j < k; ++j) {
+      const int e = p.topk_idx[t * k + j];
+      if ((unsigned)e < (unsigned)N) atomicOr(&mask[wave][e], 1ull << lane);
     }
-    __syncthreads();
-    if (live) {
-      for (int j = 0; j < k; ++j) {
-        const int e = p.topk_idx[t * k + j];
-        int row = -1;
-        if ((unsigned)e < (unsigned)N) {
-          int slot = running[e] + __popcll(mask[wave][e] & below);
-          for (int w = 0; w < wave; ++w) slot += __popcll(mask[w][e]);
-          if (slot < C) {
-            row = off_s[e] + slot;
-            p.token_of_row[row] = t * k + j;
-          }
+  }
+  __syncthreads();
+  if (live) {
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int j = 0; j < k; ++j) {
+      const int e = p.topk_idx[t * k + j];
+      int row = -1;
+      if ((unsigned)e < (unsigned)N) {
+        int slot = start_s[e] + __popcll(mask[wave][e] & below);
+        for (int w = 0; w < wave; ++w) slot += __popcll(mask[w][e]);
+        if (slot < C) {
+          row = off_s[e] + slot;
+          p.token_of_row[row] = t * k + j;
         }
-        p.row_of[t * k + j] = row;
       }
+      p.row_of[t * k + j] = row;
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < N; e += kBlock) {
-      int c = 0;
-      for (int w = 0; w < kWaves; ++w) c += __popcll(mask[w][e]);
-      running[e] += c;
-    }
-    __syncthreads();
   }
 }
 
@@ -175,8 +174,7 @@ __global__ __launch_bounds__(kBlock) void permute_kernel(DispatchParams p) {
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {
   const int ntiles = (p.T + kDispatchTile - 1) / kDispatchTile;
   hipLaunchKernelGGL(count_kernel, dim3(ntiles), dim3(kBlock), 0, s, p);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kBlock), 0, s, p, ntiles);
-  hipLaunchKernelGGL(slots_kernel, dim3(ntiles), dim3(kBlock), 0, s, p);
+  hipLaunchKernelGGL(rows_kernel, dim3(ntiles), dim3(kBlock), 0, s, p, ntiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.x_perm == nullptr) return err;
   return launch_permute(p, s);

@@ -55,7 +55,27 @@ template <> struct Mfma<float> {
   }
 };
 
-__device__ inline float gelu_erf(float u) { return 0.5f * u * (1.f + erff(u * 0.70710678118654752f)); }
+// GELU(u) = u Phi(u), Phi the standard normal CDF (the erf form of GELU).
+// For x = |u| / sqrt(2), Phi(u) = 1 - erfc(x)/2 (u >= 0) or erfc(x)/2 (u < 0),
+// with erfc(x) = R(t) exp(-x^2), t = 1 / (1 + 0.35 x) and R a degree-9
+// polynomial fitted to the scaled complement erfc(x) exp(x^2) on x in
+// [0, 9.3] (fit_gelu.py beside this file derives the constants). Relative
+// error below 2e-5 everywhere, including the negative tail that
+// 0.5 u (1 + erf(x)) loses to cancellation; about 20 VALU operations against
+// about 45 for erff and its two-path branch.
+__device__ inline float gelu_erf(float u) {
+  constexpr float c[10] = {-5.558532939e-05f, 1.986937672e-01f, 1.856181175e-01f, 2.510680556e-01f,
+                           -6.972948462e-02f, 6.612331271e-01f, -7.248843908e-01f, 8.268299699e-01f,
+                           -3.940122724e-01f, 6.523866206e-02f};
+  const float x = fabsf(u) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.35f, x, 1.f));
+  float r = c[9];
+#pragma unroll
+  for (int i = 8; i >= 0; --i) r = fmaf(r, t, c[i]);
+  // exp(-x^2) = 2^(-x^2 log2(e)); inputs below -126 give zero (u < -13.4 or > 13.4)
+  const float e = 0.5f * r * __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);
+  return u * (u >= 0.f ? 1.f - e : e);
+}
 
 // 16 bytes per lane from the buffer at byte offset voff straight into LDS:
 // lane l writes dst + 16 l (dst is wave-uniform). Out-of-range reads write zeros.
@@ -470,9 +490,14 @@ constexpr int kNumCUs = 256;
 template <typename E, typename O, bool G>
 hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStream_t s) {
   if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, 8, 4, G>>(p, s);
+  // 256x256 tiles (8 waves, one block per CU) need half the L1 bandwidth per
+  // flop of 128x128 ones; they are used once they give at least half as many
+  // tiles as CUs, except for a short-K GEMM with the GELU epilogue, where two
+  // 128x128 blocks per CU let one block's epilogue run beside the other's
+  // MFMAs (measured on the FFN shapes of the workloads)
   const int groups = p.seg ? p.groups : 0;
   const int64_t tiles256 = (int64_t)(p.M / 256 + groups) * ((p.Ncols + 255) / 256);
-  if (max_rows >= 1536 && tiles256 >= kNumCUs)
+  if (tiles256 >= kNumCUs / 2 && !(G && p.K <= 1024))
     return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s);
   return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s);
 }

@@ -44,12 +44,11 @@ struct CosineParams {
 hipError_t launch_cosine_select(const CosineParams& p, hipStream_t s);
 
 // ---- dispatch (dispatch.hip)
-constexpr int kDispatchTile = 1024;  // tokens per dispatch tile
+constexpr int kDispatchTile = 256;  // tokens per dispatch tile (one per thread of a block)
 struct DispatchParams {
   const void* x;            // [T, d]
   const int32_t* topk_idx;  // [T, k]
   int32_t* tile_counts;     // [nTiles, N] workspace
-  int32_t* tile_base;       // [nTiles, N] workspace
   int32_t* expert_count;    // [N]
   int32_t* expert_off;      // [N+1]
   int32_t* row_of;          // [T*k]

@@ -1,0 +1,73 @@
+"""The GELU of the expert FFN kernel (gemm.hip): its constants are the ones
+fit_gelu.py derives, and the formula, evaluated step by step in fp32, stays
+within its stated error of the exact GELU (scipy's erfc in fp64)."""
+import math
+import os
+import re
+import sys
+
+import numpy as np
+import pytest
+
+scipy_special = pytest.importorskip("scipy.special")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixture_experts_sparse_gate_amd", "csrc")
+
+
+def kernel_constants():
+    src = open(os.path.join(CSRC, "gemm.hip")).read()
+    m = re.search(r"constexpr float c\[10\] = \{([^}]*)\}", src)
+    assert m, "GELU constants not found in gemm.hip"
+    return np.array([float(v.strip().rstrip("f")) for v in m.group(1).split(",")], dtype=np.float32)
+
+
+def gelu_kernel_fp32(u, c):
+    f = np.float32
+    u = u.astype(f)
+    x = (np.abs(u) * f(0.70710678118654752)).astype(f)
+    t = (f(1) / (f(0.35) * x + f(1))).astype(f)
+    r = c[9]
+    for i in range(8, -1, -1):
+        r = (r * t + c[i]).astype(f)
+    e = (f(0.5) * r * np.exp2((-(x * x) * f(1.4426950408889634)).astype(f)).astype(f)).astype(f)
+    return (u * np.where(u >= 0, f(1) - e, e).astype(f)).astype(f)
+
+
+def gelu_exact(u):
+    u = u.astype(np.float64)
+    return 0.5 * u * scipy_special.erfc(-u / math.sqrt(2.0))
+
+
+def test_constants_come_from_the_fit():
+    sys.path.insert(0, CSRC)
+    try:
+        import fit_gelu
+    finally:
+        sys.path.pop(0)
+    np.testing.assert_array_equal(kernel_constants(), fit_gelu.fit())
+
+
+def test_error_against_exact_gelu():
+    c = kernel_constants()
+    u = np.linspace(-13.0, 13.0, 1_300_001).astype(np.float32)
+    got = gelu_kernel_fp32(u, c).astype(np.float64)
+    ref = gelu_exact(u)
+    nz = np.abs(ref) > 1e-30
+    rel = np.abs(got - ref)[nz] / np.abs(ref)[nz]
+    assert rel.max() < 5e-5
+    # special cases: GELU(0) = 0, GELU(u) -> u for large u, -> 0 for very negative u
+    z = gelu_kernel_fp32(np.array([0.0, 20.0, -20.0], dtype=np.float32), c)
+    assert z[0] == 0.0 and z[1] == np.float32(20.0) and z[2] == 0.0
+
+
+def test_bf16_rounding_matches_exact():
+    def bf16_bits(v):
+        b = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+        return (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+
+    c = kernel_constants()
+    u = np.linspace(-4.0, 4.0, 800_001).astype(np.float32)
+    got = gelu_kernel_fp32(u, c)
+    ref = gelu_exact(u)
+    assert np.mean(bf16_bits(got) != bf16_bits(ref)) < 1e-4
