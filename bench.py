@@ -95,6 +95,8 @@ def main() -> int:
     ap.add_argument("--workload", default="noisy_top2_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--skip-extras", action="store_true",
+                    help="time only the warm steps (no graph replay, no cold-cache steps): counter runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     ap.add_argument("--summarize", default=None, help="rocprofv3 results.db to condense (no GPU)")
@@ -187,6 +189,8 @@ def main() -> int:
     # ---- moe_forward replayed from a HIP graph
     graph_ms = None
     try:
+        if args.skip_extras:
+            raise RuntimeError("skipped (--skip-extras)")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -211,7 +215,7 @@ def main() -> int:
     # ---- cold caches: each step alone after a 512 MiB write
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     cold = []
-    for _ in range(min(K, 20)):
+    for _ in range(0 if args.skip_extras else min(K, 20)):
         flush.fill_(1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -221,9 +225,11 @@ def main() -> int:
         cold.append(a.elapsed_time(b))
     del flush
     cold.sort()
-    cold_ms = {"median_ms": cold[len(cold) // 2], "p10_ms": cold[len(cold) // 10],
-               "p90_ms": cold[(9 * len(cold)) // 10], "reps": len(cold)}
-    cold_ms["tokens_per_s"] = spec.T / (cold_ms["median_ms"] * 1e-3)
+    cold_ms = None
+    if cold:
+        cold_ms = {"median_ms": cold[len(cold) // 2], "p10_ms": cold[len(cold) // 10],
+                   "p90_ms": cold[(9 * len(cold)) // 10], "reps": len(cold)}
+        cold_ms["tokens_per_s"] = spec.T / (cold_ms["median_ms"] * 1e-3)
 
     # algorithmic work of one step, from this step's routing
     off = dev.expert_off.cpu().numpy().astype(np.int64)
