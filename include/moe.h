@@ -39,7 +39,10 @@
  *    fixed summation order in every reduction.
  *  - Sizes: 1 <= N <= 256, 1 <= k <= min(N, 32), T*k < 2^31, d and h
  *    multiples of 8 (bf16) or 4 (fp32), cosine proj_dim a multiple of 8 and
- *    at most 256.
+ *    at most 256. Outside those: MOE_ERR_INVALID. With s the element bytes,
+ *    T*max(d,h)*s, d*h*s and d*N*s (cosine: d*proj_dim*s) must each stay
+ *    below 2^31 bytes (the kernels' 32-bit buffer ranges); larger layers
+ *    get MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -191,7 +194,10 @@ typedef struct moe_layer_tensors {
 
 /* The whole layer: route, dispatch, expert FFN and combine, enqueued on one
  * stream with no host synchronisation (so it can be captured in a HIP
- * graph). ws: MOE_WS_FORWARD bytes; it holds x_perm, H, y_perm and every
+ * graph). Results are those of the four stage calls above, bitwise; the
+ * expert rows are gathered from x inside GEMM1's tile loads, so no x_perm
+ * copy is made (the row-grouped form of "MoE架构：稀疏激活机制如何提升模型计算
+ * 效率" §3.1, fused). ws: MOE_WS_FORWARD bytes; it holds H, y_perm and every
  * routing array the caller does not ask for. */
 MOE_API moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* tensors, void* ws,
                          size_t ws_bytes, void* stream);

@@ -71,6 +71,14 @@ moe_status_t check_desc(const moe_desc_t* d) {
     if (!isfinite(d->inv_temperature))
       return fail(MOE_ERR_INVALID, "inv_temperature must be finite");
   }
+  // the kernels address each operand through buffer descriptors with 32-bit
+  // byte ranges and offsets: every operand they cover stays below 2^31 bytes
+  const int64_t s = elem_bytes(d), lim = (int64_t)1 << 31;
+  const int64_t wide = d->d > d->h ? d->d : d->h;
+  const int64_t gate_cols = d->gate == MOE_GATE_COSINE ? d->proj_dim : d->N;
+  if (d->T * wide * s >= lim || (int64_t)d->d * d->h * s >= lim || (int64_t)d->d * gate_cols * s >= lim)
+    return fail(MOE_ERR_UNSUPPORTED, "T*max(d,h), d*h and d*%s must each stay below 2^31 bytes",
+                d->gate == MOE_GATE_COSINE ? "proj_dim" : "N");
   return MOE_OK;
 }
 
@@ -124,7 +132,7 @@ DispatchWs dispatch_ws(const moe_desc_t* d) {
 }
 
 struct ForwardWs {
-  size_t route, dispatch, topk_idx, topk_w, count, off, row_of, token_of_row, x_perm, H, y_perm,
+  size_t route, dispatch, topk_idx, topk_w, count, off, row_of, token_of_row, H, y_perm,
       bytes;
 };
 ForwardWs forward_ws(const moe_desc_t* d) {
@@ -144,7 +152,6 @@ ForwardWs forward_ws(const moe_desc_t* d) {
   w.off = take((size_t)(d->N + 1) * 4);
   w.row_of = take(Tk * 4);
   w.token_of_row = take(R * 4);
-  w.x_perm = take(R * d->d * s);
   w.H = take(R * d->h * s);
   w.y_perm = take(R * d->d * s);
   w.bytes = o;
@@ -232,15 +239,21 @@ moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx,
   return hip_status(moe::launch_dispatch(p, s), "dispatch");
 }
 
-moe_status_t do_ffn(const moe_desc_t* d, const void* x_perm, const int32_t* off, const void* W1,
-                    const void* b1, const void* W2, const void* b2, void* H, void* y_perm,
-                    hipStream_t s) {
+// A1: GEMM1's activation rows. With token_of_row null they are the rows of
+// x_perm; otherwise A1 is x itself and row r reads token token_of_row[r] / k
+// (the gather fused into GEMM1's tile loads, no x_perm round trip).
+moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of_row,
+                    const int32_t* off, const void* W1, const void* b1, const void* W2,
+                    const void* b2, void* H, void* y_perm, hipStream_t s) {
   const bool bf = d->dtype == MOE_BF16;
   const int R = (int)rows_bound_of(d);
   const int avg_rows = (int)((d->T * d->k) / d->N);
   const int max_rows = (int)capacity_of(d);
   moe::GemmParams g{};
-  g.A = x_perm;
+  g.A = A1;
+  g.gather = token_of_row;
+  g.gather_div = d->k;
+  g.a_rows = (int)d->T;
   g.B = W1;
   g.bias = b1;
   g.C = H;
@@ -256,6 +269,7 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* x_perm, const int32_t* off,
   TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s),
                  "expert GEMM1"));
   g.A = H;
+  g.gather = nullptr;
   g.B = W2;
   g.bias = b2;
   g.C = y_perm;
@@ -376,7 +390,7 @@ moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const in
   TRY(maybe(b2, "b2", 4));
   TRY(need(H, "H", 16));
   TRY(need(y_perm, "y_perm", 16));
-  return do_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, (hipStream_t)stream);
+  return do_ffn(desc, x_perm, nullptr, expert_off, W1, b1, W2, b2, H, y_perm, (hipStream_t)stream);
 }
 
 moe_status_t moe_combine(const moe_desc_t* desc, const void* y_perm, const int32_t* row_of,
@@ -416,13 +430,13 @@ moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, v
   int32_t* off = t->expert_off ? t->expert_off : at<int32_t>(ws, fw.off);
   int32_t* row_of = t->row_of ? t->row_of : at<int32_t>(ws, fw.row_of);
   int32_t* tor = t->token_of_row ? t->token_of_row : at<int32_t>(ws, fw.token_of_row);
-  void* x_perm = at<char>(ws, fw.x_perm);
   void* H = at<char>(ws, fw.H);
   void* y_perm = at<char>(ws, fw.y_perm);
   TRY(do_route(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb, t->logit_bias,
                t->logits, idx, w, at<char>(ws, fw.route), s));
-  TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, x_perm, at<char>(ws, fw.dispatch), s));
-  TRY(do_ffn(desc, x_perm, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, s));
+  // routing and row maps only: GEMM1 gathers its rows from x itself
+  TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s));
+  TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, s));
   return do_combine(desc, y_perm, row_of, w, t->y, s);
 }
 

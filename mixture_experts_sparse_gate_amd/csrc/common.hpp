@@ -74,6 +74,9 @@ typedef __attribute__((address_space(3))) const uint32_t lds_u32;
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// A buffer offset past the range of every descriptor here (all ranges are
+// below 2^31 bytes): a load at it reads zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 __device__ inline u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ inline void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -640,7 +640,6 @@ __global__ __launch_bounds__(kBlock) void gate_finish_kernel(const float* __rest
 // forms the logits and selects for its 32 tokens.
 constexpr int kGfWaves = 8;
 constexpr int kGfRows = 128;
-constexpr uint32_t kOutOfRange = 0x80000000u;  // past any descriptor's range
 
 template <bool NOISY>
 __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartialParams q, int krw,

@@ -246,9 +246,11 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   const int K = p.K, Ncols = p.Ncols;
   const int lda = (int)p.lda;
   const int rows = row_hi - row_lo;
-  const char* At = static_cast<const char*>(p.A) + (int64_t)row_lo * p.lda * ES;
+  // A rows of the tile: contiguous from row_lo, or gathered (then the
+  // descriptor spans all of A and each lane's offsets name its rows)
+  const char* At = static_cast<const char*>(p.A) + (p.gather ? 0 : (int64_t)row_lo * p.lda * ES);
   const char* Bt = static_cast<const char*>(p.B) + ((int64_t)g * p.strideB + n0) * ES;
-  const int64_t a_bytes = (int64_t)rows * lda * ES;
+  const int64_t a_bytes = (int64_t)(p.gather ? p.a_rows : rows) * lda * ES;
   const int64_t b_bytes = (int64_t)K * Ncols * ES - (int64_t)n0 * ES;
 
   // ---- asynchronous global -> LDS loads. Each 16-byte load of a wave lands
@@ -265,7 +267,13 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   for (int i = 0; i < C::A_INST; ++i) {
     const int slot = i * C::THREADS + tid;
     const int r = slot / KCA, c = (slot % KCA) ^ swz_a<KCA>(r);
-    a_off[i] = (r * lda + c * CE) * ES;
+    if (p.gather) {
+      // rows past the group read zeros: an offset past the descriptor's range
+      const int grow = row_lo + r;
+      a_off[i] = grow < row_hi ? ((p.gather[grow] / p.gather_div) * lda + c * CE) * ES : (int)kOutOfRange;
+    } else {
+      a_off[i] = (r * lda + c * CE) * ES;
+    }
   }
 #pragma unroll
   for (int i = 0; i < C::B_INST; ++i) {

@@ -67,6 +67,10 @@ struct GemmParams {
   const void* bias;     // per group [Ncols] (stride strideBias) or null
   void* C;              // rows of length Ncols, stride ldc elements
   const int32_t* seg;   // [groups+1] row offsets of each group (device); null = one group of M rows
+  // Gathered A rows: output row r reads A row gather[r] / gather_div, A holding
+  // a_rows rows (a_rows * lda * element bytes < 2^31). Null: output row r reads A row r.
+  const int32_t* gather;
+  int gather_div, a_rows;
   int64_t lda, ldc, strideB, strideBias;
   int M;                // rows when seg is null; else the row bound R
   int groups, K, Ncols;

@@ -175,3 +175,12 @@ def test_stage_argument_checks(lib):
     assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 4, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_dispatch(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw", [dict(T=1 << 20, d=1024, h=8192), dict(T=64, d=65536, h=32768),
+                                dict(T=4, d=1 << 23, h=8, N=256)])
+def test_layers_past_the_32bit_buffer_ranges_are_unsupported(lib, kw):
+    d = desc_from_spec(workloads.get("noisy_top2_bf16").with_(**kw))
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(d), _lib.MOE_WS_FORWARD, ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED
+    assert b"2^31" in lib.moe_last_error()
