@@ -9,27 +9,29 @@
 // ("MoE稀疏计算加速技术解析与应用实践" §3.2).
 //
 // Design for gfx950:
-//  - The block computes a BM x BN tile of C. MFMA 32x32 is used in the
+//  - The block computes a BM x BN tile of C. MFMA 32x32x16 is used in the
 //    transposed sense, D = B^T A^T: the weight tile is the MFMA's first
 //    operand and the activation rows its second, so each lane ends up with
 //    4 consecutive output columns of one row (8- or 16-byte stores).
-//  - Both tiles go to LDS as they lie in memory: activation rows
-//    K-contiguous, weight rows N-contiguous, copied with 16-byte loads and
-//    stores. The MFMA needs 8 consecutive K values of one weight column per
-//    lane; gfx950's LDS transpose read (ds_read_b64_tr_b16) delivers exactly
-//    that from the N-contiguous tile (two reads per 16-K fragment), so the
-//    weights are never transposed in registers or in memory. The fp32 build
-//    reads single elements instead (its MFMA takes one K value per lane).
-//  - LDS rows are padded (activation rows by 16 bytes, weight rows by 32) so
-//    that every fragment read is free of bank conflicts and every fragment
-//    address is one per-lane base plus compile-time offsets.
-//  - Two LDS stages: the next K-step's global loads are in flight while the
-//    current one feeds the MFMAs; within a step the fragment reads of
-//    substep s+1 overlap the MFMAs of substep s.
-//  - Ragged groups: the grid's x dimension is an upper bound on the number
-//    of row tiles; each block finds its (group, row range) from seg on the
-//    device, so no host synchronisation is needed. Blocks past the last tile
-//    exit at once.
+//  - Both tiles go global -> LDS with buffer_load_dwordx4 ... lds (no staging
+//    registers), as they lie in memory: activation rows K-contiguous, weight
+//    rows N-contiguous. The MFMA needs 8 consecutive K values of one weight
+//    column per lane; gfx950's LDS transpose read (ds_read_b64_tr_b16)
+//    delivers exactly that, so the weights are never transposed. The fp32
+//    build reads single elements instead (its MFMA takes one K value per lane).
+//  - 16-byte chunks are XOR-swizzled (swz_a, swz_b) so that every fragment
+//    read is free of bank conflicts on gfx950's LDS.
+//  - Four weight stages (three K-steps of loads in flight) and, for 64-byte
+//    activation rows, two buffers holding the activation tile of two K-steps
+//    each; within a step the fragment reads of substep s+1 overlap the MFMAs
+//    of substep s.
+//  - Ragged groups: the grid is an upper bound on the number of tiles; each
+//    block finds its (group, rows, columns) from seg on the device, so no host
+//    synchronisation is needed. A group's remainder of at most BM/2 rows goes
+//    to tail tiles of 32 rows per wave, scheduled after all full-height tiles.
+//    Blocks past the last tile exit at once.
+//  - GEMM1's activation rows can be gathered (row r reads A row
+//    gather[r] / gather_div) inside the tile loads.
 //  - No split-K and no atomics: each output element is written once.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -122,12 +124,19 @@ struct Cfg {
   static constexpr int B_INST = BK * B_CPR / THREADS;    // ... per weight stage
   static constexpr int LOADS = A_INST + B_INST;
   static constexpr int LDS_BYTES = AP == 1 ? S * (A_STAGE + B_STAGE) : 2 * A_STAGE + S * B_STAGE;
+  // Ragged tails: the rows of a group past its last full BM-row tile go to
+  // tiles of TBM = 32*WM rows (one 32-row fragment per wave), which load and
+  // multiply a quarter (BM = 256) of a full tile's activation rows.
+  static constexpr int TBM = 32 * WM;
+  static constexpr bool HAS_TAIL = AP == 2 && TBM < BM;
+  static constexpr int A_INST_T = HAS_TAIL ? TBM * KCA / THREADS : A_INST;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(KC == 4 || KC == 8, "activation rows of 4 or 8 chunks");
   static_assert(BM * KCA % THREADS == 0 && BK * B_CPR % THREADS == 0, "loads must divide evenly");
   static_assert(B_CPR >= (ES == 2 ? 16 : 8) && WTN % 64 == 0, "weight rows of at least 256 (bf16) or 128 (fp32) bytes, wave tiles of 64 columns");
   static_assert(S >= 2 && S <= 4 && LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS * (S - 2) < 64 && A_INST + 2 * B_INST < 64, "vmcnt range");
+  static_assert(!HAS_TAIL || (TBM * KCA % THREADS == 0 && A_INST_T >= 1), "tail tiles: whole loads per thread");
 };
 
 // Chunk swizzles, for gfx950's LDS as measured with bank-conflict counters:
@@ -169,70 +178,85 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? ST : 16];
   __shared__ __attribute__((aligned(1024))) char sa0[SA];
   __shared__ __attribute__((aligned(1024))) char sa1[SA];
-  __shared__ int sched[4];
+  __shared__ int sched[5];
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  // ---- tile schedule. Tiles are ordered group by group; within a group,
-  // n-tiles in runs of kGroupN, row tiles fastest within a run. The
+  // ---- tile schedule. A group's rows make full-height tiles of BM rows;
+  // with tail tiles (HAS_TAIL), a remainder of at most BM/2 rows makes
+  // tiles of TBM rows instead of one partial full-height tile. Phase 0 lists
+  // the full-height tiles, phase 1 the tail tiles, each group by group and,
+  // within a group, n-tiles in runs of kGroupN with row tiles fastest. Blocks
+  // take phase 0 first (the hardware starts blocks in index order), so a
+  // second round of tiles on the CUs is made of the cheap tail tiles. The
   // hardware hands blocks to the XCDs round-robin (block b -> XCD b % 8), so
-  // block b is given tile (b % 8) * per + b / 8: each XCD works through one
-  // contiguous stretch of that order, and the ~32 blocks it runs at a time
-  // share their weight slabs and activation rows in its own L2.
+  // within a phase block b takes tile (b % 8) * per + b / 8: each XCD works
+  // through one contiguous stretch of the phase, and the ~32 blocks it runs
+  // at a time share their weight slabs and activation rows in its own L2.
   if (wave == 0) {
     constexpr int GPL = 4;  // groups per lane (groups <= 256)
-    int cnt[GPL];
-    int sum = 0;
+    int lo[GPL], hi[GPL], nf[GPL], nt[GPL];
+    int sf = 0, st = 0;
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
       const int gi = lane * GPL + i;
-      cnt[i] = 0;
+      lo[i] = 0;
+      hi[i] = 0;
       if (p.seg == nullptr) {
-        if (gi == 0) cnt[i] = (p.M + BM - 1) / BM;
+        if (gi == 0) hi[i] = p.M;
       } else if (gi < p.groups) {
         // rows are clamped to [0, M] so that no offset table can address
         // outside the row buffers
-        const int lo = min(max(p.seg[gi], 0), p.M), hi = min(max(p.seg[gi + 1], lo), p.M);
-        cnt[i] = (hi - lo + BM - 1) / BM;
+        lo[i] = min(max(p.seg[gi], 0), p.M);
+        hi[i] = min(max(p.seg[gi + 1], lo[i]), p.M);
       }
-      sum += cnt[i];
+      const int n = hi[i] - lo[i], t = n % BM;
+      const bool small_tail = C::HAS_TAIL && t > 0 && t <= BM / 2;
+      nf[i] = n / BM + (t > 0 && !small_tail);
+      nt[i] = small_tail ? (t + C::TBM - 1) / C::TBM : 0;
+      sf += nf[i];
+      st += nt[i];
     }
-    int inc = sum;
+    int incf = sf, inct = st;
 #pragma unroll
     for (int m = 1; m < kWave; m <<= 1) {
-      const int o = __shfl_up(inc, m, kWave);
-      if (lane >= m) inc += o;
+      const int of = __shfl_up(incf, m, kWave), ot = __shfl_up(inct, m, kWave);
+      if (lane >= m) {
+        incf += of;
+        inct += ot;
+      }
     }
     const int NT = (p.Ncols + BN - 1) / BN;
-    const int total = __shfl(inc, kWave - 1, kWave) * NT;
-    const int per = (total + kNumXcds - 1) / kNumXcds;
-    const int b = blockIdx.x, local = b / kNumXcds;
+    const int F = __shfl(incf, kWave - 1, kWave) * NT, Tt = __shfl(inct, kWave - 1, kWave) * NT;
+    const int BF = (F + kNumXcds - 1) / kNumXcds * kNumXcds;  // blocks of phase 0
+    const int phase = (int)blockIdx.x >= BF;
+    const int b = blockIdx.x - (phase ? BF : 0);
+    const int count = phase ? Tt : F;
+    const int per = (count + kNumXcds - 1) / kNumXcds, local = b / kNumXcds;
     const int tile = (b % kNumXcds) * per + local;
-    const bool live = local < per && tile < total;
+    const bool live = local < per && tile < count;
     if (lane == 0 && !live) sched[0] = -1;
-    const int q = tile / NT;  // row tile in the concatenated order of all groups
-    int start = inc - sum;
+    const int q = tile / NT;  // row tile in the concatenated order of the phase
+    int start = phase ? inct - st : incf - sf;
 #pragma unroll
     for (int i = 0; i < GPL; ++i) {
-      if (live && q >= start && q < start + cnt[i]) {
-        const int gi = lane * GPL + i;
-        int lo = 0, hi = p.M;
-        if (p.seg != nullptr) {
-          lo = min(max(p.seg[gi], 0), p.M);
-          hi = min(max(p.seg[gi + 1], lo), p.M);
-        }
-        const int t = tile - start * NT;       // tile within the group
-        const int run = cnt[i] * kGroupN;      // tiles per run of kGroupN n-tiles
+      const int c = phase ? nt[i] : nf[i];
+      if (live && q >= start && q < start + c) {
+        const int t = tile - start * NT;  // tile within the group's part of the phase
+        const int run = c * kGroupN;      // tiles per run of kGroupN n-tiles
         const int ng = t / run, r = t % run;
         const int gn = min(kGroupN, NT - ng * kGroupN);
-        sched[0] = gi;
-        sched[1] = lo + (r / gn) * BM;
-        sched[2] = hi;
+        const int qr = r / gn;
+        const int r0 = phase ? lo[i] + (hi[i] - lo[i]) / BM * BM + qr * C::TBM : lo[i] + qr * BM;
+        sched[0] = lane * GPL + i;
+        sched[1] = r0;
+        sched[2] = min(r0 + (phase ? C::TBM : BM), hi[i]);
         sched[3] = (ng * kGroupN + r % gn) * BN;
+        sched[4] = phase;
       }
-      start += cnt[i];
+      start += c;
     }
   }
   __syncthreads();
@@ -243,6 +267,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   const int row_lo = __builtin_amdgcn_readfirstlane(sched[1]);
   const int row_hi = __builtin_amdgcn_readfirstlane(sched[2]);
   const int n0 = __builtin_amdgcn_readfirstlane(sched[3]);
+  const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[4]) != 0;
   const int K = p.K, Ncols = p.Ncols;
   const int lda = (int)p.lda;
   const int rows = row_hi - row_lo;
@@ -281,13 +306,6 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_b<ES>(k);
     b_off[i] = (k * Ncols + c * CE) * ES;
   }
-  auto issue_a = [&](char* sa, int k0) {
-    const int64_t ab = a_bytes - (int64_t)k0 * ES;
-    const __amdgpu_buffer_rsrc_t ar = make_rsrc(At + (int64_t)k0 * ES, (uint32_t)(ab > 0 ? ab : 0));
-#pragma unroll
-    for (int i = 0; i < C::A_INST; ++i)
-      lds_load16(ar, (lds_void*)(sa + (i * C::THREADS + wave * kWave) * 16), a_off[i]);
-  };
   auto issue_b = [&](char* sb, int k0) {
     const int64_t bb = b_bytes - (int64_t)k0 * Ncols * ES;
     const __amdgpu_buffer_rsrc_t br = make_rsrc(Bt + (int64_t)k0 * Ncols * ES, (uint32_t)(bb > 0 ? bb : 0));
@@ -307,180 +325,204 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     return AP == 2 ? base : base + C::A_STAGE;
   };
 
-  f32x16 acc[C::FN][C::FM];
+  // The K loop and the epilogue, for full tiles and (TAIL) for ragged-tail
+  // tiles of TBM rows: one 32-row fragment per wave and the first A_INST_T
+  // activation loads per thread; everything else is the same code.
+  auto run = [&](auto tail_c) {
+    constexpr bool TAIL = decltype(tail_c)::value;
+    constexpr int FM = TAIL ? 1 : C::FM;                 // 32-row fragments per wave
+    constexpr int WTM = TAIL ? 32 : C::WTM;              // rows per wave
+    constexpr int AI = TAIL ? C::A_INST_T : C::A_INST;   // activation loads per thread per stage
+    auto issue_a = [&](char* sa, int k0) {
+      const int64_t ab = a_bytes - (int64_t)k0 * ES;
+      const __amdgpu_buffer_rsrc_t ar = make_rsrc(At + (int64_t)k0 * ES, (uint32_t)(ab > 0 ? ab : 0));
 #pragma unroll
-  for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FM; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int i = 0; i < AI; ++i)
+        lds_load16(ar, (lds_void*)(sa + (i * C::THREADS + wave * kWave) * 16), a_off[i]);
+    };
 
-  // ---- per-lane fragment offsets within a stage
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  // activation fragment (MFMA second operand): row wm*WTM + 32j + lane%32,
-  // chunk 2s + lane/32 (swizzled); one offset per substep
-  // (AP == 2: the first K-step of a pair; the second reads chunk + KC, and as
-  // the swizzle only permutes the low three chunk bits, that is offset ^ 64)
-  int fa_off[KC / 2];
+    f32x16 acc[C::FN][FM];
 #pragma unroll
-  for (int ss = 0; ss < KC / 2; ++ss)
-    fa_off[ss] = (wm * C::WTM + lrow) * KCA * 16 + (((2 * ss + lhalf) ^ swz_a<KCA>(lrow)) * 16);
-  // weight fragment, bf16: 16-lane group q, lane r in it: rows 16s + 8(q/2) + 4p + r/4,
-  // columns wn*WTN + 32i + 16(q%2) + 4(r%4) .. +3; the row's swizzle depends on r/4 only
-  const int q16 = lane >> 4, r16 = lane & 15;
-  int fw[C::FN];
+    for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-  for (int i = 0; i < C::FN; ++i) {
-    const int chunk = wn * C::WTN / 8 + 4 * i + 2 * (q16 & 1) + ((r16 & 3) >> 1);
-    fw[i] = (8 * (q16 >> 1) + (r16 >> 2)) * C::B_CPR * 16 + (chunk ^ swz_b<ES>(r16 >> 2)) * 16 + 8 * (r16 & 1);
-  }
-  // weight fragment, fp32: row 8s + 4(lane/32) + e, column wn*WTN + 32i + lane%32
-  int fw32[4];
+      for (int j = 0; j < FM; ++j)
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    fw32[e] = (4 * lhalf + e) * C::B_CPR * 16 + (wn * C::WTN / 4 + ((lrow >> 2) ^ swz_b<ES>(e))) * 16 + (lrow & 3) * 4;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 fa[2][C::FN], fb[2][C::FM];
-  auto load_frags = [&](const char* sa, const char* sb, int ss, int buf, int hi) {
+    // ---- per-lane fragment offsets within a stage
+    const int lrow = lane & 31, lhalf = lane >> 5;
+    // activation fragment (MFMA second operand): row wm*WTM + 32j + lane%32,
+    // chunk 2s + lane/32 (swizzled); one offset per substep
+    // (AP == 2: the first K-step of a pair; the second reads chunk + KC, and as
+    // the swizzle only permutes the low three chunk bits, that is offset ^ 64)
+    int fa_off[KC / 2];
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j)
-      fb[buf][j] = *(lds_u32x4*)(sa + (fa_off[ss] ^ hi) + j * 32 * KCA * 16);
-    if constexpr (ES == 2) {
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i) {
-        const char* w = sb + fw[i];
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + (16 * ss) * C::B_CPR * 16));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + (16 * ss + 4) * C::B_CPR * 16));
-        const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
-        fa[buf][i] = u32x4{x[0], x[1], y[0], y[1]};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          fa[buf][i][e] = *(lds_u32*)(sb + fw32[e] + (8 * ss) * C::B_CPR * 16 + i * 128);
-    }
-  };
-  auto compute = [&](const char* sa, const char* sb, int hi) {
-    load_frags(sa, sb, 0, 0, hi);
-#pragma unroll
-    for (int ss = 0; ss < KC / 2; ++ss) {
-      if (ss + 1 < KC / 2) load_frags(sa, sb, ss + 1, (ss + 1) & 1, hi);
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FM; ++j) Mfma<E>::step(acc[i][j], fa[ss & 1][i], fb[ss & 1][j]);
-    }
-  };
-
-  // ---- S-stage pipeline, one barrier per K-step: wait until this step's
-  // loads have landed (later steps' loads may still be in flight), barrier
-  // (everyone's loads visible; everyone done with the previous stage), start
-  // the loads S-1 steps ahead into the stage just freed, compute.
-  // AP == 2 (S == 4): even steps also start the activation pair two steps
-  // ahead into the buffer the previous pair used. The counts hold whatever
-  // order the compiler gives the loads within a step: an even step waits for
-  // everything but the previous step's weight loads (this step's pair was
-  // started two steps back), an odd step for everything but the last two
-  // steps' loads (its weights were started three steps back, by an even step).
-  const int nk = (K + BK - 1) / BK;
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  issue_a(a_stage(I0{}), 0);
-  issue_b(b_stage(I0{}), 0);
-  if constexpr (S > 2) {
-    if constexpr (AP == 1) issue_a(a_stage(I1{}), BK);
-    issue_b(b_stage(I1{}), BK);
-  }
-  if constexpr (S > 3) {
-    if constexpr (AP == 1) issue_a(a_stage(I2{}), 2 * BK);
-    issue_b(b_stage(I2{}), 2 * BK);
-  }
-  auto step = [&](auto st, int kt) {
-    constexpr int cur = decltype(st)::value;
-    constexpr int nxt = (cur + S - 1) % S;
-    if constexpr (AP == 1) wait_vmcnt<C::LOADS * (S - 2)>();
-    else if constexpr (cur % 2 == 0) wait_vmcnt<C::B_INST>();
-    else wait_vmcnt<C::A_INST + 2 * C::B_INST>();
-    __builtin_amdgcn_s_barrier();
-    const int kn = (kt + S - 1) * BK;
-    if constexpr (AP == 1) issue_a(a_stage(std::integral_constant<int, nxt>{}), kn);
-    else if constexpr (cur % 2 == 0) issue_a(a_stage(std::integral_constant<int, (cur + 2) % 4>{}), (kt + 2) * BK);
-    issue_b(b_stage(std::integral_constant<int, nxt>{}), kn);
-    compute(a_stage(st), b_stage(st), (AP == 2 && (cur & 1)) ? 64 : 0);
-    if constexpr (ES == 2 && C::THREADS == 512) {
-      // (8-wave tiles) instruction order for the step: the first substep's LDS reads, then
-      // each MFMA followed by one of the next substep's LDS reads and, after
-      // every second MFMA, one of the step's global->LDS loads, so that the
-      // loads reach the address unit evenly spread over the step
-      constexpr int DSR = C::FM + 2 * C::FN;
-      constexpr int MF = C::FM * C::FN;
-      constexpr int VM = (AP == 1 || cur % 2 == 0) ? C::LOADS : C::B_INST;
-      __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);
-#pragma unroll
-      for (int ss = 0; ss < KC / 2; ++ss)
-#pragma unroll
-        for (int m = 0; m < MF; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (ss + 1 < KC / 2 && m < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          if ((ss * MF + m) % 2 == 1 && (ss * MF + m) / 2 < VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-        }
-    }
-  };
-  // whole groups of S steps run as one straight-line loop body: steps guarded
-  // by a branch inside the body make the compiler merge its load tracking at
-  // the loop head and drain every load in flight there once per iteration
-  int kt = 0;
-  for (; kt + S <= nk; kt += S) {
-    step(std::integral_constant<int, 0>{}, kt);
-    step(std::integral_constant<int, 1>{}, kt + 1);
-    if constexpr (S > 2) step(std::integral_constant<int, 2 % S>{}, kt + 2);
-    if constexpr (S > 3) step(std::integral_constant<int, 3 % S>{}, kt + 3);
-  }
-  if (kt < nk) step(std::integral_constant<int, 0>{}, kt);
-  if constexpr (S > 2) if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
-  if constexpr (S > 3) if (kt + 2 < nk) step(std::integral_constant<int, 2 % S>{}, kt + 2);
-  wait_vmcnt<0>();
-
-  // ---- epilogue: lane holds row m = .. + lane%32, columns n = .. + 8*(r/4) + 4*(lane/32) + r%4
-  O* Cp = static_cast<O*>(p.C);
-  const E* bias = p.bias ? static_cast<const E*>(p.bias) + (int64_t)g * p.strideBias : nullptr;
-#pragma unroll
-  for (int j = 0; j < C::FM; ++j) {
-    const int grow = row_lo + wm * C::WTM + j * 32 + lrow;
-    if (grow >= row_hi) continue;
+    for (int ss = 0; ss < KC / 2; ++ss)
+      fa_off[ss] = (wm * WTM + lrow) * KCA * 16 + (((2 * ss + lhalf) ^ swz_a<KCA>(lrow)) * 16);
+    // weight fragment, bf16: 16-lane group q, lane r in it: rows 16s + 8(q/2) + 4p + r/4,
+    // columns wn*WTN + 32i + 16(q%2) + 4(r%4) .. +3; the row's swizzle depends on r/4 only
+    const int q16 = lane >> 4, r16 = lane & 15;
+    int fw[C::FN];
 #pragma unroll
     for (int i = 0; i < C::FN; ++i) {
+      const int chunk = wn * C::WTN / 8 + 4 * i + 2 * (q16 & 1) + ((r16 & 3) >> 1);
+      fw[i] = (8 * (q16 >> 1) + (r16 >> 2)) * C::B_CPR * 16 + (chunk ^ swz_b<ES>(r16 >> 2)) * 16 + 8 * (r16 & 1);
+    }
+    // weight fragment, fp32: row 8s + 4(lane/32) + e, column wn*WTN + 32i + lane%32
+    int fw32[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = n0 + wn * C::WTN + i * 32 + 8 * q + 4 * lhalf;
-        if (col >= Ncols) continue;
-        float v[4];
+    for (int e = 0; e < 4; ++e)
+      fw32[e] = (4 * lhalf + e) * C::B_CPR * 16 + (wn * C::WTN / 4 + ((lrow >> 2) ^ swz_b<ES>(e))) * 16 + (lrow & 3) * 4;
+
+    u32x4 fa[2][C::FN], fb[2][FM];
+    auto load_frags = [&](const char* sa, const char* sb, int ss, int buf, int hi) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = acc[i][j][4 * q + r];
-          if (bias) v[r] += ElemTraits<E>::to_f32(bias[col + r]);
-          if (C::GELU) v[r] = gelu_erf(v[r]);
+      for (int j = 0; j < FM; ++j)
+        fb[buf][j] = *(lds_u32x4*)(sa + (fa_off[ss] ^ hi) + j * 32 * KCA * 16);
+      if constexpr (ES == 2) {
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+          const char* w = sb + fw[i];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + (16 * ss) * C::B_CPR * 16));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + (16 * ss + 4) * C::B_CPR * 16));
+          const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+          fa[buf][i] = u32x4{x[0], x[1], y[0], y[1]};
         }
-        Store<O>::four(Cp + grow * p.ldc + col, v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            fa[buf][i][e] = *(lds_u32*)(sb + fw32[e] + (8 * ss) * C::B_CPR * 16 + i * 128);
+      }
+    };
+    auto compute = [&](const char* sa, const char* sb, int hi) {
+      load_frags(sa, sb, 0, 0, hi);
+#pragma unroll
+      for (int ss = 0; ss < KC / 2; ++ss) {
+        if (ss + 1 < KC / 2) load_frags(sa, sb, ss + 1, (ss + 1) & 1, hi);
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j) Mfma<E>::step(acc[i][j], fa[ss & 1][i], fb[ss & 1][j]);
+      }
+    };
+
+    // ---- S-stage pipeline, one barrier per K-step: wait until this step's
+    // loads have landed (later steps' loads may still be in flight), barrier
+    // (everyone's loads visible; everyone done with the previous stage), start
+    // the loads S-1 steps ahead into the stage just freed, compute.
+    // AP == 2 (S == 4): even steps also start the activation pair two steps
+    // ahead into the buffer the previous pair used. The counts hold whatever
+    // order the compiler gives the loads within a step: an even step waits for
+    // everything but the previous step's weight loads (this step's pair was
+    // started two steps back), an odd step for everything but the last two
+    // steps' loads (its weights were started three steps back, by an even step).
+    const int nk = (K + BK - 1) / BK;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    issue_a(a_stage(I0{}), 0);
+    issue_b(b_stage(I0{}), 0);
+    if constexpr (S > 2) {
+      if constexpr (AP == 1) issue_a(a_stage(I1{}), BK);
+      issue_b(b_stage(I1{}), BK);
+    }
+    if constexpr (S > 3) {
+      if constexpr (AP == 1) issue_a(a_stage(I2{}), 2 * BK);
+      issue_b(b_stage(I2{}), 2 * BK);
+    }
+    auto step = [&](auto st, int kt) {
+      constexpr int cur = decltype(st)::value;
+      constexpr int nxt = (cur + S - 1) % S;
+      if constexpr (AP == 1) wait_vmcnt<(AI + C::B_INST) * (S - 2)>();
+      else if constexpr (cur % 2 == 0) wait_vmcnt<C::B_INST>();
+      else wait_vmcnt<AI + 2 * C::B_INST>();
+      __builtin_amdgcn_s_barrier();
+      const int kn = (kt + S - 1) * BK;
+      if constexpr (AP == 1) issue_a(a_stage(std::integral_constant<int, nxt>{}), kn);
+      else if constexpr (cur % 2 == 0) issue_a(a_stage(std::integral_constant<int, (cur + 2) % 4>{}), (kt + 2) * BK);
+      issue_b(b_stage(std::integral_constant<int, nxt>{}), kn);
+      compute(a_stage(st), b_stage(st), (AP == 2 && (cur & 1)) ? 64 : 0);
+      if constexpr (ES == 2 && C::THREADS == 512) {
+        // (8-wave tiles) instruction order for the step: the first substep's LDS reads, then
+        // each MFMA followed by one of the next substep's LDS reads and, after
+        // every second MFMA, one of the step's global->LDS loads, so that the
+        // loads reach the address unit evenly spread over the step
+        constexpr int DSR = FM + 2 * C::FN;
+        constexpr int MF = FM * C::FN;
+        constexpr int VM = (AP == 1 || cur % 2 == 0) ? (AI + C::B_INST) : C::B_INST;
+        __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);
+#pragma unroll
+        for (int ss = 0; ss < KC / 2; ++ss)
+#pragma unroll
+          for (int m = 0; m < MF; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (ss + 1 < KC / 2 && m < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if ((ss * MF + m) % 2 == 1 && (ss * MF + m) / 2 < VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+          }
+      }
+    };
+    // whole groups of S steps run as one straight-line loop body: steps guarded
+    // by a branch inside the body make the compiler merge its load tracking at
+    // the loop head and drain every load in flight there once per iteration
+    int kt = 0;
+    for (; kt + S <= nk; kt += S) {
+      step(std::integral_constant<int, 0>{}, kt);
+      step(std::integral_constant<int, 1>{}, kt + 1);
+      if constexpr (S > 2) step(std::integral_constant<int, 2 % S>{}, kt + 2);
+      if constexpr (S > 3) step(std::integral_constant<int, 3 % S>{}, kt + 3);
+    }
+    if (kt < nk) step(std::integral_constant<int, 0>{}, kt);
+    if constexpr (S > 2) if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (S > 3) if (kt + 2 < nk) step(std::integral_constant<int, 2 % S>{}, kt + 2);
+    wait_vmcnt<0>();
+
+    // ---- epilogue: lane holds row m = .. + lane%32, columns n = .. + 8*(r/4) + 4*(lane/32) + r%4
+    O* Cp = static_cast<O*>(p.C);
+    const E* bias = p.bias ? static_cast<const E*>(p.bias) + (int64_t)g * p.strideBias : nullptr;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int grow = row_lo + wm * WTM + j * 32 + lrow;
+      if (grow >= row_hi) continue;
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * C::WTN + i * 32 + 8 * q + 4 * lhalf;
+          if (col >= Ncols) continue;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v[r] = acc[i][j][4 * q + r];
+            if (bias) v[r] += ElemTraits<E>::to_f32(bias[col + r]);
+            if (C::GELU) v[r] = gelu_erf(v[r]);
+          }
+          Store<O>::four(Cp + grow * p.ldc + col, v[0], v[1], v[2], v[3]);
+        }
       }
     }
+  };
+  if constexpr (C::HAS_TAIL) {
+    if (tail_tile) run(std::true_type{});
+    else run(std::false_type{});
+  } else {
+    run(std::false_type{});
   }
 }
 
 template <class C>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
-  int mtiles;
-  if (p.seg == nullptr)
-    mtiles = (p.M + C::BM - 1) / C::BM;
-  else
-    mtiles = p.M / C::BM + p.groups + 1;  // >= sum over groups of ceil(rows_g / BM)
+  // upper bounds on the row tiles of each phase: per group, the full-height
+  // tiles plus at most one partial one, and at most BM/(2 TBM) tail tiles;
+  // each phase's blocks are a multiple of the XCD count
+  const int groups = p.seg ? p.groups : 1;
+  const int64_t full_max = (int64_t)(p.M / C::BM + groups);
+  const int64_t tail_max = C::HAS_TAIL ? (int64_t)groups * (C::BM / (2 * C::TBM)) : 0;
   const int ntiles = (p.Ncols + C::BN - 1) / C::BN;
-  if (mtiles <= 0 || ntiles <= 0) return hipSuccess;
-  // a multiple of the XCD count, so that every XCD has room for its share
-  const int64_t blocks = ((int64_t)mtiles * ntiles + kNumXcds - 1) / kNumXcds * kNumXcds;
+  if (p.M <= 0 || ntiles <= 0) return hipSuccess;
+  auto xcd_round = [](int64_t n) { return (n + kNumXcds - 1) / kNumXcds * kNumXcds; };
+  const int64_t blocks = xcd_round(full_max * ntiles) + xcd_round(tail_max * ntiles);
   hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
@@ -499,13 +541,12 @@ template <typename E, typename O, bool G>
 hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStream_t s) {
   if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, 8, 4, G>>(p, s);
   // 256x256 tiles (8 waves, one block per CU) need half the L1 bandwidth per
-  // flop of 128x128 ones; they are used once they give at least half as many
-  // tiles as CUs, except for a short-K GEMM with the GELU epilogue, where two
-  // 128x128 blocks per CU let one block's epilogue run beside the other's
-  // MFMAs (measured on the FFN shapes of the workloads)
+  // flop of 128x128 ones; with ragged tails in cheap tail tiles run last,
+  // they are the faster choice on every FFN shape of the workloads once they
+  // give at least half as many tiles as CUs
   const int groups = p.seg ? p.groups : 0;
   const int64_t tiles256 = (int64_t)(p.M / 256 + groups) * ((p.Ncols + 255) / 256);
-  if (tiles256 >= kNumCUs / 2 && !(G && p.K <= 1024))
+  if (tiles256 >= kNumCUs / 2)
     return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s);
   return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s);
 }
