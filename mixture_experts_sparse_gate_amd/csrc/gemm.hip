@@ -158,6 +158,28 @@ template <int KC> __device__ inline int swz_a(int r) {
 template <int ES> __device__ inline int swz_b(int k) {
   return ES == 2 ? ((2 * (k & 3)) ^ (8 * (k & 1))) : 2 * (k & 3);
 }
+// Epilogue slices (32 rows of 8 or 16 chunks): chunk c of row r sits at
+// c ^ swz_c(r). Row reads (ds_read_b128, CPR lanes per row) stay free of bank
+// conflicts; the fragment writes (one column chunk, 32 rows) go in two passes
+// for 8-byte pieces (the minimum for 16 distinct bank pairs) and one per
+// 16 lanes for 16-byte pieces.
+template <int OB> __device__ inline int swz_c(int r) { return OB == 2 ? ((r >> 1) & 7) : (r & 15); }
+
+// 4 floats as O into LDS: 8 bytes (bf16) or 16 bytes (fp32)
+template <typename O> struct Pack;
+template <> struct Pack<bf16> {
+  __device__ static inline void four_lds(char* dst, const float* v) {
+    u32x2 w;
+    w[0] = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    w[1] = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *(__attribute__((address_space(3))) u32x2*)dst = w;
+  }
+};
+template <> struct Pack<float> {
+  __device__ static inline void four_lds(char* dst, const float* v) {
+    *(__attribute__((address_space(3))) f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+  }
+};
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) {
@@ -478,29 +500,59 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     if constexpr (S > 3) if (kt + 2 < nk) step(std::integral_constant<int, 2 % S>{}, kt + 2);
     wait_vmcnt<0>();
 
-    // ---- epilogue: lane holds row m = .. + lane%32, columns n = .. + 8*(r/4) + 4*(lane/32) + r%4
+    // ---- epilogue. The lane holds row .. + lane%32, columns .. + 8*(r/4) +
+    // 4*(lane/32) + r%4 of each 32x32 fragment. Stored from there, one store
+    // instruction would cover 32 rows with 16 bytes each, and the L2 would see
+    // a request per 16 bytes. Instead each 32-row slice of the wave's tile is
+    // finished in registers (bias, GELU, conversion), written to a per-wave
+    // LDS region, and read back as 16-byte pieces of rows, CPR lanes per row,
+    // so that every store writes whole 128- or 256-byte row segments.
+    __syncthreads();  // every wave is done reading the stage buffers
+    constexpr int OB = sizeof(O);
+    constexpr int CPR = C::WTN * OB / 16;  // 16-byte chunks per slice row
+    constexpr int RPI = kWave / CPR;       // slice rows per 64-lane read
+    constexpr int REG = 32 * CPR * 16;     // bytes of one slice
+    constexpr int WPS = (C::THREADS / kWave + S - 1) / S;  // waves per stage buffer
+    static_assert(WPS * REG <= ST, "epilogue slices fit the stage buffers");
+    const int wsel = wave % S;
+    char* const reg = (wsel == 0 ? st0 : wsel == 1 ? st1 : wsel == 2 ? st2 : st3) + (wave / S) * REG;
     O* Cp = static_cast<O*>(p.C);
     const E* bias = p.bias ? static_cast<const E*>(p.bias) + (int64_t)g * p.strideBias : nullptr;
+    const int ccol0 = n0 + wn * C::WTN;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int grow = row_lo + wm * WTM + j * 32 + lrow;
-      if (grow >= row_hi) continue;
+      const int frow = row_lo + wm * WTM + j * 32;
+      if (frow >= row_hi) break;  // wave-uniform
 #pragma unroll
       for (int i = 0; i < C::FN; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * C::WTN + i * 32 + 8 * q + 4 * lhalf;
-          if (col >= Ncols) continue;
+          const int cb = (i * 32 + 8 * q + 4 * lhalf) * OB;  // byte offset in the slice row
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             v[r] = acc[i][j][4 * q + r];
-            if (bias) v[r] += ElemTraits<E>::to_f32(bias[col + r]);
+            if (bias && ccol0 + i * 32 + 8 * q + 4 * lhalf + r < Ncols)
+              v[r] += ElemTraits<E>::to_f32(bias[ccol0 + i * 32 + 8 * q + 4 * lhalf + r]);
             if (C::GELU) v[r] = gelu_erf(v[r]);
           }
-          Store<O>::four(Cp + grow * p.ldc + col, v[0], v[1], v[2], v[3]);
+          Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 32 / RPI; ++t) {
+        const int rr = t * RPI + lane / CPR, ch = lane % CPR;
+        const u32x4 val = *(lds_u32x4*)(reg + rr * CPR * 16 + ((ch ^ swz_c<OB>(rr)) * 16));
+        const int col = ccol0 + ch * (16 / OB);
+        if (frow + rr < row_hi && col < Ncols)
+          *reinterpret_cast<u32x4*>(Cp + (int64_t)(frow + rr) * p.ldc + col) = val;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   };
   if constexpr (C::HAS_TAIL) {
