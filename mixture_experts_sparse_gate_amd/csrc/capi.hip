@@ -132,9 +132,11 @@ DispatchWs dispatch_ws(const moe_desc_t* d) {
 }
 
 struct ForwardWs {
-  size_t route, dispatch, topk_idx, topk_w, count, off, row_of, token_of_row, H, y_perm,
-      bytes;
+  size_t route, dispatch, ffn_counters, topk_idx, topk_w, count, off, row_of, token_of_row, H,
+      y_perm, bytes;
+  int n_counters;
 };
+int ffn_counters_of(const moe_desc_t* d);
 ForwardWs forward_ws(const moe_desc_t* d) {
   ForwardWs w{};
   const size_t Tk = (size_t)d->T * d->k, R = (size_t)rows_bound_of(d), s = elem_bytes(d);
@@ -146,6 +148,8 @@ ForwardWs forward_ws(const moe_desc_t* d) {
   };
   w.route = take(route_ws(d).bytes);
   w.dispatch = take(dispatch_ws(d).bytes);
+  w.n_counters = ffn_counters_of(d);
+  w.ffn_counters = take((size_t)w.n_counters * 4);
   w.topk_idx = take(Tk * 4);
   w.topk_w = take(Tk * 4);
   w.count = take((size_t)d->N * 4);
@@ -217,9 +221,11 @@ moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, co
   return hip_status(moe::launch_gate_plain_noisy(g, bf, d->gate == MOE_GATE_NOISY, s), "gate");
 }
 
+// zero, zero_n: ints for the dispatch to clear on the way (the fused FFN's
+// counters), or null
 moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx, int32_t* count,
                          int32_t* off, int32_t* row_of, int32_t* token_of_row, void* x_perm,
-                         void* ws, hipStream_t s) {
+                         void* ws, hipStream_t s, int32_t* zero = nullptr, int zero_n = 0) {
   const DispatchWs dw = dispatch_ws(d);
   moe::DispatchParams p{};
   p.x = x;
@@ -236,20 +242,20 @@ moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx,
   p.k = d->k;
   p.C = (int)capacity_of(d);
   p.elem_bytes = elem_bytes(d);
+  p.zero = zero;
+  p.zero_n = zero_n;
   return hip_status(moe::launch_dispatch(p, s), "dispatch");
 }
 
-// A1: GEMM1's activation rows. With token_of_row null they are the rows of
-// x_perm; otherwise A1 is x itself and row r reads token token_of_row[r] / k
-// (the gather fused into GEMM1's tile loads, no x_perm round trip).
-moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of_row,
-                    const int32_t* off, const void* W1, const void* b1, const void* W2,
-                    const void* b2, void* H, void* y_perm, hipStream_t s) {
-  const bool bf = d->dtype == MOE_BF16;
-  const int R = (int)rows_bound_of(d);
-  const int avg_rows = (int)((d->T * d->k) / d->N);
-  const int max_rows = (int)capacity_of(d);
-  moe::GemmParams g{};
+// The two expert GEMMs. A1: GEMM1's activation rows. With token_of_row null
+// they are the rows of x_perm; otherwise A1 is x itself and row r reads token
+// token_of_row[r] / k (the gather fused into GEMM1's tile loads, no x_perm
+// round trip). Pointers may be null where only the shapes matter.
+void ffn_gemms(const moe_desc_t* d, const void* A1, const int32_t* token_of_row, const int32_t* off,
+               const void* W1, const void* b1, const void* W2, const void* b2, void* H, void* y_perm,
+               moe::GemmParams* g1, moe::GemmParams* g2) {
+  moe::GemmParams& g = *g1;
+  g = moe::GemmParams{};
   g.A = A1;
   g.gather = token_of_row;
   g.gather_div = d->k;
@@ -262,24 +268,49 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of
   g.ldc = d->h;
   g.strideB = (int64_t)d->d * d->h;
   g.strideBias = d->h;
-  g.M = R;
+  g.M = (int)rows_bound_of(d);
   g.groups = d->N;
   g.K = d->d;
   g.Ncols = d->h;
-  TRY(hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s),
+  moe::GemmParams& h = *g2;
+  h = g;
+  h.A = H;
+  h.gather = nullptr;
+  h.B = W2;
+  h.bias = b2;
+  h.C = y_perm;
+  h.lda = d->h;
+  h.ldc = d->d;
+  h.strideB = (int64_t)d->h * d->d;
+  h.strideBias = d->d;
+  h.K = d->h;
+  h.Ncols = d->d;
+}
+
+// counters of the fused FFN launch for this layer (0 where it does not apply)
+int ffn_counters_of(const moe_desc_t* d) {
+  static const int32_t shape_only[1] = {0};  // sizing reads no pointer
+  moe::GemmParams g1, g2;
+  ffn_gemms(d, nullptr, nullptr, shape_only, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, &g1, &g2);
+  const int avg_rows = (int)((d->T * d->k) / d->N);
+  return moe::fused_ffn_fits(g1, g2, d->dtype == MOE_BF16, avg_rows) ? moe::fused_ffn_counters(g1) : 0;
+}
+
+// counters: fused-FFN counters (ffn_counters_of ints, zeroed earlier on the
+// stream) or null for two grouped-GEMM launches. Both give the same bits.
+moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of_row,
+                    const int32_t* off, const void* W1, const void* b1, const void* W2,
+                    const void* b2, void* H, void* y_perm, int32_t* counters, hipStream_t s) {
+  const bool bf = d->dtype == MOE_BF16;
+  const int avg_rows = (int)((d->T * d->k) / d->N);
+  const int max_rows = (int)capacity_of(d);
+  moe::GemmParams g1, g2;
+  ffn_gemms(d, A1, token_of_row, off, W1, b1, W2, b2, H, y_perm, &g1, &g2);
+  if (counters && moe::fused_ffn_fits(g1, g2, bf, avg_rows))
+    return hip_status(moe::launch_fused_ffn(g1, g2, counters, s), "expert FFN");
+  TRY(hip_status(moe::launch_grouped_gemm(g1, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s),
                  "expert GEMM1"));
-  g.A = H;
-  g.gather = nullptr;
-  g.B = W2;
-  g.bias = b2;
-  g.C = y_perm;
-  g.lda = d->h;
-  g.ldc = d->d;
-  g.strideB = (int64_t)d->h * d->d;
-  g.strideBias = d->d;
-  g.K = d->h;
-  g.Ncols = d->d;
-  return hip_status(moe::launch_grouped_gemm(g, moe::GemmKind::kFfn2, bf, avg_rows, max_rows, s),
+  return hip_status(moe::launch_grouped_gemm(g2, moe::GemmKind::kFfn2, bf, avg_rows, max_rows, s),
                     "expert GEMM2");
 }
 
@@ -390,7 +421,7 @@ moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const in
   TRY(maybe(b2, "b2", 4));
   TRY(need(H, "H", 16));
   TRY(need(y_perm, "y_perm", 16));
-  return do_ffn(desc, x_perm, nullptr, expert_off, W1, b1, W2, b2, H, y_perm, (hipStream_t)stream);
+  return do_ffn(desc, x_perm, nullptr, expert_off, W1, b1, W2, b2, H, y_perm, nullptr, (hipStream_t)stream);
 }
 
 moe_status_t moe_combine(const moe_desc_t* desc, const void* y_perm, const int32_t* row_of,
@@ -435,8 +466,11 @@ moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, v
   TRY(do_route(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb, t->logit_bias,
                t->logits, idx, w, at<char>(ws, fw.route), s));
   // routing and row maps only: GEMM1 gathers its rows from x itself
-  TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s));
-  TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, s));
+  // (the dispatch also clears the fused FFN's counters)
+  int32_t* counters = fw.n_counters ? at<int32_t>(ws, fw.ffn_counters) : nullptr;
+  TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s, counters,
+                  fw.n_counters));
+  TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, s));
   return do_combine(desc, y_perm, row_of, w, t->y, s);
 }
 

@@ -43,6 +43,8 @@ __global__ __launch_bounds__(kBlock) void count_kernel(DispatchParams p) {
   }
   __syncthreads();
   for (int e = threadIdx.x; e < N; e += kBlock) p.tile_counts[blockIdx.x * N + e] = hist[e];
+  if (blockIdx.x == 0 && p.zero)
+    for (int i = threadIdx.x; i < p.zero_n; i += kBlock) p.zero[i] = 0;
 }
 
 static_assert(kDispatchTile == kBlock, "rows_kernel: one token per thread");

@@ -181,115 +181,36 @@ template <> struct Pack<float> {
   }
 };
 
-template <class C>
-__global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) {
+// LDS objects of a block of configuration C (declared in each kernel).
+#define MOE_GEMM_LDS(C) \
+  constexpr int ST = C::AP == 1 ? C::A_STAGE + C::B_STAGE : C::B_STAGE; \
+  constexpr int SA = C::AP == 1 ? 16 : C::A_STAGE; \
+  __shared__ __attribute__((aligned(1024))) char st0[ST]; \
+  __shared__ __attribute__((aligned(1024))) char st1[ST]; \
+  __shared__ __attribute__((aligned(1024))) char st2[C::S > 2 ? ST : 16]; \
+  __shared__ __attribute__((aligned(1024))) char st3[C::S > 3 ? ST : 16]; \
+  __shared__ __attribute__((aligned(1024))) char sa0[SA]; \
+  __shared__ __attribute__((aligned(1024))) char sa1[SA];
+
+// One BM x BN output tile (rows [row_lo, row_hi) of group g, columns from
+// n0; TBM rows if tail_tile): the K loop and the epilogue, GELU'd if gelu.
+// All threads of the block call it with the same arguments; the LDS
+// objects are the block's (MOE_GEMM_LDS). at_k_end() runs between the K
+// loop and the epilogue.
+template <class C, class AtKEnd>
+__device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* st0, char* st1, char* st2,
+                                          char* st3, char* sa0, char* sa1, int g, int row_lo, int row_hi,
+                                          int n0, bool tail_tile, AtKEnd&& at_k_end) {
   using E = typename C::Elem;
   using O = typename C::Out;
   constexpr int CE = C::CE, KC = C::KC, BK = C::BK, BM = C::BM, BN = C::BN, ES = C::ES, S = C::S;
   constexpr int AP = C::AP, KCA = C::KCA;
-  // one LDS object per stage, so that the compiler can tell a stage being
-  // filled by the asynchronous loads from the one being read. AP == 1: stage
-  // i holds the activation tile at offset 0 and the weight tile at A_STAGE.
-  // AP == 2: st0..st3 hold weight tiles only; sa0/sa1 hold activation tiles
-  // for K-step pairs (0,1) and (2,3) of each group of four.
-  constexpr int ST = AP == 1 ? C::A_STAGE + C::B_STAGE : C::B_STAGE;
-  constexpr int SA = AP == 1 ? 16 : C::A_STAGE;
-  __shared__ __attribute__((aligned(1024))) char st0[ST];
-  __shared__ __attribute__((aligned(1024))) char st1[ST];
-  __shared__ __attribute__((aligned(1024))) char st2[S > 2 ? ST : 16];
-  __shared__ __attribute__((aligned(1024))) char st3[S > 3 ? ST : 16];
-  __shared__ __attribute__((aligned(1024))) char sa0[SA];
-  __shared__ __attribute__((aligned(1024))) char sa1[SA];
-  __shared__ int sched[5];
-
+  constexpr int ST = AP == 1 ? C::A_STAGE + C::B_STAGE : C::B_STAGE;  // bytes of st0..st3
+  (void)BM;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int wm = wave / C::WN, wn = wave % C::WN;
-  // ---- tile schedule. A group's rows make full-height tiles of BM rows;
-  // with tail tiles (HAS_TAIL), a remainder of at most BM/2 rows makes
-  // tiles of TBM rows instead of one partial full-height tile. Phase 0 lists
-  // the full-height tiles, phase 1 the tail tiles, each group by group and,
-  // within a group, n-tiles in runs of kGroupN with row tiles fastest. Blocks
-  // take phase 0 first (the hardware starts blocks in index order), so a
-  // second round of tiles on the CUs is made of the cheap tail tiles. The
-  // hardware hands blocks to the XCDs round-robin (block b -> XCD b % 8), so
-  // within a phase block b takes tile (b % 8) * per + b / 8: each XCD works
-  // through one contiguous stretch of the phase, and the ~32 blocks it runs
-  // at a time share their weight slabs and activation rows in its own L2.
-  if (wave == 0) {
-    constexpr int GPL = 4;  // groups per lane (groups <= 256)
-    int lo[GPL], hi[GPL], nf[GPL], nt[GPL];
-    int sf = 0, st = 0;
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int gi = lane * GPL + i;
-      lo[i] = 0;
-      hi[i] = 0;
-      if (p.seg == nullptr) {
-        if (gi == 0) hi[i] = p.M;
-      } else if (gi < p.groups) {
-        // rows are clamped to [0, M] so that no offset table can address
-        // outside the row buffers
-        lo[i] = min(max(p.seg[gi], 0), p.M);
-        hi[i] = min(max(p.seg[gi + 1], lo[i]), p.M);
-      }
-      const int n = hi[i] - lo[i], t = n % BM;
-      const bool small_tail = C::HAS_TAIL && t > 0 && t <= BM / 2;
-      nf[i] = n / BM + (t > 0 && !small_tail);
-      nt[i] = small_tail ? (t + C::TBM - 1) / C::TBM : 0;
-      sf += nf[i];
-      st += nt[i];
-    }
-    int incf = sf, inct = st;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) {
-      const int of = __shfl_up(incf, m, kWave), ot = __shfl_up(inct, m, kWave);
-      if (lane >= m) {
-        incf += of;
-        inct += ot;
-      }
-    }
-    const int NT = (p.Ncols + BN - 1) / BN;
-    const int F = __shfl(incf, kWave - 1, kWave) * NT, Tt = __shfl(inct, kWave - 1, kWave) * NT;
-    const int BF = (F + kNumXcds - 1) / kNumXcds * kNumXcds;  // blocks of phase 0
-    const int phase = (int)blockIdx.x >= BF;
-    const int b = blockIdx.x - (phase ? BF : 0);
-    const int count = phase ? Tt : F;
-    const int per = (count + kNumXcds - 1) / kNumXcds, local = b / kNumXcds;
-    const int tile = (b % kNumXcds) * per + local;
-    const bool live = local < per && tile < count;
-    if (lane == 0 && !live) sched[0] = -1;
-    const int q = tile / NT;  // row tile in the concatenated order of the phase
-    int start = phase ? inct - st : incf - sf;
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-      const int c = phase ? nt[i] : nf[i];
-      if (live && q >= start && q < start + c) {
-        const int t = tile - start * NT;  // tile within the group's part of the phase
-        const int run = c * kGroupN;      // tiles per run of kGroupN n-tiles
-        const int ng = t / run, r = t % run;
-        const int gn = min(kGroupN, NT - ng * kGroupN);
-        const int qr = r / gn;
-        const int r0 = phase ? lo[i] + (hi[i] - lo[i]) / BM * BM + qr * C::TBM : lo[i] + qr * BM;
-        sched[0] = lane * GPL + i;
-        sched[1] = r0;
-        sched[2] = min(r0 + (phase ? C::TBM : BM), hi[i]);
-        sched[3] = (ng * kGroupN + r % gn) * BN;
-        sched[4] = phase;
-      }
-      start += c;
-    }
-  }
-  __syncthreads();
-  // block-uniform: keep them in scalar registers so that the buffer
-  // descriptors built from them are uniform too
-  const int g = __builtin_amdgcn_readfirstlane(sched[0]);
-  if (g < 0) return;
-  const int row_lo = __builtin_amdgcn_readfirstlane(sched[1]);
-  const int row_hi = __builtin_amdgcn_readfirstlane(sched[2]);
-  const int n0 = __builtin_amdgcn_readfirstlane(sched[3]);
-  const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[4]) != 0;
   const int K = p.K, Ncols = p.Ncols;
   const int lda = (int)p.lda;
   const int rows = row_hi - row_lo;
@@ -499,6 +420,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     if constexpr (S > 2) if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
     if constexpr (S > 3) if (kt + 2 < nk) step(std::integral_constant<int, 2 % S>{}, kt + 2);
     wait_vmcnt<0>();
+    at_k_end();
 
     // ---- epilogue. The lane holds row .. + lane%32, columns .. + 8*(r/4) +
     // 4*(lane/32) + r%4 of each 32x32 fragment. Stored from there, one store
@@ -534,7 +456,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
             v[r] = acc[i][j][4 * q + r];
             if (bias && ccol0 + i * 32 + 8 * q + 4 * lhalf + r < Ncols)
               v[r] += ElemTraits<E>::to_f32(bias[ccol0 + i * 32 + 8 * q + 4 * lhalf + r]);
-            if (C::GELU) v[r] = gelu_erf(v[r]);
+            if (gelu) v[r] = gelu_erf(v[r]);
           }
           Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
         }
@@ -560,6 +482,290 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
     else run(std::false_type{});
   } else {
     run(std::false_type{});
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) {
+  using E = typename C::Elem;
+  using O = typename C::Out;
+  constexpr int BM = C::BM, BN = C::BN;
+  // one LDS object per stage, so that the compiler can tell a stage being
+  // filled by the asynchronous loads from the one being read. AP == 1: stage
+  // i holds the activation tile at offset 0 and the weight tile at A_STAGE.
+  // AP == 2: st0..st3 hold weight tiles only; sa0/sa1 hold activation tiles
+  // for K-step pairs (0,1) and (2,3) of each group of four.
+  MOE_GEMM_LDS(C)
+  __shared__ int sched[5];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  // ---- tile schedule. A group's rows make full-height tiles of BM rows;
+  // with tail tiles (HAS_TAIL), a remainder of at most BM/2 rows makes
+  // tiles of TBM rows instead of one partial full-height tile. Phase 0 lists
+  // the full-height tiles, phase 1 the tail tiles, each group by group and,
+  // within a group, n-tiles in runs of kGroupN with row tiles fastest. Blocks
+  // take phase 0 first (the hardware starts blocks in index order), so a
+  // second round of tiles on the CUs is made of the cheap tail tiles. The
+  // hardware hands blocks to the XCDs round-robin (block b -> XCD b % 8), so
+  // within a phase block b takes tile (b % 8) * per + b / 8: each XCD works
+  // through one contiguous stretch of the phase, and the ~32 blocks it runs
+  // at a time share their weight slabs and activation rows in its own L2.
+  if (wave == 0) {
+    constexpr int GPL = 4;  // groups per lane (groups <= 256)
+    int lo[GPL], hi[GPL], nf[GPL], nt[GPL];
+    int sf = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int gi = lane * GPL + i;
+      lo[i] = 0;
+      hi[i] = 0;
+      if (p.seg == nullptr) {
+        if (gi == 0) hi[i] = p.M;
+      } else if (gi < p.groups) {
+        // rows are clamped to [0, M] so that no offset table can address
+        // outside the row buffers
+        lo[i] = min(max(p.seg[gi], 0), p.M);
+        hi[i] = min(max(p.seg[gi + 1], lo[i]), p.M);
+      }
+      const int n = hi[i] - lo[i], t = n % BM;
+      const bool small_tail = C::HAS_TAIL && t > 0 && t <= BM / 2;
+      nf[i] = n / BM + (t > 0 && !small_tail);
+      nt[i] = small_tail ? (t + C::TBM - 1) / C::TBM : 0;
+      sf += nf[i];
+      st += nt[i];
+    }
+    int incf = sf, inct = st;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int of = __shfl_up(incf, m, kWave), ot = __shfl_up(inct, m, kWave);
+      if (lane >= m) {
+        incf += of;
+        inct += ot;
+      }
+    }
+    const int NT = (p.Ncols + BN - 1) / BN;
+    const int F = __shfl(incf, kWave - 1, kWave) * NT, Tt = __shfl(inct, kWave - 1, kWave) * NT;
+    const int BF = (F + kNumXcds - 1) / kNumXcds * kNumXcds;  // blocks of phase 0
+    const int phase = (int)blockIdx.x >= BF;
+    const int b = blockIdx.x - (phase ? BF : 0);
+    const int count = phase ? Tt : F;
+    const int per = (count + kNumXcds - 1) / kNumXcds, local = b / kNumXcds;
+    const int tile = (b % kNumXcds) * per + local;
+    const bool live = local < per && tile < count;
+    if (lane == 0 && !live) sched[0] = -1;
+    const int q = tile / NT;  // row tile in the concatenated order of the phase
+    int start = phase ? inct - st : incf - sf;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int c = phase ? nt[i] : nf[i];
+      if (live && q >= start && q < start + c) {
+        const int t = tile - start * NT;  // tile within the group's part of the phase
+        const int run = c * kGroupN;      // tiles per run of kGroupN n-tiles
+        const int ng = t / run, r = t % run;
+        const int gn = min(kGroupN, NT - ng * kGroupN);
+        const int qr = r / gn;
+        const int r0 = phase ? lo[i] + (hi[i] - lo[i]) / BM * BM + qr * C::TBM : lo[i] + qr * BM;
+        sched[0] = lane * GPL + i;
+        sched[1] = r0;
+        sched[2] = min(r0 + (phase ? C::TBM : BM), hi[i]);
+        sched[3] = (ng * kGroupN + r % gn) * BN;
+        sched[4] = phase;
+      }
+      start += c;
+    }
+  }
+  __syncthreads();
+  // block-uniform: keep them in scalar registers so that the buffer
+  // descriptors built from them are uniform too
+  const int g = __builtin_amdgcn_readfirstlane(sched[0]);
+  if (g < 0) return;
+  const int row_lo = __builtin_amdgcn_readfirstlane(sched[1]);
+  const int row_hi = __builtin_amdgcn_readfirstlane(sched[2]);
+  const int n0 = __builtin_amdgcn_readfirstlane(sched[3]);
+  const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[4]) != 0;
+  gemm_tile<C>(p, C::GELU, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0, tail_tile, [] {});
+}
+
+// ---- the expert FFN (GEMM1 + GELU, then GEMM2) as one persistent launch.
+// Row tiles (each group's full-height tiles, then its tail tiles, as in
+// grouped_gemm_kernel) are dealt to the XCDs in contiguous runs; each XCD's
+// blocks take work items from that XCD's queue in the order: GEMM1 tiles of
+// its full row tiles, of its tail row tiles, then GEMM2 tiles of the same.
+// A GEMM2 tile needs all GEMM1 column tiles of its row tile (its K runs over
+// all of H's columns): after storing its H tile, a GEMM1 block waits for its
+// stores to complete and counts the tile in ready[row tile]; a GEMM2 block
+// waits for that count. H is produced and consumed under one XCD's L2, so
+// completed stores are what the consumer reads. No block waits on a tile
+// that no running block holds: every GEMM1 tile of an XCD is dequeued before
+// any of its GEMM2 tiles, by a block that computes it without waiting. The
+// wait is bounded all the same. A block's XCD is read from the hardware, so
+// the placement of blocks does not matter for correctness; every XCD gets
+// blocks as the grid is a multiple of the XCD count.
+struct FusedFfn {
+  GemmParams g1, g2;  // GEMM1 (GELU) and GEMM2, as for two launches
+  int32_t* counters;  // [kNumXcds] queues, then ready[row tiles]: zero at launch
+};
+
+constexpr uint32_t kHwRegXccId = (3u << 11) | 20u;  // s_getreg: XCC_ID[3:0]
+constexpr int kFusedMaxGroups = 256;
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
+  constexpr int BM = C::BM, BN = C::BN, TBM = C::TBM;
+  static_assert(C::HAS_TAIL, "tail row tiles follow the full ones");
+  MOE_GEMM_LDS(C)
+  // group table: first row, end row, and how many full / tail row tiles
+  // come before the group's (exclusive prefixes)
+  __shared__ int g_lo[kFusedMaxGroups], g_hi[kFusedMaxGroups], g_ef[kFusedMaxGroups], g_et[kFusedMaxGroups];
+  __shared__ int tot[2];
+  __shared__ int sched[8];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int xcc = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kNumXcds - 1));
+  if (wave == 0) {
+    const GemmParams& p1 = f.g1;
+    const int groups = p1.groups;
+    constexpr int GPL = kFusedMaxGroups / kWave;
+    int lo[GPL], hi[GPL], nf[GPL], nt[GPL];
+    int sf = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int gi = lane * GPL + i;
+      lo[i] = hi[i] = 0;
+      if (gi < groups) {
+        lo[i] = min(max(p1.seg[gi], 0), p1.M);
+        hi[i] = min(max(p1.seg[gi + 1], lo[i]), p1.M);
+      }
+      const int n = hi[i] - lo[i], t = n % BM;
+      const bool small_tail = t > 0 && t <= BM / 2;
+      nf[i] = n / BM + (t > 0 && !small_tail);
+      nt[i] = small_tail ? (t + TBM - 1) / TBM : 0;
+      sf += nf[i];
+      st += nt[i];
+    }
+    int incf = sf, inct = st;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int of = __shfl_up(incf, m, kWave), ot = __shfl_up(inct, m, kWave);
+      if (lane >= m) {
+        incf += of;
+        inct += ot;
+      }
+    }
+    int ef = incf - sf, et = inct - st;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int gi = lane * GPL + i;
+      g_lo[gi] = lo[i];
+      g_hi[gi] = hi[i];
+      g_ef[gi] = ef;
+      g_et[gi] = et;
+      ef += nf[i];
+      et += nt[i];
+    }
+    if (lane == kWave - 1) {
+      tot[0] = incf;
+      tot[1] = inct;
+    }
+  }
+  // item indices: the first taken here, each next one while the current
+  // tile's epilogue runs (its result is stored to sched[0] after it)
+  if (tid == 0)
+    sched[0] = __hip_atomic_fetch_add(f.counters + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    // Everything below reads the arguments through fp, re-read for each
+    // tile: the empty asm hides that fp never changes, so that the compiler
+    // does not hold the arguments of both GEMMs in registers across the
+    // tile's code (it would run out of them). fp points at the kernel
+    // argument in the kernel-argument segment (f is the only argument);
+    // taking f's address instead would make the compiler copy f to
+    // private memory.
+    const __attribute__((address_space(4))) FusedFfn* fp =
+        (const __attribute__((address_space(4))) FusedFfn*)__builtin_amdgcn_kernarg_segment_ptr();
+    __asm__ volatile("" : "+s"(fp));
+    const int NT1 = (fp->g1.Ncols + BN - 1) / BN, NT2 = (fp->g2.Ncols + BN - 1) / BN;
+    int32_t* const ready = fp->counters + kNumXcds;
+    __syncthreads();  // sched[0]: this item's index
+    if (wave == 0) {
+      const int groups = fp->g1.groups;
+      const int Fr = tot[0], Tr = tot[1];
+      // this XCD's row tiles: full [fa, fb), tail [ta, tb) (tails dealt in
+      // reverse, so that XCDs with fewer full tiles tend to get more tails)
+      const int fa = xcc * Fr / kNumXcds, fb = (xcc + 1) * Fr / kNumXcds;
+      const int ta = (kNumXcds - 1 - xcc) * Tr / kNumXcds, tb = (kNumXcds - xcc) * Tr / kNumXcds;
+      const int nfx = fb - fa, ntx = tb - ta;
+      int t = sched[0], kind = 0, tail = 0, NT = 0, c = 0, base = 0;
+      if (t < nfx * NT1) {
+        kind = 1, NT = NT1, c = nfx, base = fa;
+      } else if ((t -= nfx * NT1) < ntx * NT1) {
+        kind = 1, tail = 1, NT = NT1, c = ntx, base = ta;
+      } else if ((t -= ntx * NT1) < nfx * NT2) {
+        kind = 2, NT = NT2, c = nfx, base = fa;
+      } else if ((t -= nfx * NT2) < ntx * NT2) {
+        kind = 2, tail = 1, NT = NT2, c = ntx, base = ta;
+      }
+      if (lane == 0) sched[1] = -1;  // done (or no tile found)
+      if (kind != 0) {
+        // runs of kGroupN column tiles, as in grouped_gemm_kernel
+        const int run = c * kGroupN, ng = t / run, r = t % run;
+        const int gn = min(kGroupN, NT - ng * kGroupN);
+        const int q = base + r / gn, col = ng * kGroupN + r % gn;
+#pragma unroll
+        for (int i = 0; i < kFusedMaxGroups / kWave; ++i) {
+          const int gi = lane * (kFusedMaxGroups / kWave) + i;
+          if (gi < groups) {
+            const int lo = g_lo[gi], hi = g_hi[gi], n = hi - lo, rem = n % BM;
+            const bool small_tail = rem > 0 && rem <= BM / 2;
+            const int e = tail ? g_et[gi] : g_ef[gi];
+            const int cnt = tail ? (small_tail ? (rem + TBM - 1) / TBM : 0) : n / BM + (rem > 0 && !small_tail);
+            if (q >= e && q < e + cnt) {
+              const int r0 = tail ? lo + n / BM * BM + (q - e) * TBM : lo + (q - e) * BM;
+              sched[1] = kind;
+              sched[2] = gi;
+              sched[3] = r0;
+              sched[4] = min(r0 + (tail ? TBM : BM), hi);
+              sched[5] = col * BN;
+              sched[6] = tail;
+              sched[7] = tail ? Fr + q : q;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int kind = __builtin_amdgcn_readfirstlane(sched[1]);
+    if (kind < 0) break;
+    const int g = __builtin_amdgcn_readfirstlane(sched[2]);
+    const int row_lo = __builtin_amdgcn_readfirstlane(sched[3]);
+    const int row_hi = __builtin_amdgcn_readfirstlane(sched[4]);
+    const int n0 = __builtin_amdgcn_readfirstlane(sched[5]);
+    const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[6]) != 0;
+    const int rid = __builtin_amdgcn_readfirstlane(sched[7]);
+    if (kind == 2) {
+      if (tid == 0) {
+        for (int spin = 0; spin < (1 << 20); ++spin) {
+          if (__hip_atomic_load(ready + rid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NT1) break;
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      __syncthreads();
+    }
+    // one copy of the tile code for both GEMMs
+    const __attribute__((address_space(4))) GemmParams* pp = kind == 1 ? &fp->g1 : &fp->g2;
+    int next = 0;
+    gemm_tile<C>(*(const GemmParams*)pp, kind == 1, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0,
+                 tail_tile, [&] {
+                   if (tid == 0)
+                     next = __hip_atomic_fetch_add(fp->counters + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                 });
+    if (kind == 1) {
+      wait_vmcnt<0>();  // this thread's H stores are in the L2
+      __syncthreads();  // ... and every thread's
+      if (tid == 0) __hip_atomic_fetch_add(ready + rid, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) sched[0] = next;
   }
 }
 
@@ -603,7 +809,31 @@ hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStre
   return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s);
 }
 
+using FusedCfg = Cfg<bf16, bf16, 256, 256, 2, 4, 4, 4, false>;
+
 }  // namespace
+
+int fused_ffn_counters(const GemmParams& g1) {
+  const int64_t full_max = (int64_t)g1.M / FusedCfg::BM + g1.groups;
+  const int64_t tail_max = (int64_t)g1.groups * (FusedCfg::BM / (2 * FusedCfg::TBM));
+  return (int)(kNumXcds + full_max + tail_max);
+}
+
+bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16_, int avg_rows) {
+  // the same tile configuration for both GEMMs as the two launches would take
+  auto big = [](const GemmParams& p) {
+    return (int64_t)(p.M / 256 + p.groups) * ((p.Ncols + 255) / 256) >= kNumCUs / 2;
+  };
+  return bf16_ && g1.seg && g2.seg && avg_rows >= 64 && g1.groups <= kFusedMaxGroups && big(g1) && big(g2) &&
+         g1.M > 0;
+}
+
+hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, hipStream_t s) {
+  FusedFfn f{g1, g2, counters};
+  // one block per CU (a multiple of the XCD count)
+  hipLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, f);
+  return hipGetLastError();
+}
 
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16_, int avg_rows,
                                int max_rows, hipStream_t s) {

@@ -54,7 +54,8 @@ struct DispatchParams {
   int32_t* row_of;          // [T*k]
   int32_t* token_of_row;    // [R]
   void* x_perm;             // [R, d] or null (skip the copy)
-  int T, d, N, k, C, elem_bytes;
+  int32_t* zero;            // zero_n ints to clear on the way (or null)
+  int T, d, N, k, C, elem_bytes, zero_n;
 };
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
 hipError_t launch_permute(const DispatchParams& p, hipStream_t s);
@@ -79,6 +80,12 @@ enum class GemmKind { kFfn1Gelu, kFfn2, kProjF32 };
 // avg_rows / max_rows: expected and largest rows per group (tile choice only)
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, int avg_rows,
                                int max_rows, hipStream_t s);
+// The expert FFN (GEMM1 kFfn1Gelu, then GEMM2 kFfn2 on GEMM1's output) in one
+// persistent launch, where fused_ffn_fits(); counters: fused_ffn_counters()
+// ints of zeros (they are consumed).
+bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16, int avg_rows);
+int fused_ffn_counters(const GemmParams& g1);
+hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, hipStream_t s);
 
 // ---- combine (combine.hip)
 struct CombineParams {

@@ -126,6 +126,36 @@ def test_full_size_forward(name):
         assert torch.count_nonzero(dev.y[torch.as_tensor(dropped, device=dev.y.device)]) == 0
 
 
+# Shapes whose two expert GEMMs both take 256x256 tiles: there moe_forward
+# runs the expert FFN as one persistent launch (GEMM2 tiles waiting on the
+# GEMM1 tiles of their rows) while moe_expert_ffn makes two launches; the
+# tiles and their arithmetic are the same, so the results must agree bit for
+# bit, call after call (the launch consumes counters the dispatch clears).
+FUSED = {
+    "noisy_top2_bf16": W["noisy_top2_bf16"],
+    "cosine_zipf_top4_bf16": W["cosine_zipf_top4_bf16"],
+    "large_expert_top2_bf16": W["large_expert_top2_bf16"],
+    # skewed demand over 16 experts: empty, small and capped groups, tails
+    "zipf16_top2": workloads.MoESpec("zipf16_top2", T=8192, d=1024, h=1024, N=16, k=2, capacity_factor=2.0,
+                                     gate="softmax", renorm=True, dtype="bf16", zipf_s=1.5),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_fused_ffn_forward_equals_stages(name):
+    spec = FUSED[name]
+    inp, dev = run_staged(spec, 11)
+    y_st = dev.y.clone()
+    counts = host(dev.expert_count)
+    say(f"   expert demand: min {counts.min()} max {counts.max()} zero {(counts == 0).sum()}")
+    for rep in range(2):
+        dev.y.zero_()
+        say(f"[case] fused forward {spec.name} call {rep}")
+        dev.run_forward(inspect=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dev.y, y_st)
+
+
 EDGE = {
     # one expert: every weight is 1 and y = FFN_0(x)
     "single_expert": workloads.MoESpec("single_expert", T=300, d=64, h=128, N=1, k=1, capacity_factor=1.0,
