@@ -30,7 +30,7 @@ that a device copy of known size calibrates both counters), condensed by
 
     python bench.py --summarize <results.db> --kind traffic --workload W --out profiles/...
 
-into profiles/grouped_gemm_<workload>_traffic.txt. That figure is used only
+into profiles/expert_ffn_<workload>_traffic.txt. That figure is used only
 while the file's hash of the GEMM source matches the current source.
 """
 from __future__ import annotations
@@ -67,7 +67,7 @@ def gemm_source_hash() -> str:
 
 
 def traffic_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"grouped_gemm_{workload}_traffic.txt")
+    return os.path.join(ROOT, "profiles", f"expert_ffn_{workload}_traffic.txt")
 
 
 def read_traffic(workload: str):
@@ -117,7 +117,7 @@ def main() -> int:
 
     import torch
 
-    from mixture_experts_sparse_gate_amd import api, workloads
+    from mixture_experts_sparse_gate_amd import _lib, api, workloads
     from mixture_experts_sparse_gate_amd.inputs import make_inputs
 
     spec = workloads.get(args.workload)
@@ -154,7 +154,7 @@ def main() -> int:
         if ev:
             ev[2].record(stream)
         api.expert_ffn(dev.desc, dev.x_perm, dev.expert_off, dev.W1, dev.b1, dev.W2, dev.b2, dev.H,
-                       dev.y_perm)
+                       dev.y_perm, ws=dev.ws)
         if ev:
             ev[3].record(stream)
         api.combine(dev.desc, dev.y_perm, dev.row_of, dev.topk_w, dev.y)
@@ -162,15 +162,9 @@ def main() -> int:
             ev[4].record(stream)
 
     K = args.steps
-    # ---- headline: K steps of moe_forward
-    for _ in range(args.warmup):
-        forward()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(K):
-        forward()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    # The headline (K moe_forward steps after W warm-up steps) is timed last,
+    # after the breakdowns below, so that the GPU has left its idle clocks
+    # behind while the inputs were being generated on the host.
 
     # ---- stage breakdown through the four stage entry points
     for _ in range(3):
@@ -231,6 +225,16 @@ def main() -> int:
                    "p90_ms": cold[(9 * len(cold)) // 10], "reps": len(cold)}
         cold_ms["tokens_per_s"] = spec.T / (cold_ms["median_ms"] * 1e-3)
 
+    # ---- headline: W warm-up steps, then exactly K timed steps of moe_forward
+    for _ in range(args.warmup):
+        forward()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        forward()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+
     # algorithmic work of one step, from this step's routing
     off = dev.expert_off.cpu().numpy().astype(np.int64)
     kept = np.diff(off)
@@ -249,7 +253,12 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": ffn_flops / ffn_s / 1e12, "peak": MFMA_PEAK_TFLOPS[spec.dtype],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["kernel"] = "grouped_gemm_kernel, launched twice per step (GEMM1+GELU, GEMM2); duration from HIP events around moe_expert_ffn"
+    if api.workspace_size(dev.desc, _lib.MOE_WS_FFN) > 0:
+        roof["kernel"] = ("fused_ffn_kernel: GEMM1+GELU and GEMM2 in one persistent launch (after a counter "
+                          "fill kernel); duration from HIP events around moe_expert_ffn")
+    else:
+        roof["kernel"] = ("grouped_gemm_kernel, launched twice per step (GEMM1+GELU, GEMM2); duration from HIP "
+                          "events around moe_expert_ffn")
     roof["algorithmic"] = {"flops": ffn_flops, "touched_weight_bytes": touched_weight_bytes}
     traffic, tsrc = read_traffic(spec.name)
     roof["traffic"] = traffic
@@ -349,8 +358,12 @@ def _short(name: str) -> str:
     m = re.search(r"CfgI(\w+?)EEEEEvNS_10GemmParamsE", name)
     if m:
         return "grouped_gemm_kernel<" + m.group(1) + ">"
+    m = re.search(r"fused_ffn_kernelINS0_3CfgI(\w+?)EEEEEvNS0_8FusedFfnE", name)
+    if m:
+        return "fused_ffn_kernel<" + m.group(1) + ">"
     for key in ("gate_logits_kernel", "gate_select_kernel", "cosine_select_kernel", "count_kernel",
-                "scan_kernel", "slots_kernel", "permute_kernel", "combine_kernel"):
+                "scan_kernel", "slots_kernel", "permute_kernel", "combine_kernel", "fill_kernel",
+                "gate_fused_kernel", "gate_partial_kernel", "gate_finish_kernel", "rows_kernel"):
         if key in name:
             return key
     return name[:70]
@@ -376,10 +389,12 @@ def summarize(args):
             rows = _pmc_per_kernel(db, counter)
             copies = [v for d, n, g, v in rows if "copy" in n.lower() and "bfloat16" not in n.lower()]
             calib_kib = max(copies) if copies else None
-            # expert-FFN launches only (GEMM1, GEMM2 alternate); the cosine
-            # gate's projection (bf16 in, fp32 out: "DF16bf" in the name) is not
+            # expert-FFN launches only: one fused_ffn_kernel per step, or
+            # GEMM1 and GEMM2 alternating; the cosine gate's projection (bf16
+            # in, fp32 out: "DF16bf" in the name) is not
+            fused = [v for d, n, g, v in rows if "fused_ffn_kernel" in n]
             gemm = [v for d, n, g, v in rows if "grouped_gemm_kernel" in n and "DF16bfLi" not in n]
-            out[tag] = dict(calib_kib=calib_kib, gemm_kib=gemm)
+            out[tag] = dict(calib_kib=calib_kib, gemm_kib=gemm, fused_kib=fused)
         mib = None
         if args.command:
             m = re.search(r"--calib-copy-mib\s+(\d+)", args.command)
@@ -391,7 +406,7 @@ def summarize(args):
             o = out[tag]
             fac = known_kib / o["calib_kib"] if o["calib_kib"] and known_kib else float("nan")
             g = o["gemm_kib"]
-            per_step = [g[i] + g[i + 1] for i in range(0, len(g) - 1, 2)]
+            per_step = list(o["fused_kib"]) if o["fused_kib"] else [g[i] + g[i + 1] for i in range(0, len(g) - 1, 2)]
             steady = per_step[len(per_step) // 2:] or per_step
             kib = sum(steady) / max(len(steady), 1)
             res[tag] = kib * fac * 1024

@@ -102,7 +102,8 @@ typedef struct moe_desc {
 typedef enum moe_ws_kind {
   MOE_WS_ROUTE = 0,
   MOE_WS_DISPATCH = 1,
-  MOE_WS_FORWARD = 2
+  MOE_WS_FORWARD = 2,
+  MOE_WS_FFN = 3
 } moe_ws_kind_t;
 
 /* Expert capacity C = min(T, ceil((capacity_factor * (T*k)) / N)), evaluated
@@ -155,10 +156,15 @@ MOE_API moe_status_t moe_dispatch(const moe_desc_t* desc, const void* x, const i
  *   y_perm[r] = H[r] W2[e] + b2[e]                   fp32 accumulation, rounded once
  * with GELU(u) = u/2 (1 + erf(u / sqrt 2)). H [R, h] and y_perm [R, d] are
  * outputs; rows >= expert_off[N] are not written. The grid is sized from R,
- * so no host read of expert_off is needed. */
+ * so no host read of expert_off is needed.
+ * ws: MOE_WS_FFN bytes, or NULL. It holds the work counters of the
+ * single-launch form of the two GEMMs (bf16 layers with enough rows and
+ * columns for 256x256 tiles), in which GEMM2's tiles wait for the rows of H
+ * they read; with NULL the two GEMMs always run as two launches. The values
+ * do not depend on which form runs. */
 MOE_API moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
                             const void* W1, const void* b1, const void* W2, const void* b2,
-                            void* H, void* y_perm, void* stream);
+                            void* H, void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
 /* Gate-weighted combine: y[t] = sum over j with row_of[t*k+j] >= 0, in j order,
  * of topk_w[t, j] * y_perm[row_of[t*k+j]], accumulated in fp32 and rounded once;

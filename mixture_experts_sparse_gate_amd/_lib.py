@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_gfx950.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_NOISY, MOE_GATE_COSINE = 0, 1, 2
-MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_FORWARD = 0, 1, 2
+MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_FORWARD, MOE_WS_FFN = 0, 1, 2, 3
 
 
 class MoeDesc(ctypes.Structure):
@@ -45,7 +45,7 @@ SIGNATURES = {
     "moe_workspace_size": (c_int, [POINTER(MoeDesc), c_int, POINTER(c_size_t)]),
     "moe_route": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 10 + [c_void_p, c_size_t, c_void_p]),
     "moe_dispatch": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 7 + [c_void_p, c_size_t, c_void_p]),
-    "moe_expert_ffn": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 8 + [c_void_p]),
+    "moe_expert_ffn": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 4 + [c_void_p]),
     "moe_forward": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p, c_size_t, c_void_p]),
     "moe_status_string": (c_char_p, [c_int]),

@@ -92,10 +92,10 @@ def dispatch(desc, x, topk_idx, expert_count, expert_off, row_of, token_of_row, 
     _check(st, "moe_dispatch")
 
 
-def expert_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, stream=None):
+def expert_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, ws=None, stream=None):
     st = _lib.load().moe_expert_ffn(ctypes.byref(desc), _ptr(x_perm), _ptr(expert_off), _ptr(W1),
-                                    _ptr(b1), _ptr(W2), _ptr(b2), _ptr(H), _ptr(y_perm),
-                                    _stream(stream))
+                                    _ptr(b1), _ptr(W2), _ptr(b2), _ptr(H), _ptr(y_perm), _ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "moe_expert_ffn")
 
 
@@ -173,7 +173,7 @@ class DeviceLayer:
         dispatch(self.desc, self.x, self.topk_idx, self.expert_count, self.expert_off, self.row_of,
                  self.token_of_row, self.x_perm, ws=self.ws, stream=stream)
         expert_ffn(self.desc, self.x_perm, self.expert_off, self.W1, self.b1, self.W2, self.b2, self.H,
-                   self.y_perm, stream=stream)
+                   self.y_perm, ws=self.ws, stream=stream)
         combine(self.desc, self.y_perm, self.row_of, self.topk_w, self.y, stream=stream)
 
     def layer_tensors(self, inspect: bool = True) -> dict:

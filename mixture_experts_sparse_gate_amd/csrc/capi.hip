@@ -296,18 +296,19 @@ int ffn_counters_of(const moe_desc_t* d) {
   return moe::fused_ffn_fits(g1, g2, d->dtype == MOE_BF16, avg_rows) ? moe::fused_ffn_counters(g1) : 0;
 }
 
-// counters: fused-FFN counters (ffn_counters_of ints, zeroed earlier on the
-// stream) or null for two grouped-GEMM launches. Both give the same bits.
+// counters: fused-FFN counters (ffn_counters_of ints; cleared here unless
+// cleared says the dispatch did it) or null for two grouped-GEMM launches.
+// Both give the same bits.
 moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of_row,
                     const int32_t* off, const void* W1, const void* b1, const void* W2,
-                    const void* b2, void* H, void* y_perm, int32_t* counters, hipStream_t s) {
+                    const void* b2, void* H, void* y_perm, int32_t* counters, bool cleared, hipStream_t s) {
   const bool bf = d->dtype == MOE_BF16;
   const int avg_rows = (int)((d->T * d->k) / d->N);
   const int max_rows = (int)capacity_of(d);
   moe::GemmParams g1, g2;
   ffn_gemms(d, A1, token_of_row, off, W1, b1, W2, b2, H, y_perm, &g1, &g2);
   if (counters && moe::fused_ffn_fits(g1, g2, bf, avg_rows))
-    return hip_status(moe::launch_fused_ffn(g1, g2, counters, s), "expert FFN");
+    return hip_status(moe::launch_fused_ffn(g1, g2, counters, !cleared, s), "expert FFN");
   TRY(hip_status(moe::launch_grouped_gemm(g1, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s),
                  "expert GEMM1"));
   return hip_status(moe::launch_grouped_gemm(g2, moe::GemmKind::kFfn2, bf, avg_rows, max_rows, s),
@@ -374,6 +375,7 @@ moe_status_t moe_workspace_size(const moe_desc_t* desc, moe_ws_kind_t kind, size
     case MOE_WS_ROUTE: *bytes = route_ws(desc).bytes; return MOE_OK;
     case MOE_WS_DISPATCH: *bytes = dispatch_ws(desc).bytes; return MOE_OK;
     case MOE_WS_FORWARD: *bytes = forward_ws(desc).bytes; return MOE_OK;
+    case MOE_WS_FFN: *bytes = align_up((size_t)ffn_counters_of(desc) * 4); return MOE_OK;
   }
   return fail(MOE_ERR_INVALID, "unknown workspace kind %d", (int)kind);
 }
@@ -411,7 +413,7 @@ moe_status_t moe_dispatch(const moe_desc_t* desc, const void* x, const int32_t* 
 
 moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
                             const void* W1, const void* b1, const void* W2, const void* b2,
-                            void* H, void* y_perm, void* stream) {
+                            void* H, void* y_perm, void* ws, size_t ws_bytes, void* stream) {
   TRY(check_desc(desc));
   TRY(need(x_perm, "x_perm", 16));
   TRY(need(expert_off, "expert_off", 4));
@@ -421,7 +423,11 @@ moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const in
   TRY(maybe(b2, "b2", 4));
   TRY(need(H, "H", 16));
   TRY(need(y_perm, "y_perm", 16));
-  return do_ffn(desc, x_perm, nullptr, expert_off, W1, b1, W2, b2, H, y_perm, nullptr, (hipStream_t)stream);
+  // without a workspace the two GEMMs run as two launches
+  const int n_counters = ws ? ffn_counters_of(desc) : 0;
+  TRY(check_ws(ws, ws_bytes, align_up((size_t)n_counters * 4)));
+  return do_ffn(desc, x_perm, nullptr, expert_off, W1, b1, W2, b2, H, y_perm,
+                n_counters ? static_cast<int32_t*>(ws) : nullptr, false, (hipStream_t)stream);
 }
 
 moe_status_t moe_combine(const moe_desc_t* desc, const void* y_perm, const int32_t* row_of,
@@ -470,7 +476,7 @@ moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, v
   int32_t* counters = fw.n_counters ? at<int32_t>(ws, fw.ffn_counters) : nullptr;
   TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s, counters,
                   fw.n_counters));
-  TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, s));
+  TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s));
   return do_combine(desc, y_perm, row_of, w, t->y, s);
 }
 

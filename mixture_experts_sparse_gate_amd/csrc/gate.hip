@@ -640,6 +640,7 @@ __global__ __launch_bounds__(kBlock) void gate_finish_kernel(const float* __rest
 // forms the logits and selects for its 32 tokens.
 constexpr int kGfWaves = 8;
 constexpr int kGfRows = 128;
+static_assert(kGtTok * kGtCols % (kGfWaves * kWave) == 0, "logit entries per thread");
 
 template <bool NOISY>
 __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartialParams q, int krw,
@@ -661,6 +662,19 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
   f32x16 acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  // the noise and bias each thread adds to its logits below, loaded now so
+  // that they arrive while the product runs (32 tokens x N <= 32 columns:
+  // at most two entries per thread)
+  constexpr int kPre = kGtTok * kGtCols / (kGfWaves * kWave);
+  float pre_noise[kPre], pre_bias[kPre];
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int i = threadIdx.x + j * kGfWaves * kWave;
+    const int t = i / p.N, c = i % p.N;
+    const bool ok = i < kGtTok * p.N && t0 + t < p.T;
+    pre_noise[j] = NOISY && ok ? p.noise[(int64_t)(t0 + t) * p.N + c] : 0.f;
+    pre_bias[j] = p.logit_bias && ok ? p.logit_bias[c] : 0.f;
+  }
   const int kw0 = wave * krw, kw1 = min(kw0 + krw, q.d);
   constexpr int U = kGfRows / 16;         // 16-K steps per chunk
   constexpr int G = kGfRows * 4 / kWave;  // 16-byte gate granules per lane per chunk
@@ -746,9 +760,11 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
   // of 256 floats for the selection (the gate-row area is free now)
   float (*lg)[kWave * kMaxExpertsPerLane] = reinterpret_cast<float (*)[kWave * kMaxExpertsPerLane]>(&wl[0][0]);
   const int N = p.N;
-  for (int i = threadIdx.x; i < kGtTok * N; i += kGfWaves * kWave) {
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) {
+    const int i = threadIdx.x + j * kGfWaves * kWave;
     const int t = i / N, c = i % N, tok = t0 + t;
-    if (tok >= p.T) continue;
+    if (i >= kGtTok * N || tok >= p.T) continue;
     float l = red[0][t][c];
 #pragma unroll
     for (int w = 1; w < kGfWaves; ++w) l += red[w][t][c];
@@ -756,9 +772,9 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
       float u = red[0][t][N + c];
 #pragma unroll
       for (int w = 1; w < kGfWaves; ++w) u += red[w][t][N + c];
-      l += p.noise[(int64_t)tok * N + c] * softplusf(u);
+      l += pre_noise[j] * softplusf(u);
     }
-    if (p.logit_bias) l += p.logit_bias[c];
+    if (p.logit_bias) l += pre_bias[j];
     if (p.logits) p.logits[(int64_t)tok * N + c] = l;
     lg[t][c] = l;
   }

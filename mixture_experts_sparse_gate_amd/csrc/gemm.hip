@@ -811,6 +811,12 @@ hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStre
 
 using FusedCfg = Cfg<bf16, bf16, 256, 256, 2, 4, 4, 4, false>;
 
+// zeros n ints (graph-safe, unlike a memset node)
+__global__ __launch_bounds__(256) void fill_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
 
 int fused_ffn_counters(const GemmParams& g1) {
@@ -828,7 +834,12 @@ bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16_, int 
          g1.M > 0;
 }
 
-hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, hipStream_t s) {
+hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
+                            hipStream_t s) {
+  if (clear) {
+    const int n = fused_ffn_counters(g1);
+    hipLaunchKernelGGL(fill_kernel, dim3((n + 255) / 256), dim3(256), 0, s, counters, n);
+  }
   FusedFfn f{g1, g2, counters};
   // one block per CU (a multiple of the XCD count)
   hipLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, f);

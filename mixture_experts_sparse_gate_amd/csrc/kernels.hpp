@@ -82,10 +82,12 @@ hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, in
                                int max_rows, hipStream_t s);
 // The expert FFN (GEMM1 kFfn1Gelu, then GEMM2 kFfn2 on GEMM1's output) in one
 // persistent launch, where fused_ffn_fits(); counters: fused_ffn_counters()
-// ints of zeros (they are consumed).
+// ints, zero at launch (they are consumed): cleared first by a small kernel
+// if clear, else by the caller earlier on the stream.
 bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16, int avg_rows);
 int fused_ffn_counters(const GemmParams& g1);
-hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, hipStream_t s);
+hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
+                            hipStream_t s);
 
 // ---- combine (combine.hip)
 struct CombineParams {

@@ -79,12 +79,12 @@ def test_workspace_sizes(lib):
     for T in (1, 100, 1024, 4096, 10000):
         d = desc_from_spec(base.with_(T=T))
         sizes = []
-        for kind in (_lib.MOE_WS_ROUTE, _lib.MOE_WS_DISPATCH, _lib.MOE_WS_FORWARD):
+        for kind in (_lib.MOE_WS_ROUTE, _lib.MOE_WS_DISPATCH, _lib.MOE_WS_FORWARD, _lib.MOE_WS_FFN):
             n = ctypes.c_size_t()
             assert lib.moe_workspace_size(ctypes.byref(d), kind, ctypes.byref(n)) == _lib.MOE_OK
             assert n.value % 256 == 0
             sizes.append(n.value)
-        assert sizes[2] >= sizes[0] + sizes[1]
+        assert sizes[2] >= sizes[0] + sizes[1] + sizes[3]
         assert sizes[2] > prev
         prev = sizes[2]
 
@@ -172,7 +172,8 @@ def test_forward_argument_checks(lib):
 @no_gpu
 def test_stage_argument_checks(lib):
     d = desc_from_spec(workloads.get("large_expert_top2_bf16"))
-    assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
     assert lib.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 4, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_dispatch(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
 

@@ -148,6 +148,16 @@ def test_fused_ffn_forward_equals_stages(name):
     y_st = dev.y.clone()
     counts = host(dev.expert_count)
     say(f"   expert demand: min {counts.min()} max {counts.max()} zero {(counts == 0).sum()}")
+    # the stage call ran the single launch (it had a workspace); the two
+    # launches (no workspace) give the same H and y_perm bit for bit
+    A = int(host(dev.expert_off)[-1])
+    H1, Y1 = dev.H[:A].clone(), dev.y_perm[:A].clone()
+    dev.H.zero_()
+    dev.y_perm.zero_()
+    say(f"[case] two-launch FFN {spec.name}")
+    api.expert_ffn(dev.desc, dev.x_perm, dev.expert_off, dev.W1, dev.b1, dev.W2, dev.b2, dev.H, dev.y_perm)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.H[:A], H1) and torch.equal(dev.y_perm[:A], Y1)
     for rep in range(2):
         dev.y.zero_()
         say(f"[case] fused forward {spec.name} call {rep}")
