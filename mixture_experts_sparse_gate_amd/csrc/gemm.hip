@@ -58,25 +58,26 @@ template <> struct Mfma<float> {
 };
 
 // GELU(u) = u Phi(u), Phi the standard normal CDF (the erf form of GELU).
-// For x = |u| / sqrt(2), Phi(u) = 1 - erfc(x)/2 (u >= 0) or erfc(x)/2 (u < 0),
-// with erfc(x) = R(t) exp(-x^2), t = 1 / (1 + 0.35 x) and R a degree-9
-// polynomial fitted to the scaled complement erfc(x) exp(x^2) on x in
-// [0, 9.3] (fit_gelu.py beside this file derives the constants). Relative
-// error below 2e-5 everywhere, including the negative tail that
-// 0.5 u (1 + erf(x)) loses to cancellation; about 20 VALU operations against
-// about 45 for erff and its two-path branch.
+// With x = |u| / sqrt(2) and e = erfc(x) / 2 = Phi(-|u|),
+//     GELU(u) = max(u, 0) - |u| e
+// (u - u e for u >= 0, u e for u < 0), one fma with one rounding. erfc is
+// R(t) exp(-x^2), t = 1 / (1 + 0.35 x), R a degree-7 polynomial fitted to
+// the scaled complement erfc(x) exp(x^2) on x in [0, 9.3] (fit_gelu.py
+// beside this file derives the constants, which are R's halved). Relative
+// error of R below 2.3e-6 everywhere, including the negative tail that
+// 0.5 u (1 + erf(x)) loses to cancellation; 13 VALU operations and two
+// transcendental ones, against about 45 for erff and its two-path branch.
 __device__ inline float gelu_erf(float u) {
-  constexpr float c[10] = {-5.558532939e-05f, 1.986937672e-01f, 1.856181175e-01f, 2.510680556e-01f,
-                           -6.972948462e-02f, 6.612331271e-01f, -7.248843908e-01f, 8.268299699e-01f,
-                           -3.940122724e-01f, 6.523866206e-02f};
-  const float x = fabsf(u) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.35f, x, 1.f));
-  float r = c[9];
+  constexpr float h[8] = {1.738272113e-04f, 9.559800476e-02f, 1.226225942e-01f, -7.414813619e-03f, 3.312253952e-01f, -3.146309555e-01f, 3.652992249e-01f, -9.287211299e-02f};
+  const float a = fabsf(u);
+  // t = 1 / (1 + 0.35 |u| / sqrt(2))
+  const float t = __builtin_amdgcn_rcpf(fmaf(a, 0.24748737341529164f, 1.f));
+  float r = h[7];
 #pragma unroll
-  for (int i = 8; i >= 0; --i) r = fmaf(r, t, c[i]);
-  // exp(-x^2) = 2^(-x^2 log2(e)); inputs below -126 give zero (u < -13.4 or > 13.4)
-  const float e = 0.5f * r * __builtin_amdgcn_exp2f(-(x * x) * 1.4426950408889634f);
-  return u * (u >= 0.f ? 1.f - e : e);
+  for (int i = 6; i >= 0; --i) r = fmaf(r, t, h[i]);
+  // exp(-x^2) = 2^(-u^2 log2(e) / 2); below -126 it gives zero (|u| > 13.4)
+  const float e = r * __builtin_amdgcn_exp2f((u * -0.72134752044448170f) * u);
+  return fmaf(-a, e, fmaxf(u, 0.f));
 }
 
 // 16 bytes per lane from the buffer at byte offset voff straight into LDS:
@@ -445,6 +446,24 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     for (int j = 0; j < FM; ++j) {
       const int frow = row_lo + wm * WTM + j * 32;
       if (frow >= row_hi) break;  // wave-uniform
+      // bias and GELU over the whole slice, each behind one uniform branch
+      if (bias) {
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int col = ccol0 + i * 32 + 8 * q + 4 * lhalf + r;
+              if (col < Ncols) acc[i][j][4 * q + r] += ElemTraits<E>::to_f32(bias[col]);
+            }
+      }
+      if (gelu) {
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = gelu_erf(acc[i][j][r]);
+      }
 #pragma unroll
       for (int i = 0; i < C::FN; ++i) {
 #pragma unroll
@@ -452,12 +471,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
           const int cb = (i * 32 + 8 * q + 4 * lhalf) * OB;  // byte offset in the slice row
           float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v[r] = acc[i][j][4 * q + r];
-            if (bias && ccol0 + i * 32 + 8 * q + 4 * lhalf + r < Ncols)
-              v[r] += ElemTraits<E>::to_f32(bias[ccol0 + i * 32 + 8 * q + 4 * lhalf + r]);
-            if (gelu) v[r] = gelu_erf(v[r]);
-          }
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
           Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
         }
       }
