@@ -104,7 +104,8 @@ moe_status_t maybe(const void* p, const char* name, size_t align) {
 // ---------------------------------------------------------------- workspace
 
 struct RouteWs {
-  size_t z, logits, partial, bytes;
+  size_t z, logits, partial, hist, bytes;
+  bool has_hist;  // the gate writes per-32-token choice counts (for moe_forward's dispatch)
 };
 RouteWs route_ws(const moe_desc_t* d) {
   RouteWs w{};
@@ -116,6 +117,11 @@ RouteWs route_ws(const moe_desc_t* d) {
   w.partial = o;
   if (d->gate != MOE_GATE_COSINE && d->dtype == MOE_BF16)
     o += align_up(moe::gate_partial_bytes(d->T, d->d, d->N, d->gate == MOE_GATE_NOISY));
+  w.hist = o;
+  w.has_hist = d->gate != MOE_GATE_COSINE &&
+               moe::gate_writes_hist(d->dtype == MOE_BF16, d->gate == MOE_GATE_NOISY, d->N);
+  if (w.has_hist)
+    o += align_up((size_t)((d->T + moe::kGateHistTokens - 1) / moe::kGateHistTokens) * d->N * 4);
   w.bytes = o;
   return w;
 }
@@ -169,9 +175,12 @@ T* at(void* ws, size_t off) {
 
 // ---------------------------------------------------------------- stages (arguments checked)
 
+// hist: the gate's per-32-token choice counts (route_ws().hist, where
+// has_hist), or null
 moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, const void* w_noise,
                       const float* noise, const void* proj, const float* emb, const float* bias,
-                      float* logits, int32_t* idx, float* w, void* ws, hipStream_t s) {
+                      float* logits, int32_t* idx, float* w, void* ws, hipStream_t s,
+                      int32_t* hist = nullptr) {
   const RouteWs rw = route_ws(d);
   const bool bf = d->dtype == MOE_BF16;
   if (d->gate == MOE_GATE_COSINE) {
@@ -213,6 +222,7 @@ moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, co
   g.topk_idx = idx;
   g.topk_w = w;
   g.partial = at<float>(ws, rw.partial);
+  g.hist = rw.has_hist ? hist : nullptr;
   g.T = (int)d->T;
   g.d = d->d;
   g.N = d->N;
@@ -223,9 +233,11 @@ moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, co
 
 // zero, zero_n: ints for the dispatch to clear on the way (the fused FFN's
 // counters), or null
+// hist32: the gate's per-32-token choice counts, or null (counted here)
 moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx, int32_t* count,
                          int32_t* off, int32_t* row_of, int32_t* token_of_row, void* x_perm,
-                         void* ws, hipStream_t s, int32_t* zero = nullptr, int zero_n = 0) {
+                         void* ws, hipStream_t s, int32_t* zero = nullptr, int zero_n = 0,
+                         const int32_t* hist32 = nullptr) {
   const DispatchWs dw = dispatch_ws(d);
   moe::DispatchParams p{};
   p.x = x;
@@ -244,6 +256,7 @@ moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx,
   p.elem_bytes = elem_bytes(d);
   p.zero = zero;
   p.zero_n = zero_n;
+  p.hist32 = hist32;
   return hip_status(moe::launch_dispatch(p, s), "dispatch");
 }
 
@@ -469,13 +482,17 @@ moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, v
   int32_t* tor = t->token_of_row ? t->token_of_row : at<int32_t>(ws, fw.token_of_row);
   void* H = at<char>(ws, fw.H);
   void* y_perm = at<char>(ws, fw.y_perm);
+  // the gate also counts each 32 tokens' choices where it can, which
+  // spares the dispatch its counting pass
+  const RouteWs rw = route_ws(desc);
+  int32_t* hist = rw.has_hist ? at<int32_t>(ws, fw.route + rw.hist) : nullptr;
   TRY(do_route(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb, t->logit_bias,
-               t->logits, idx, w, at<char>(ws, fw.route), s));
+               t->logits, idx, w, at<char>(ws, fw.route), s, hist));
   // routing and row maps only: GEMM1 gathers its rows from x itself
   // (the dispatch also clears the fused FFN's counters)
   int32_t* counters = fw.n_counters ? at<int32_t>(ws, fw.ffn_counters) : nullptr;
   TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s, counters,
-                  fw.n_counters));
+                  fw.n_counters, hist));
   TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s));
   return do_combine(desc, y_perm, row_of, w, t->y, s);
 }

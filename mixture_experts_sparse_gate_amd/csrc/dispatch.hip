@@ -43,8 +43,6 @@ __global__ __launch_bounds__(kBlock) void count_kernel(DispatchParams p) {
   }
   __syncthreads();
   for (int e = threadIdx.x; e < N; e += kBlock) p.tile_counts[blockIdx.x * N + e] = hist[e];
-  if (blockIdx.x == 0 && p.zero)
-    for (int i = threadIdx.x; i < p.zero_n; i += kBlock) p.zero[i] = 0;
 }
 
 static_assert(kDispatchTile == kBlock, "rows_kernel: one token per thread");
@@ -58,8 +56,41 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(DispatchParams p, int ntil
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int tile = blockIdx.x;
+  if (tile == 0 && p.zero)
+    for (int i = threadIdx.x; i < p.zero_n; i += kBlock) p.zero[i] = 0;
+  if (p.hist32) {
+    // per expert: choices of the tokens before this tile, and of all tokens,
+    // from the gate's per-32-token counts (entries (b, e) of the [nb, N]
+    // table, eight loads in flight per thread before any is added up)
+    constexpr int kPer = kDispatchTile / kGateHistTokens;  // gate blocks per tile
+    const int nb = (p.T + kGateHistTokens - 1) / kGateHistTokens, ne = nb * N;
+    for (int e = threadIdx.x; e < N; e += kBlock) start_s[e] = off_s[e] = 0;
+    __syncthreads();
+    for (int i0 = 0; i0 < ne; i0 += 8 * kBlock) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kBlock + threadIdx.x;
+        c[u] = i < ne ? p.hist32[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * kBlock + threadIdx.x;
+        if (c[u]) {
+          atomicAdd(&off_s[i % N], c[u]);  // totals, for now
+          if (i / N < tile * kPer) atomicAdd(&start_s[i % N], c[u]);
+        }
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < N; e += kBlock) {
+      const int total = off_s[e];
+      kept_s[e] = min(total, C);
+      if (tile == 0) p.expert_count[e] = total;
+    }
+  }
   // per expert: slots taken by earlier tiles, total, kept
-  for (int e = threadIdx.x; e < N; e += kBlock) {
+  for (int e = threadIdx.x; e < N && !p.hist32; e += kBlock) {
     int before = 0, total = 0;
     int t = 0;
     for (; t + 8 <= ntiles; t += 8) {  // eight loads in flight
@@ -175,7 +206,7 @@ __global__ __launch_bounds__(kBlock) void permute_kernel(DispatchParams p) {
 
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s) {
   const int ntiles = (p.T + kDispatchTile - 1) / kDispatchTile;
-  hipLaunchKernelGGL(count_kernel, dim3(ntiles), dim3(kBlock), 0, s, p);
+  if (!p.hist32) hipLaunchKernelGGL(count_kernel, dim3(ntiles), dim3(kBlock), 0, s, p);
   hipLaunchKernelGGL(rows_kernel, dim3(ntiles), dim3(kBlock), 0, s, p, ntiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.x_perm == nullptr) return err;

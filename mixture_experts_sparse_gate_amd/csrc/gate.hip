@@ -781,12 +781,23 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
   __syncthreads();
   // selection: one lane per token
   const int t = threadIdx.x;
+  int* const hs = reinterpret_cast<int*>(&red[0][0][0]);  // free now
+  if (p.hist && t >= kWave && t < kWave + N) hs[t - kWave] = 0;
+  int32_t* io = p.topk_idx + (int64_t)(t0 + t) * p.k;
   if (t < kGtTok && t0 + t < p.T) {
-    int32_t* io = p.topk_idx + (int64_t)(t0 + t) * p.k;
     float* wo = p.topk_w + (int64_t)(t0 + t) * p.k;
     if (N <= 8) select_lane<8>(lg[t], N, p.k, p.renorm, io, wo);
     else if (N <= 16) select_lane<16>(lg[t], N, p.k, p.renorm, io, wo);
     else select_lane<32>(lg[t], N, p.k, p.renorm, io, wo);
+  }
+  if (p.hist) {
+    // the block's choices per expert, for the dispatch (the lane reads back
+    // the indices it has just written)
+    __syncthreads();
+    if (t < kGtTok && t0 + t < p.T)
+      for (int j = 0; j < p.k; ++j) atomicAdd(&hs[io[j]], 1);
+    __syncthreads();
+    if (t < N) p.hist[(int64_t)blockIdx.x * N + t] = hs[t];
   }
 }
 
@@ -854,7 +865,11 @@ hipError_t launch_e(const GateParams& p, hipStream_t s) {
   return launch_tw<E, 1, NOISY>(p, s);
 }
 
+static_assert(kGtTok == kGateHistTokens, "the gate's histogram blocks");
+
 }  // namespace
+
+bool gate_writes_hist(bool bf16_, bool noisy, int N) { return bf16_ && (noisy ? 2 * N : N) <= kGtCols; }
 
 GateSplit gate_split(int64_t T, int d, int N, bool noisy) {
   GateSplit sp{};

@@ -19,8 +19,13 @@ struct GateParams {
   int32_t* topk_idx;       // [T, k]
   float* topk_w;           // [T, k]
   float* partial;          // bf16 only: gate_partial_bytes() of scratch for the split product
+  // [ceil(T/32), N] or null: the choices of each 32 tokens per expert
+  // (written where gate_writes_hist(): the bf16 single-kernel gate)
+  int32_t* hist;
   int T, d, N, k, renorm;
 };
+bool gate_writes_hist(bool bf16, bool noisy, int N);
+constexpr int kGateHistTokens = 32;
 hipError_t launch_gate_plain_noisy(const GateParams& p, bool bf16, bool noisy, hipStream_t s);
 
 // How the bf16 plain/noisy gate product x [W_g | W_n] is split: column
@@ -55,6 +60,9 @@ struct DispatchParams {
   int32_t* token_of_row;    // [R]
   void* x_perm;             // [R, d] or null (skip the copy)
   int32_t* zero;            // zero_n ints to clear on the way (or null)
+  // the gate's per-32-token choice counts (GateParams::hist), or null: then
+  // the dispatch counts them itself
+  const int32_t* hist32;
   int T, d, N, k, C, elem_bytes, zero_n;
 };
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
