@@ -94,6 +94,17 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The same with no LDS operation outstanding (lgkmcnt 0). A wave issues it
+// before a barrier after which other waves refill LDS it has been reading:
+// gfx950's s_barrier does not wait for the wave's own LDS reads to complete
+// (and the compiler adds no wait before a bare s_barrier), so a read still
+// in flight could otherwise return the refilled data.
+template <int N>
+__device__ inline void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 constexpr int kNumXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 constexpr int kGroupN = 4;   // n-tiles per run of the tile order
 
@@ -353,8 +364,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     };
 
     // ---- S-stage pipeline, one barrier per K-step: wait until this step's
-    // loads have landed (later steps' loads may still be in flight), barrier
-    // (everyone's loads visible; everyone done with the previous stage), start
+    // loads have landed (later steps' loads may still be in flight) and this
+    // wave's reads of the previous stage have returned, barrier (everyone's
+    // loads visible; everyone done with the previous stage), start
     // the loads S-1 steps ahead into the stage just freed, compute.
     // AP == 2 (S == 4): even steps also start the activation pair two steps
     // ahead into the buffer the previous pair used. The counts hold whatever
@@ -379,9 +391,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     auto step = [&](auto st, int kt) {
       constexpr int cur = decltype(st)::value;
       constexpr int nxt = (cur + S - 1) % S;
-      if constexpr (AP == 1) wait_vmcnt<(AI + C::B_INST) * (S - 2)>();
-      else if constexpr (cur % 2 == 0) wait_vmcnt<C::B_INST>();
-      else wait_vmcnt<AI + 2 * C::B_INST>();
+      if constexpr (AP == 1) wait_vmcnt_lds<(AI + C::B_INST) * (S - 2)>();
+      else if constexpr (cur % 2 == 0) wait_vmcnt_lds<C::B_INST>();
+      else wait_vmcnt_lds<AI + 2 * C::B_INST>();
       __builtin_amdgcn_s_barrier();
       const int kn = (kt + S - 1) * BK;
       if constexpr (AP == 1) issue_a(a_stage(std::integral_constant<int, nxt>{}), kn);
