@@ -435,6 +435,30 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     wait_vmcnt<0>();
     at_k_end();
 
+    // The lane's bias values: 4 consecutive columns per (fragment, 8-column
+    // group), the same for every row, one buffer load each for the whole
+    // tile (columns past Ncols read zeros; d and h are multiples of the
+    // 16-byte chunk, so no group of 4 straddles Ncols).
+    const bool has_bias = p.bias != nullptr;
+    const int ccol0 = n0 + wn * C::WTN;
+    u32x4 bv[C::FN][4];
+    if (has_bias) {
+      const __amdgpu_buffer_rsrc_t rb =
+          make_rsrc(static_cast<const char*>(p.bias) + (int64_t)g * p.strideBias * ES, (uint32_t)(Ncols * ES));
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int off = (ccol0 + i * 32 + 8 * q + 4 * lhalf) * ES;
+          if constexpr (ES == 2) {
+            const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
+            bv[i][q] = u32x4{w[0], w[1], 0u, 0u};
+          } else {
+            bv[i][q] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+          }
+        }
+    }
+
     // ---- epilogue. The lane holds row .. + lane%32, columns .. + 8*(r/4) +
     // 4*(lane/32) + r%4 of each 32x32 fragment. Stored from there, one store
     // instruction would cover 32 rows with 16 bytes each, and the L2 would see
@@ -452,23 +476,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     const int wsel = wave % S;
     char* const reg = (wsel == 0 ? st0 : wsel == 1 ? st1 : wsel == 2 ? st2 : st3) + (wave / S) * REG;
     O* Cp = static_cast<O*>(p.C);
-    const E* bias = p.bias ? static_cast<const E*>(p.bias) + (int64_t)g * p.strideBias : nullptr;
-    const int ccol0 = n0 + wn * C::WTN;
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int frow = row_lo + wm * WTM + j * 32;
       if (frow >= row_hi) break;  // wave-uniform
       // bias and GELU over the whole slice, each behind one uniform branch
-      if (bias) {
+      if (has_bias) {
 #pragma unroll
         for (int i = 0; i < C::FN; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int col = ccol0 + i * 32 + 8 * q + 4 * lhalf + r;
-              if (col < Ncols) acc[i][j][4 * q + r] += ElemTraits<E>::to_f32(bias[col]);
-            }
+            for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][q], r);
       }
       if (gelu) {
 #pragma unroll
