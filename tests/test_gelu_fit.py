@@ -1,5 +1,6 @@
-"""The GELU of the expert FFN kernel (gemm.hip): its constants are the ones
-fit_gelu.py derives, and the formula, evaluated step by step in fp32, stays
+"""The two GELUs of the expert FFN kernel (gemm.hip; the accurate one for
+fp32 results, the cheaper one for bf16 results): their constants are the ones
+fit_gelu.py derives, and each formula, evaluated step by step in fp32, stays
 within its stated error of the exact GELU (scipy's erfc in fp64)."""
 import math
 import os
@@ -15,11 +16,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mixture_experts_sparse_gate_amd", "csrc")
 
 
-def kernel_constants():
+def kernel_constants(decl=r"h\[8\]"):
     src = open(os.path.join(CSRC, "gemm.hip")).read()
-    m = re.search(r"constexpr float h\[8\] = \{([^}]*)\}", src)
+    m = re.search(r"constexpr float " + decl + r" = \{([^}]*)\}", src)
     assert m, "GELU constants not found in gemm.hip"
     return np.array([float(v.strip().rstrip("f")) for v in m.group(1).split(",")], dtype=np.float32)
+
+
+def fit_module():
+    sys.path.insert(0, CSRC)
+    try:
+        import fit_gelu
+    finally:
+        sys.path.pop(0)
+    return fit_gelu
 
 
 def fma32(a, b, c):
@@ -44,18 +54,34 @@ def gelu_kernel_fp32(u, h):
     return fma32(-a, e, np.maximum(u, f(0)))
 
 
+def gelu_bf16_kernel_fp32(u, g):
+    """The kernel's gelu_erf_bf16 step by step in fp32: a = min(|u|, 6),
+    Q = p(a)^32 by Horner's rule and five squarings, then max(u, 0) - |u| Q."""
+    f = np.float32
+    u = u.astype(f)
+    a = np.minimum(np.abs(u), f(6.0))
+    q = np.full_like(u, g[6])
+    for i in range(5, -1, -1):
+        q = fma32(q, a, g[i])
+    for _ in range(5):
+        q = (q * q).astype(f)
+    return fma32(-np.abs(u), q, np.maximum(u, f(0)))
+
+
+def bf16_bits(v):
+    b = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+
+
 def gelu_exact(u):
     u = u.astype(np.float64)
     return 0.5 * u * scipy_special.erfc(-u / math.sqrt(2.0))
 
 
 def test_constants_come_from_the_fit():
-    sys.path.insert(0, CSRC)
-    try:
-        import fit_gelu
-    finally:
-        sys.path.pop(0)
+    fit_gelu = fit_module()
     np.testing.assert_array_equal(kernel_constants(), fit_gelu.kernel_constants())
+    np.testing.assert_array_equal(kernel_constants(r"g\[7\]"), fit_gelu.kernel_constants_bf16())
 
 
 def test_error_against_exact_gelu():
@@ -72,12 +98,35 @@ def test_error_against_exact_gelu():
 
 
 def test_bf16_rounding_matches_exact():
-    def bf16_bits(v):
-        b = v.astype(np.float32).view(np.uint32).astype(np.uint64)
-        return (b + 0x7FFF + ((b >> 16) & 1)) >> 16
-
     c = kernel_constants()
     u = np.linspace(-4.0, 4.0, 800_001).astype(np.float32)
     got = gelu_kernel_fp32(u, c)
     ref = gelu_exact(u)
     assert np.mean(bf16_bits(got) != bf16_bits(ref)) < 1e-4
+
+
+def test_bf16_form_error_against_exact_gelu():
+    g = kernel_constants(r"g\[7\]")
+    u = np.linspace(-13.0, 13.0, 2_600_001).astype(np.float32)
+    got = gelu_bf16_kernel_fp32(u, g).astype(np.float64)
+    ref = gelu_exact(u)
+    inner = np.abs(u) <= 6.0
+    rel = np.abs(got - ref)[inner] / np.maximum(np.abs(ref)[inner], 1e-30)
+    assert rel[np.abs(ref)[inner] > 0].max() < 3e-5  # relative, negative tail included
+    assert np.abs(got - ref)[~inner].max() < 2e-8      # past the clamp: Q(6) |u|
+    z = gelu_bf16_kernel_fp32(np.array([0.0, 20.0, 1e-30, -1e-30], dtype=np.float32), g)
+    assert z[0] == 0.0 and z[1] == np.float32(20.0)
+    # tiny inputs: GELU(u) = u / 2 to first order, within the same relative bound
+    assert abs(z[2] / 5e-31 - 1) < 3e-5 and abs(z[3] / -5e-31 - 1) < 3e-5
+
+
+def test_bf16_form_rounds_like_exact():
+    """After rounding to bf16 (what the kernel stores) the cheaper form
+    agrees with the correctly rounded exact GELU almost everywhere, and
+    elsewhere by one bf16 unit."""
+    g = kernel_constants(r"g\[7\]")
+    u = np.linspace(-6.0, 6.0, 1_200_001).astype(np.float32)
+    got = bf16_bits(gelu_bf16_kernel_fp32(u, g)).astype(np.int64)
+    ref = bf16_bits(gelu_exact(u)).astype(np.int64)
+    assert np.mean(got != ref) < 1e-3
+    assert np.abs(got - ref).max() <= 1
