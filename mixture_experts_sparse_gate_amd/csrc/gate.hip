@@ -399,17 +399,15 @@ __global__ __launch_bounds__(kBlock) void cosine_select_kernel(CosineParams p) {
       *reinterpret_cast<f32x4*>(&es[r][c]) =
           e < N ? *reinterpret_cast<const f32x4*>(p.emb + (int64_t)e * P + c) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // norms: each wave takes 16 rows, lanes split the row
-    for (int r = wave * (kWave / kWavesPerBlock); r < (wave + 1) * (kWave / kWavesPerBlock); ++r) {
-      const int e = g * kWave + r;
+    __syncthreads();
+    // norms from the staged rows (zeros past N): four threads per row
+    {
+      const int r = threadIdx.x / 4, qd = threadIdx.x % 4;
       float ss = 0.f;
-      if (e < N)
-        for (int c = lane; c < P; c += kWave) {
-          const float v = p.emb[(int64_t)e * P + c];
-          ss += v * v;
-        }
-      ss = wave_sum(ss);
-      if (lane == 0) enorm[r] = fmaxf(sqrtf(ss), 1e-12f);
+      for (int c = qd; c < P; c += 4) ss = fmaf(es[r][c], es[r][c], ss);
+      ss += __shfl_xor(ss, 1, kWave);
+      ss += __shfl_xor(ss, 2, kWave);
+      if (qd == 0) enorm[r] = fmaxf(sqrtf(ss), 1e-12f);
     }
     __syncthreads();
   };
@@ -484,6 +482,159 @@ __global__ __launch_bounds__(kBlock) void cosine_select_kernel(CosineParams p) {
         for (int e = lane; e < N; e += kWave) p.logits[(int64_t)(t0 + t) * N + e] = lg[wave][t][e];
     select_tokens<kCosTW>(lg[wave], valid, N, p.k, p.renorm, p.topk_idx + (int64_t)t0 * p.k,
                           p.topk_w + (int64_t)t0 * p.k);
+  }
+}
+
+// Cosine gate for N <= 64 experts and p <= 256, 64 tokens per block. The
+// block stages its z rows and the expert table in LDS (every load in flight
+// at once), takes the norms from there, computes the 64 x N dot products on
+// the fp32 MFMA (one 32-token x 32-expert tile per wave, over all of p), and
+// selects with four lanes per token. Logits are acc / (|z| |e|) / tau + bias
+// as in the general kernel above.
+constexpr int kCgTok = 64;
+constexpr int kCgMaxN = 64;
+constexpr int kCgMaxP = 256;
+constexpr int kCgStride = kCgMaxP + 4;  // floats per staged row: 16-byte row reads spread over the banks
+constexpr int kCgLg = kCgMaxN + 1;      // floats per logit row
+
+__global__ __launch_bounds__(kBlock) void cosine_gate_kernel(CosineParams p) {
+  __shared__ __attribute__((aligned(16))) float zt[kCgTok * kCgStride];
+  __shared__ __attribute__((aligned(16))) float et[kCgMaxN * kCgStride];
+  __shared__ float lg[kCgTok * kCgLg];
+  __shared__ float zn[kCgTok], en[kCgMaxN];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int P = p.p, N = p.N, T = p.T;
+  const int t0 = blockIdx.x * kCgTok;
+
+  // ---- staging: 16-byte pieces, row r = 4 j + tid / 64, piece tid % 64
+  // (pieces past p, rows past T or N are zeros)
+  constexpr int J = kCgTok * (kCgMaxP / 4) / kBlock;
+  static_assert(kCgTok == kCgMaxN && J * kBlock == kCgTok * (kCgMaxP / 4), "staging shape");
+  const int c4 = tid % (kCgMaxP / 4);
+  const bool col_ok = 4 * c4 < P;
+  f32x4 zv[J], ev[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int r = j * (kBlock / (kCgMaxP / 4)) + tid / (kCgMaxP / 4);
+    zv[j] = col_ok && t0 + r < T ? *reinterpret_cast<const f32x4*>(p.z + (int64_t)(t0 + r) * P + 4 * c4)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+    ev[j] = col_ok && r < N ? *reinterpret_cast<const f32x4*>(p.emb + (int64_t)r * P + 4 * c4)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int r = j * (kBlock / (kCgMaxP / 4)) + tid / (kCgMaxP / 4);
+    if (col_ok) {
+      *reinterpret_cast<f32x4*>(&zt[r * kCgStride + 4 * c4]) = zv[j];
+      *reinterpret_cast<f32x4*>(&et[r * kCgStride + 4 * c4]) = ev[j];
+    }
+  }
+  __syncthreads();
+
+  // ---- norms: four threads per row, summed over the quad
+  {
+    const int r = tid / 4, qd = tid % 4;
+    float sz = 0.f, se = 0.f;
+    for (int c = qd; c < P; c += 4) {
+      const float a = zt[r * kCgStride + c], b = et[r * kCgStride + c];
+      sz = fmaf(a, a, sz);
+      se = fmaf(b, b, se);
+    }
+    sz += __shfl_xor(sz, 1, kWave);
+    sz += __shfl_xor(sz, 2, kWave);
+    se += __shfl_xor(se, 1, kWave);
+    se += __shfl_xor(se, 2, kWave);
+    if (qd == 0) {
+      zn[r] = fmaxf(sqrtf(sz), 1e-12f);
+      en[r] = fmaxf(sqrtf(se), 1e-12f);
+    }
+  }
+  __syncthreads();
+
+  // ---- dots: wave w takes tokens 32 (w % 2) .. and experts 32 (w / 2) ..
+  // One MFMA step multiplies k pair {c + i, c + 4 + i} (lane half h brings
+  // k = c + 4h + i of its row), so each lane reads 16 bytes per 4 steps.
+  // The lane ends up with token tt*32 + lane%32 and experts
+  // eb + 8(r/4) + 4(lane/32) + r%4 of its 16 accumulators.
+  {
+    const int tt = wave & 1, eb = (wave >> 1) * 32;
+    if (eb < N) {
+      const int row = lane & 31, h = lane >> 5;
+      const float* za = &zt[(tt * 32 + row) * kCgStride + 4 * h];
+      const float* ea = &et[(eb + row) * kCgStride + 4 * h];
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      for (int c = 0; c < P; c += 8) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(ea + c);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(za + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
+      }
+      const int t = tt * 32 + row;
+      const float znt = zn[t];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int e = eb + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (e < N) {
+          const float bias = p.logit_bias ? p.logit_bias[e] : 0.f;
+          lg[t * kCgLg + e] = acc[r] / (znt * en[e]) * p.inv_temperature + bias;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (p.logits)
+    for (int i = tid; i < kCgTok * N; i += kBlock) {
+      const int t = i / N, e = i % N;
+      if (t0 + t < T) p.logits[(int64_t)(t0 + t) * N + e] = lg[t * kCgLg + e];
+    }
+
+  // ---- selection: four lanes per token, lane q holding experts 16q .. 16q+15.
+  // Keys are (logit order, inverted index), so the largest key is the largest
+  // logit with ties to the lower index; the j-th winner is the largest key
+  // below the (j-1)-th.
+  const int tq = tid >> 2, qd = tid & 3, tok = t0 + tq;
+  const float* lrow = &lg[tq * kCgLg];
+  uint64_t key[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = 16 * qd + i;
+    key[i] = e < N ? ((uint64_t)float_order_key(lrow[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+  }
+  auto next_below = [&](uint64_t below) {
+    uint64_t b = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b = key[i] < below && key[i] > b ? key[i] : b;
+    uint64_t o = shfl_xor_u64(b, 1);
+    b = o > b ? o : b;
+    o = shfl_xor_u64(b, 2);
+    return o > b ? o : b;
+  };
+  auto expert_of = [](uint64_t kk) { return (int)(0xFFFFFFFFu - (uint32_t)kk); };
+  const float m = lrow[expert_of(next_below(~0ull))];  // the largest logit
+  float s = 0.f;
+  if (!p.renorm) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (16 * qd + i < N) s += expf(lrow[16 * qd + i] - m);
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
+  } else {
+    uint64_t b = ~0ull;
+    for (int j = 0; j < p.k; ++j) {
+      b = next_below(b);
+      s += expf(lrow[expert_of(b)] - m);
+    }
+  }
+  uint64_t b = ~0ull;
+  for (int j = 0; j < p.k; ++j) {
+    b = next_below(b);
+    if (tok < T && (j & 3) == qd) {
+      const int e = expert_of(b);
+      p.topk_idx[(int64_t)tok * p.k + j] = e;
+      p.topk_w[(int64_t)tok * p.k + j] = expf(lrow[e] - m) / s;
+    }
   }
 }
 
@@ -897,6 +1048,10 @@ hipError_t launch_gate_plain_noisy(const GateParams& p, bool bf16_, bool noisy, 
 }
 
 hipError_t launch_cosine_select(const CosineParams& p, hipStream_t s) {
+  if (p.N <= kCgMaxN && p.p <= kCgMaxP) {
+    hipLaunchKernelGGL(cosine_gate_kernel, dim3((p.T + kCgTok - 1) / kCgTok), dim3(kBlock), 0, s, p);
+    return hipGetLastError();
+  }
   const int nbatch = (p.T + kCosTW - 1) / kCosTW;
   const int want = (nbatch + kWavesPerBlock - 1) / kWavesPerBlock;
   const int grid = want < 256 ? want : 256;  // persistent: one block per CU stages the table once

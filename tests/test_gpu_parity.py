@@ -196,6 +196,11 @@ EDGE = {
     "cosine_small_p": workloads.MoESpec("cosine_small_p", T=1111, d=128, h=64, N=100, k=5,
                                         capacity_factor=0.9, gate="cosine", renorm=True, dtype="bf16",
                                         proj_dim=40, temperature=0.1, zipf_s=0.7),
+    # N <= 64: the single-pass cosine kernel, with a partly filled expert tile,
+    # renormalised weights, a small p and a ragged last block of tokens
+    "cosine_n40_renorm": workloads.MoESpec("cosine_n40_renorm", T=777, d=96, h=64, N=40, k=3,
+                                           capacity_factor=1.3, gate="cosine", renorm=True, dtype="bf16",
+                                           proj_dim=24, temperature=0.2, zipf_s=0.5, expert_bias=True),
 }
 
 
