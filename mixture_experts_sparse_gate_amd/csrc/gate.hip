@@ -84,64 +84,6 @@ __device__ void select_token(const float* lg, int N, int k, int renorm, int32_t*
   }
 }
 
-// Top-k selection and weights for one token by a single lane, for N <= 32
-// (same rules and the same (logit, index) key as select_token). The k
-// winners are found twice, once for the indices and the softmax
-// denominator, once for the weights, so that nothing is indexed by j.
-struct Pick {
-  uint32_t taken;  // experts taken so far, bit e
-  int e;           // the winner
-  float l;         // its logit
-};
-
-// The largest logit among the first N of v not yet taken, ties to the lower
-// index: candidates in ascending index, replaced only by a strictly larger
-// order key (the same order as select_token's (logit, -index) key).
-template <int NM>
-__device__ __forceinline__ Pick pick_next(const float (&v)[NM], int N, uint32_t taken) {
-  uint32_t best = 0;
-  int be = -1;
-  float bl = 0.f;
-#pragma unroll
-  for (int e = 0; e < NM; ++e) {
-    const uint32_t key = float_order_key(v[e]);
-    const bool better = e < N && !((taken >> e) & 1u) && (be < 0 || key > best);
-    best = better ? key : best;
-    be = better ? e : be;
-    bl = better ? v[e] : bl;
-  }
-  return Pick{taken | (1u << be), be, bl};
-}
-
-// Top-k selection and weights for one token by a single lane, N <= NM <= 32.
-// The k winners are found twice, once for the indices and the softmax
-// denominator, once for the weights, so that nothing is indexed by j.
-template <int NM>
-__device__ __forceinline__ void select_lane(const float* lg, int N, int k, int renorm, int32_t* idx_out,
-                                            float* w_out) {
-  float v[NM];
-#pragma unroll
-  for (int e = 0; e < NM; ++e) v[e] = e < N ? lg[e] : 0.f;
-  uint32_t taken = 0;
-  float m = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const Pick pk = pick_next(v, N, taken);
-    taken = pk.taken;
-    idx_out[j] = pk.e;
-    if (j == 0) m = pk.l;  // the largest logit
-  }
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < NM; ++e)
-    if (e < N && (!renorm || ((taken >> e) & 1u))) s += expf(v[e] - m);
-  uint32_t again = 0;
-  for (int j = 0; j < k; ++j) {
-    const Pick pk = pick_next(v, N, again);
-    again = pk.taken;
-    w_out[j] = expf(pk.l - m) / s;
-  }
-}
-
 // Top-k selection and weights for TW tokens at once (same rules as
 // select_token); the TW reductions are independent, so their shuffles
 // interleave instead of running back to back. lg[t] holds token t's N
@@ -798,8 +740,10 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
                                                                        GateParams p) {
   __shared__ __attribute__((aligned(1024))) char wl[kGfWaves][kGfRows * kGtCols * 2];
   __shared__ __attribute__((aligned(16))) float red[kGfWaves][kGtTok][kGtCols];
+  __shared__ int hs[kGtCols];  // the block's choices per expert, for the dispatch
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int t0 = blockIdx.x * kGtTok;
+  if (threadIdx.x < kGtCols) hs[threadIdx.x] = 0;  // read after the barriers below
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int q16 = lane >> 4, r16 = lane & 15;
   const int rows = min(kGtTok, q.T - t0);
@@ -909,7 +853,8 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
   __syncthreads();
   // logits of the block's tokens (waves' sums in wave order), into LDS rows
   // of 256 floats for the selection (the gate-row area is free now)
-  float (*lg)[kWave * kMaxExpertsPerLane] = reinterpret_cast<float (*)[kWave * kMaxExpertsPerLane]>(&wl[0][0]);
+  constexpr int kLg = kGtCols + 1;  // floats per logit row
+  float* const lg = reinterpret_cast<float*>(&wl[0][0]);
   const int N = p.N;
 #pragma unroll
   for (int j = 0; j < kPre; ++j) {
@@ -927,28 +872,64 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
     }
     if (p.logit_bias) l += pre_bias[j];
     if (p.logits) p.logits[(int64_t)tok * N + c] = l;
-    lg[t][c] = l;
+    lg[t * kLg + c] = l;
   }
   __syncthreads();
-  // selection: one lane per token
-  const int t = threadIdx.x;
-  int* const hs = reinterpret_cast<int*>(&red[0][0][0]);  // free now
-  if (p.hist && t >= kWave && t < kWave + N) hs[t - kWave] = 0;
-  int32_t* io = p.topk_idx + (int64_t)(t0 + t) * p.k;
-  if (t < kGtTok && t0 + t < p.T) {
-    float* wo = p.topk_w + (int64_t)(t0 + t) * p.k;
-    if (N <= 8) select_lane<8>(lg[t], N, p.k, p.renorm, io, wo);
-    else if (N <= 16) select_lane<16>(lg[t], N, p.k, p.renorm, io, wo);
-    else select_lane<32>(lg[t], N, p.k, p.renorm, io, wo);
+  // selection: eight lanes per token on waves 0-3, lane q of a group holding
+  // experts 4q .. 4q+3. Keys are (logit order, inverted index): the largest
+  // key is the largest logit with ties to the lower index, and the j-th
+  // winner is the largest key below the (j-1)-th.
+  const int tid = threadIdx.x;
+  if (tid < kGtTok * 8) {  // wave-uniform
+    const int tq = tid >> 3, q = tid & 7, tok = t0 + tq;
+    const float* lrow = lg + tq * kLg;
+    uint64_t key[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * q + i;
+      key[i] = e < N ? ((uint64_t)float_order_key(lrow[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e) : 0ull;
+    }
+    auto next_below = [&](uint64_t below) {
+      uint64_t b = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b = key[i] < below && key[i] > b ? key[i] : b;
+#pragma unroll
+      for (int m = 1; m < 8; m <<= 1) {
+        const uint64_t o = shfl_xor_u64(b, m);
+        b = o > b ? o : b;
+      }
+      return b;
+    };
+    auto expert_of = [](uint64_t kk) { return (int)(0xFFFFFFFFu - (uint32_t)kk); };
+    const float m = lrow[expert_of(next_below(~0ull))];  // the largest logit
+    float s = 0.f;
+    if (!p.renorm) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < N) s += expf(lrow[4 * q + i] - m);
+#pragma unroll
+      for (int mm = 1; mm < 8; mm <<= 1) s += __shfl_xor(s, mm, kWave);
+    } else {
+      uint64_t b = ~0ull;
+      for (int j = 0; j < p.k; ++j) {
+        b = next_below(b);
+        s += expf(lrow[expert_of(b)] - m);
+      }
+    }
+    uint64_t b = ~0ull;
+    for (int j = 0; j < p.k; ++j) {
+      b = next_below(b);
+      if (tok < p.T && (j & 7) == q) {
+        const int e = expert_of(b);
+        p.topk_idx[(int64_t)tok * p.k + j] = e;
+        p.topk_w[(int64_t)tok * p.k + j] = expf(lrow[e] - m) / s;
+        if (p.hist) atomicAdd(&hs[e], 1);
+      }
+    }
   }
   if (p.hist) {
-    // the block's choices per expert, for the dispatch (the lane reads back
-    // the indices it has just written)
     __syncthreads();
-    if (t < kGtTok && t0 + t < p.T)
-      for (int j = 0; j < p.k; ++j) atomicAdd(&hs[io[j]], 1);
-    __syncthreads();
-    if (t < N) p.hist[(int64_t)blockIdx.x * N + t] = hs[t];
+    if (tid < N) p.hist[(int64_t)blockIdx.x * N + tid] = hs[tid];
   }
 }
 
