@@ -63,7 +63,7 @@ extern "C" {
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID = 1,     /* bad argument: null/misaligned pointer, size out of range */
-  MOE_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+  MOE_ERR_UNSUPPORTED = 2, /* valid request the library does not implement */
   MOE_ERR_WORKSPACE = 3,   /* ws_bytes below moe_workspace_size() */
   MOE_ERR_HIP = 4          /* a HIP launch failed; moe_last_error() has the HIP message */
 } moe_status_t;
@@ -207,6 +207,17 @@ typedef struct moe_layer_tensors {
  * routing array the caller does not ask for. */
 MOE_API moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* tensors, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* Profiling aid. While set, the expert FFN's kernel launches (in
+ * moe_expert_ffn and moe_forward) record start_event (a hipEvent_t) when the
+ * FFN's first kernel begins executing and stop_event when its last kernel
+ * ends (hipExtLaunchKernel), so that hipEventElapsedTime(start, stop) is the
+ * FFN's execution time without launch overheads; with two launches that span
+ * includes the gap between them. NULL for both switches it off. The caller
+ * creates the events and keeps them alive while they are set. The setting is
+ * process-wide and unsynchronised: change it while no other thread enqueues
+ * layers. Always returns MOE_OK. */
+MOE_API moe_status_t moe_time_ffn_launches(void* start_event, void* stop_event);
 
 /* Static name of a status code. */
 MOE_API const char* moe_status_string(moe_status_t status);

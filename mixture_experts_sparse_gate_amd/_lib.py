@@ -48,6 +48,7 @@ SIGNATURES = {
     "moe_expert_ffn": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 8 + [c_void_p, c_size_t, c_void_p]),
     "moe_combine": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 4 + [c_void_p]),
     "moe_forward": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p, c_size_t, c_void_p]),
+    "moe_time_ffn_launches": (c_int, [c_void_p, c_void_p]),
     "moe_status_string": (c_char_p, [c_int]),
     "moe_last_error": (c_char_p, []),
     "moe_version": (c_char_p, []),

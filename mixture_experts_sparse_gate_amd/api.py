@@ -99,6 +99,13 @@ def expert_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, ws=None, str
     _check(st, "moe_expert_ffn")
 
 
+def time_ffn_launches(start_event=None, stop_event=None):
+    """Has the expert FFN's launches record two HIP events (hipEvent_t
+    handles, as ints) at the start and end of its kernels' execution; None
+    switches it off."""
+    _check(_lib.load().moe_time_ffn_launches(start_event, stop_event), "moe_time_ffn_launches")
+
+
 def combine(desc, y_perm, row_of, topk_w, y, stream=None):
     st = _lib.load().moe_combine(ctypes.byref(desc), _ptr(y_perm), _ptr(row_of), _ptr(topk_w), _ptr(y),
                                  _stream(stream))

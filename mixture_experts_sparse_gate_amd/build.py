@@ -3,7 +3,7 @@
     python -m mixture_experts_sparse_gate_amd.build [-j JOBS]
 
 Objects go to <repo>/_build/ and the library next to this file. Every call
-recompiles (the build is the check that the sources compile).
+recompiles, so a call always checks that the current sources compile.
 """
 from __future__ import annotations
 

@@ -312,6 +312,9 @@ int ffn_counters_of(const moe_desc_t* d) {
 // counters: fused-FFN counters (ffn_counters_of ints; cleared here unless
 // cleared says the dispatch did it) or null for two grouped-GEMM launches.
 // Both give the same bits.
+// Events the expert FFN's launches record (moe_time_ffn_launches), or null.
+moe::LaunchEvents g_ffn_events;
+
 moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of_row,
                     const int32_t* off, const void* W1, const void* b1, const void* W2,
                     const void* b2, void* H, void* y_perm, int32_t* counters, bool cleared, hipStream_t s) {
@@ -320,11 +323,12 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of
   const int max_rows = (int)capacity_of(d);
   moe::GemmParams g1, g2;
   ffn_gemms(d, A1, token_of_row, off, W1, b1, W2, b2, H, y_perm, &g1, &g2);
+  const moe::LaunchEvents ev = g_ffn_events;
   if (counters && moe::fused_ffn_fits(g1, g2, bf, avg_rows))
-    return hip_status(moe::launch_fused_ffn(g1, g2, counters, !cleared, s), "expert FFN");
-  TRY(hip_status(moe::launch_grouped_gemm(g1, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s),
+    return hip_status(moe::launch_fused_ffn(g1, g2, counters, !cleared, s, ev), "expert FFN");
+  TRY(hip_status(moe::launch_grouped_gemm(g1, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s, {ev.start, nullptr}),
                  "expert GEMM1"));
-  return hip_status(moe::launch_grouped_gemm(g2, moe::GemmKind::kFfn2, bf, avg_rows, max_rows, s),
+  return hip_status(moe::launch_grouped_gemm(g2, moe::GemmKind::kFfn2, bf, avg_rows, max_rows, s, {nullptr, ev.stop}),
                     "expert GEMM2");
 }
 
@@ -495,6 +499,12 @@ moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, v
                   fw.n_counters, hist));
   TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s));
   return do_combine(desc, y_perm, row_of, w, t->y, s);
+}
+
+moe_status_t moe_time_ffn_launches(void* start_event, void* stop_event) {
+  g_ffn_events.start = static_cast<hipEvent_t>(start_event);
+  g_ffn_events.stop = static_cast<hipEvent_t>(stop_event);
+  return MOE_OK;
 }
 
 const char* moe_status_string(moe_status_t st) {

@@ -33,6 +33,8 @@
 //  - GEMM1's activation rows can be gathered (row r reads A row
 //    gather[r] / gather_div) inside the tile loads.
 //  - No split-K and no atomics: each output element is written once.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -834,7 +836,7 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
 }
 
 template <class C>
-hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
+hipError_t launch_cfg(const GemmParams& p, hipStream_t s, LaunchEvents ev) {
   // upper bounds on the row tiles of each phase: per group, the full-height
   // tiles plus at most one partial one, and at most BM/(2 TBM) tail tiles;
   // each phase's blocks are a multiple of the XCD count
@@ -845,7 +847,11 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   if (p.M <= 0 || ntiles <= 0) return hipSuccess;
   auto xcd_round = [](int64_t n) { return (n + kNumXcds - 1) / kNumXcds * kNumXcds; };
   const int64_t blocks = xcd_round(full_max * ntiles) + xcd_round(tail_max * ntiles);
-  hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p);
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, ev.start,
+                          ev.stop, 0, p);
+  else
+    hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
@@ -860,8 +866,8 @@ constexpr int kNumCUs = 256;
 // tiles that stream the weights with deep prefetch.
 // Cfg<elem, out, BM, BN, waves M x N, K chunks per stage, stages, GELU>.
 template <typename E, typename O, bool G>
-hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStream_t s) {
-  if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, 8, 4, G>>(p, s);
+hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStream_t s, LaunchEvents ev) {
+  if (avg_rows < 64) return launch_cfg<Cfg<E, O, 32, 256, 1, 4, 8, 4, G>>(p, s, ev);
   // 256x256 tiles (8 waves, one block per CU) need half the L1 bandwidth per
   // flop of 128x128 ones; with ragged tails in cheap tail tiles run last,
   // they are the faster choice on every FFN shape of the workloads once they
@@ -869,8 +875,8 @@ hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStre
   const int groups = p.seg ? p.groups : 0;
   const int64_t tiles256 = (int64_t)(p.M / 256 + groups) * ((p.Ncols + 255) / 256);
   if (tiles256 >= kNumCUs / 2)
-    return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s);
-  return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s);
+    return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s, ev);
+  return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s, ev);
 }
 
 using FusedCfg = Cfg<bf16, bf16, 256, 256, 2, 4, 4, 4, false>;
@@ -899,29 +905,33 @@ bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16_, int 
 }
 
 hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
-                            hipStream_t s) {
+                            hipStream_t s, LaunchEvents ev) {
   if (clear) {
     const int n = fused_ffn_counters(g1);
     hipLaunchKernelGGL(fill_kernel, dim3((n + 255) / 256), dim3(256), 0, s, counters, n);
   }
   FusedFfn f{g1, g2, counters};
   // one block per CU (a multiple of the XCD count)
-  hipLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, f);
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, ev.start,
+                          ev.stop, 0, f);
+  else
+    hipLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, f);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16_, int avg_rows,
-                               int max_rows, hipStream_t s) {
+                               int max_rows, hipStream_t s, LaunchEvents ev) {
   switch (kind) {
     case GemmKind::kFfn1Gelu:
-      return bf16_ ? launch_dtype<bf16, bf16, true>(p, avg_rows, max_rows, s)
-                   : launch_dtype<float, float, true>(p, avg_rows, max_rows, s);
+      return bf16_ ? launch_dtype<bf16, bf16, true>(p, avg_rows, max_rows, s, ev)
+                   : launch_dtype<float, float, true>(p, avg_rows, max_rows, s, ev);
     case GemmKind::kFfn2:
-      return bf16_ ? launch_dtype<bf16, bf16, false>(p, avg_rows, max_rows, s)
-                   : launch_dtype<float, float, false>(p, avg_rows, max_rows, s);
+      return bf16_ ? launch_dtype<bf16, bf16, false>(p, avg_rows, max_rows, s, ev)
+                   : launch_dtype<float, float, false>(p, avg_rows, max_rows, s, ev);
     case GemmKind::kProjF32:
-      return bf16_ ? launch_dtype<bf16, float, false>(p, avg_rows, max_rows, s)
-                   : launch_dtype<float, float, false>(p, avg_rows, max_rows, s);
+      return bf16_ ? launch_dtype<bf16, float, false>(p, avg_rows, max_rows, s, ev)
+                   : launch_dtype<float, float, false>(p, avg_rows, max_rows, s, ev);
   }
   return hipErrorInvalidValue;
 }

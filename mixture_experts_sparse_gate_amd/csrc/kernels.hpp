@@ -85,9 +85,14 @@ struct GemmParams {
   int groups, K, Ncols;
 };
 enum class GemmKind { kFfn1Gelu, kFfn2, kProjF32 };
+// Events a launch records when its kernel starts and when it ends executing
+// (hipExtLaunchKernel), each or both null for none.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
 // avg_rows / max_rows: expected and largest rows per group (tile choice only)
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, int avg_rows,
-                               int max_rows, hipStream_t s);
+                               int max_rows, hipStream_t s, LaunchEvents ev = {});
 // The expert FFN (GEMM1 kFfn1Gelu, then GEMM2 kFfn2 on GEMM1's output) in one
 // persistent launch, where fused_ffn_fits(); counters: fused_ffn_counters()
 // ints, zero at launch (they are consumed): cleared first by a small kernel
@@ -95,7 +100,7 @@ hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, in
 bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16, int avg_rows);
 int fused_ffn_counters(const GemmParams& g1);
 hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
-                            hipStream_t s);
+                            hipStream_t s, LaunchEvents ev = {});
 
 // ---- combine (combine.hip)
 struct CombineParams {

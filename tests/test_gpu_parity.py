@@ -293,3 +293,36 @@ def test_dispatch_with_caller_routing():
     A = int(o[-1])
     assert np.array_equal(host(tor)[:A], t_o_r)
     assert torch.equal(x_perm[:A].view(torch.int16), x[torch.from_numpy(t_o_r // spec.k).cuda()].view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["noisy_top2_bf16", "decode_top8_bf16"])
+def test_ffn_launch_events(name):
+    """moe_time_ffn_launches: the FFN's launches (one persistent kernel for
+    noisy top-2, two grouped GEMMs for decode) record the events around their
+    execution, inside the span of the whole step, and change no result."""
+    spec = W[name]
+    inp = make_inputs(spec, workloads.WORKLOAD_SEED[name])
+    dev = api.DeviceLayer(inp)
+    dev.run_forward(inspect=False)
+    torch.cuda.synchronize()
+    y_ref = dev.y.clone()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    say(f"[case] FFN launch events {name}")
+    api.time_ffn_launches(e0._as_parameter_, e1._as_parameter_)
+    try:
+        dev.y.zero_()
+        a.record(s)
+        dev.run_forward(inspect=False)
+        b.record(s)
+        torch.cuda.synchronize()
+    finally:
+        api.time_ffn_launches(None, None)
+    ffn_ms, step_ms = e0.elapsed_time(e1), a.elapsed_time(b)
+    say(f"   FFN {ffn_ms * 1e3:.1f} us of a {step_ms * 1e3:.1f} us step")
+    assert 0 < ffn_ms < step_ms
+    assert torch.equal(dev.y, y_ref)
