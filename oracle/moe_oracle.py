@@ -30,6 +30,11 @@ in their order and notation:
                    ["MoE稀疏计算加速技术解析与应用实践" §3.2]
   combine          y = sum_i g_i(x) E_i(x) over the kept experts
                    ["MoE架构：突破单卡算力瓶颈的密钥" §1.2]
+  load balance     importance_e = sum_t gates[t, e] (before drops);
+                   load_balance_loss = sum_e (mean - importance_e)^2
+                   ["MoE架构：突破单卡算力瓶颈的密钥" §3.1];
+                   importance loss = 0.1 std(importance)
+                   ["MoE稀疏计算加速技术解析与应用实践" §4.1]
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): ties in top-k go to the lower expert index; selection compares
@@ -138,6 +143,35 @@ def sparse_gates(N: int, top_k_indices: np.ndarray, w: np.ndarray) -> np.ndarray
     g = np.zeros((top_k_indices.shape[0], N), np.float64)
     np.put_along_axis(g, top_k_indices, w, axis=1)
     return g
+
+
+# ----------------------------------------------------------------------------
+# Load-balance terms of the gate
+# ----------------------------------------------------------------------------
+
+def expert_importance(N: int, top_k_indices: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """The load each expert receives from the gate: the column sums of the
+    sparse gate matrix, before any capacity drop (gate_output.sum(dim=0) on
+    "MoE架构：突破单卡算力瓶颈的密钥" §3.1, gates.sum(dim=0) on
+    "MoE稀疏计算加速技术解析与应用实践" §4.1)."""
+    return sparse_gates(N, top_k_indices, w).sum(axis=0)
+
+
+def load_balance_loss(importance: np.ndarray) -> float:
+    """The sum over experts of (mean load - load)^2
+    ["MoE架构：突破单卡算力瓶颈的密钥" §3.1, load_balance_loss]."""
+    mean = importance.mean()
+    return float(((mean - importance) ** 2).sum())
+
+
+def importance_loss(importance: np.ndarray) -> float:
+    """0.1 times the standard deviation of the loads, with torch.std's default
+    N - 1 denominator ["MoE稀疏计算加速技术解析与应用实践" §4.1,
+    expert_importance_loss]; NaN for a single expert, as that estimate is."""
+    N = importance.shape[0]
+    if N < 2:
+        return float("nan")
+    return 0.1 * float(np.sqrt(((importance - importance.mean()) ** 2).sum() / (N - 1)))
 
 
 # ----------------------------------------------------------------------------

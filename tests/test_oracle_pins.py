@@ -244,6 +244,50 @@ def test_noisy_topk_gating_of_the_pages():
     np.testing.assert_allclose(O.sparse_gates(s.N, r["topk_idx"], r["topk_w"]), ref, rtol=1e-13, atol=1e-15)
 
 
+# ---------------------------------------------------------------- load balance
+
+def test_load_balance_terms_hand_worked():
+    """Two tokens, both routed to expert 0 of 3 with weight 1: loads [2, 0, 0],
+    mean 2/3, so the squared-deviation loss is (4/3)^2 + 2 (2/3)^2 = 8/3 and
+    the unbiased standard deviation is sqrt((16/9 + 8/9) / 2) = sqrt(4/3)."""
+    idx = np.array([[0], [0]])
+    w = np.array([[1.0], [1.0]])
+    imp = O.expert_importance(3, idx, w)
+    assert imp.tolist() == [2.0, 0.0, 0.0]
+    assert math.isclose(O.load_balance_loss(imp), 8 / 3, rel_tol=1e-15)
+    assert math.isclose(O.importance_loss(imp), 0.1 * math.sqrt(4 / 3), rel_tol=1e-15)
+
+
+def test_load_balance_terms_vanish_on_uniform_load():
+    """Token t goes to experts t % N and (t + 1) % N with weights 0.25 and
+    0.75: every expert receives the same load and both losses are zero."""
+    T, N = 40, 8
+    idx = np.stack([np.arange(T) % N, (np.arange(T) + 1) % N], axis=1)
+    w = np.tile([0.25, 0.75], (T, 1))
+    imp = O.expert_importance(N, idx, w)
+    np.testing.assert_allclose(imp, np.full(N, T / N), rtol=0, atol=1e-14)
+    assert O.load_balance_loss(imp) < 1e-26 and O.importance_loss(imp) < 1e-14
+
+
+def test_importance_of_a_routing():
+    """On a routed layer: importance equals a loop over every (token, choice);
+    with renormalised weights each token contributes exactly 1 in total; the
+    squared-deviation loss is N - 1 times the variance whose root the
+    importance loss takes; one expert alone leaves the standard deviation
+    undefined (NaN)."""
+    s = _small("noisy", T=50, N=6, k=2, renorm=True)
+    r = O.route(s, make_inputs(s, seed=3))
+    imp = O.expert_importance(s.N, r["topk_idx"], r["topk_w"])
+    brute = np.zeros(s.N)
+    for t in range(s.T):
+        for j in range(s.k):
+            brute[r["topk_idx"][t, j]] += r["topk_w"][t, j]
+    np.testing.assert_allclose(imp, brute, rtol=1e-14)
+    assert math.isclose(imp.sum(), s.T, rel_tol=1e-13)
+    assert math.isclose(O.load_balance_loss(imp), 100 * (s.N - 1) * O.importance_loss(imp) ** 2, rel_tol=1e-12)
+    assert math.isnan(O.importance_loss(np.array([5.0])))
+
+
 # ---------------------------------------------------------------- gate pieces
 
 def test_noisy_with_zero_noise_is_plain_gate():
