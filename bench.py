@@ -11,7 +11,8 @@ headline value is T tokens over the mean step time.
 Besides the headline:
   - stages: the same layer through the four stage entry points, with HIP
     events recorded on the launch stream between them; their averages give
-    each stage's duration (and the expert FFN's for the roofline object);
+    each stage's duration; aux_loss: moe_aux_loss (per-expert importance and
+    the two load-balance losses) on the step's routing, timed the same way;
   - graph_ms_per_step: moe_forward captured once in a HIP graph and replayed
     (no host launch cost per kernel);
   - cold: each step timed alone by events after writing a 512 MiB buffer
@@ -299,6 +300,19 @@ def main() -> int:
                        "touched_weight_GB/s": touched_weight_bytes / stage_ms["expert_ffn"] / 1e6},
         "combine": {"ms": stage_ms["combine"], "GB/s": comb_bytes / (stage_ms["combine"] * 1e-3) / 1e9},
     }
+    # load-balance terms on this step's routing (optional output; not in the step)
+    aux_ws = api.workspace(dev.desc, _lib.MOE_WS_AUX)
+    aux_imp = torch.empty(N, dtype=torch.float32, device="cuda")
+    aux_loss = torch.empty(2, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        api.aux_loss(dev.desc, dev.topk_idx, dev.topk_w, aux_imp, aux_loss, aux_ws)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(K):
+        api.aux_loss(dev.desc, dev.topk_idx, dev.topk_w, aux_imp, aux_loss, aux_ws)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    stages["aux_loss"] = {"ms": a0.elapsed_time(a1) / K, "T*k": T * k}
 
     cpu = None
     if args.cpu_seconds > 0:

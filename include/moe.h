@@ -103,7 +103,8 @@ typedef enum moe_ws_kind {
   MOE_WS_ROUTE = 0,
   MOE_WS_DISPATCH = 1,
   MOE_WS_FORWARD = 2,
-  MOE_WS_FFN = 3
+  MOE_WS_FFN = 3,
+  MOE_WS_AUX = 4
 } moe_ws_kind_t;
 
 /* Expert capacity C = min(T, ceil((capacity_factor * (T*k)) / N)), evaluated
@@ -207,6 +208,25 @@ typedef struct moe_layer_tensors {
  * routing array the caller does not ask for. */
 MOE_API moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* tensors, void* ws,
                          size_t ws_bytes, void* stream);
+
+/* Load-balance terms of a routing (the topk_idx / topk_w that moe_route or
+ * moe_forward produced), for an auxiliary training loss.
+ *   importance [N] fp32: importance[e] = the sum over tokens t and choices j
+ *   of topk_w[t, j] where topk_idx[t, j] == e, i.e. the column sums of the
+ *   [T, N] sparse gate matrix, counted before capacity drops
+ *   (gate_output.sum(dim=0) on "MoE架构：突破单卡算力瓶颈的密钥" §3.1,
+ *   gates.sum(dim=0) on "MoE稀疏计算加速技术解析与应用实践" §4.1).
+ *   losses [2] fp32: losses[0] = the sum over experts of
+ *   (mean importance - importance[e])^2 (load_balance_loss of the first
+ *   page); losses[1] = 0.1 times the standard deviation of importance with
+ *   the N - 1 denominator (expert_importance_loss of the second page; NaN
+ *   when N = 1).
+ * Sums run in fp32 in a fixed order: repeated calls give the same bits.
+ * Either output may be NULL (both NULL: nothing is launched). topk_idx
+ * entries outside [0, N) count for no expert. ws: MOE_WS_AUX bytes. */
+MOE_API moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_idx, const float* topk_w,
+                                  float* importance, float* losses, void* ws, size_t ws_bytes,
+                                  void* stream);
 
 /* Profiling aid. While set, the expert FFN's kernel launches (in
  * moe_expert_ffn and moe_forward) record start_event (a hipEvent_t) when the

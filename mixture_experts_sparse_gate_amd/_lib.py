@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_gfx950.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_NOISY, MOE_GATE_COSINE = 0, 1, 2
-MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_FORWARD, MOE_WS_FFN = 0, 1, 2, 3
+MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_FORWARD, MOE_WS_FFN, MOE_WS_AUX = 0, 1, 2, 3, 4
 
 
 class MoeDesc(ctypes.Structure):
@@ -49,6 +49,8 @@ SIGNATURES = {
     "moe_combine": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 4 + [c_void_p]),
     "moe_forward": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p, c_size_t, c_void_p]),
     "moe_time_ffn_launches": (c_int, [c_void_p, c_void_p]),
+    "moe_aux_loss": (c_int, [POINTER(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                             c_void_p]),
     "moe_status_string": (c_char_p, [c_int]),
     "moe_last_error": (c_char_p, []),
     "moe_version": (c_char_p, []),

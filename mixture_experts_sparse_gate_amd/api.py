@@ -99,6 +99,15 @@ def expert_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, ws=None, str
     _check(st, "moe_expert_ffn")
 
 
+def aux_loss(desc, topk_idx, topk_w, importance=None, losses=None, ws=None, stream=None):
+    """Per-expert importance [N] and the two load-balance losses [2] of a
+    routing (moe_aux_loss); either output may be None."""
+    st = _lib.load().moe_aux_loss(ctypes.byref(desc), _ptr(topk_idx), _ptr(topk_w), _ptr(importance),
+                                  _ptr(losses), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    _check(st, "moe_aux_loss")
+
+
 def time_ffn_launches(start_event=None, stop_event=None):
     """Has the expert FFN's launches record two HIP events (hipEvent_t
     handles, as ints) at the start and end of its kernels' execution; None

@@ -393,6 +393,7 @@ moe_status_t moe_workspace_size(const moe_desc_t* desc, moe_ws_kind_t kind, size
     case MOE_WS_DISPATCH: *bytes = dispatch_ws(desc).bytes; return MOE_OK;
     case MOE_WS_FORWARD: *bytes = forward_ws(desc).bytes; return MOE_OK;
     case MOE_WS_FFN: *bytes = align_up((size_t)ffn_counters_of(desc) * 4); return MOE_OK;
+    case MOE_WS_AUX: *bytes = align_up((size_t)moe::aux_blocks(desc->T) * desc->N * 4); return MOE_OK;
   }
   return fail(MOE_ERR_INVALID, "unknown workspace kind %d", (int)kind);
 }
@@ -499,6 +500,28 @@ moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, v
                   fw.n_counters, hist));
   TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s));
   return do_combine(desc, y_perm, row_of, w, t->y, s);
+}
+
+moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_idx, const float* topk_w,
+                          float* importance, float* losses, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_desc(desc));
+  TRY(need(topk_idx, "topk_idx", 4));
+  TRY(need(topk_w, "topk_w", 4));
+  TRY(maybe(importance, "importance", 4));
+  TRY(maybe(losses, "losses", 4));
+  const size_t need_bytes = align_up((size_t)moe::aux_blocks(desc->T) * desc->N * 4);
+  TRY(check_ws(ws, ws_bytes, need_bytes));
+  if (!importance && !losses) return MOE_OK;
+  moe::AuxParams p{};
+  p.topk_idx = topk_idx;
+  p.topk_w = topk_w;
+  p.partial = static_cast<float*>(ws);
+  p.importance = importance;
+  p.losses = losses;
+  p.T = (int)desc->T;
+  p.N = desc->N;
+  p.k = desc->k;
+  return hip_status(moe::launch_aux_loss(p, (hipStream_t)stream), "load-balance terms");
 }
 
 moe_status_t moe_time_ffn_launches(void* start_event, void* stop_event) {

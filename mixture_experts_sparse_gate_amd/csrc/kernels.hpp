@@ -102,6 +102,19 @@ int fused_ffn_counters(const GemmParams& g1);
 hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
                             hipStream_t s, LaunchEvents ev = {});
 
+// ---- load-balance terms (aux.hip)
+constexpr int kAuxTok = 256;  // tokens per partial-sum block
+struct AuxParams {
+  const int32_t* topk_idx;  // [T, k]
+  const float* topk_w;      // [T, k]
+  float* partial;           // [aux_blocks(T), N] workspace
+  float* importance;        // [N] or null
+  float* losses;            // [2] or null
+  int T, N, k;
+};
+int aux_blocks(int64_t T);
+hipError_t launch_aux_loss(const AuxParams& p, hipStream_t s);
+
 // ---- combine (combine.hip)
 struct CombineParams {
   const void* y_perm;      // [R, d]

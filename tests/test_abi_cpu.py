@@ -87,6 +87,10 @@ def test_workspace_sizes(lib):
         assert sizes[2] >= sizes[0] + sizes[1] + sizes[3]
         assert sizes[2] > prev
         prev = sizes[2]
+        # the load-balance terms: one fp32 partial sum per expert per 256 tokens
+        n = ctypes.c_size_t()
+        assert lib.moe_workspace_size(ctypes.byref(d), _lib.MOE_WS_AUX, ctypes.byref(n)) == _lib.MOE_OK
+        assert n.value % 256 == 0 and n.value >= ((T + 255) // 256) * d.N * 4
 
 
 def _bad(spec, **kw):
@@ -176,6 +180,10 @@ def test_stage_argument_checks(lib):
     assert lib.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
     assert lib.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 4, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_dispatch(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
+    # moe_aux_loss: both routing arrays required, outputs aligned, workspace sized
+    assert lib.moe_aux_loss(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_aux_loss(ctypes.byref(d), FAKE, FAKE, FAKE + 2, None, FAKE, 1 << 20, None) == _lib.MOE_ERR_INVALID
+    assert lib.moe_aux_loss(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("kw", [dict(T=1 << 20, d=1024, h=8192), dict(T=64, d=65536, h=32768),

@@ -6,6 +6,8 @@ check every stage; the full-size workloads run moe_forward in the same
 launch configuration bench.py times and are checked on everything that is
 cheap to check exactly (routing, slots, offsets, row maps) and on sampled
 rows and tokens otherwise."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -326,3 +328,41 @@ def test_ffn_launch_events(name):
     say(f"   FFN {ffn_ms * 1e3:.1f} us of a {step_ms * 1e3:.1f} us step")
     assert 0 < ffn_ms < step_ms
     assert torch.equal(dev.y, y_ref)
+
+
+def _aux(dev, spec, importance=True, losses=True):
+    imp = torch.full((spec.N,), -1.0, dtype=torch.float32, device="cuda") if importance else None
+    los = torch.full((2,), -1.0, dtype=torch.float32, device="cuda") if losses else None
+    api.aux_loss(dev.desc, dev.topk_idx, dev.topk_w, imp, los, api.workspace(dev.desc, _lib.MOE_WS_AUX))
+    torch.cuda.synchronize()
+    return imp, los
+
+
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER + ["single_expert"])
+def test_aux_loss_matches_oracle(name):
+    """moe_aux_loss on the GPU's own routing: the importance against the
+    oracle's column sums of the sparse gate matrix, the losses against the
+    oracle's formulas on that importance; the same bits on a second call, and
+    either output alone."""
+    spec = W[name] if name in W else EDGE[name]
+    inp = make_inputs(spec, workloads.WORKLOAD_SEED.get(name, 5))
+    dev = api.DeviceLayer(inp)
+    dev.run_forward(inspect=True)
+    torch.cuda.synchronize()
+    say(f"[case] aux loss {name}")
+    imp, los = _aux(dev, spec)
+    ref = O.expert_importance(spec.N, host(dev.topk_idx), host(dev.topk_w).astype(np.float64))
+    got = host(imp).astype(np.float64)
+    np.testing.assert_allclose(got, ref, rtol=2e-5, atol=1e-6)
+    l0, l1 = (float(v) for v in host(los))
+    say(f"   importance {got.min():.4g}..{got.max():.4g}, losses {l0:.6g} {l1:.6g}")
+    assert math.isclose(l0, O.load_balance_loss(got), rel_tol=1e-4, abs_tol=1e-6 * max(1.0, ref.max()) ** 2)
+    if spec.N == 1:
+        assert l0 == 0.0 and math.isnan(l1)
+    else:
+        assert math.isclose(l1, O.importance_loss(got), rel_tol=1e-4, abs_tol=1e-7 * max(1.0, ref.max()))
+    imp2, los2 = _aux(dev, spec)
+    assert torch.equal(imp2, imp) and torch.equal(los2[:1], los[:1])
+    only_imp, none_l = _aux(dev, spec, losses=False)
+    none_i, only_l = _aux(dev, spec, importance=False)
+    assert torch.equal(only_imp, imp) and torch.equal(only_l[:1], los[:1])
