@@ -28,9 +28,23 @@ __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(AuxParams p) {
   const int t0 = blockIdx.x * kAuxTok;
   const int n = min(kAuxTok, p.T - t0) * p.k;  // the block's choices
   const int64_t base = (int64_t)t0 * p.k;
-  for (int i = tid; i < n; i += kAuxThreads) {
-    si[i] = p.topk_idx[base + i];
-    sw[i] = p.topk_w[base + i];
+  for (int i0 = 0; i0 < n; i0 += 4 * kAuxThreads) {  // four loads of each array in flight per thread
+    int vi[4];
+    float vw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kAuxThreads + tid;
+      vi[u] = i < n ? p.topk_idx[base + i] : 0;
+      vw[u] = i < n ? p.topk_w[base + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kAuxThreads + tid;
+      if (i < n) {
+        si[i] = vi[u];
+        sw[i] = vw[u];
+      }
+    }
   }
   __syncthreads();
   // thread (expert e, range g); weights are >= 0, so adding 0 for another
@@ -39,7 +53,19 @@ __global__ __launch_bounds__(kAuxThreads) void aux_partial_kernel(AuxParams p) {
   if (g < G) {
     const int lo = (int)((int64_t)n * g / G), hi = (int)((int64_t)n * (g + 1) / G);
     float s = 0.f;
-    for (int i = lo; i < hi; ++i) s += si[i] == e ? sw[i] : 0.f;
+    int i = lo;
+    for (; i + 8 <= hi; i += 8) {  // eight entries' LDS reads in flight, added in order
+      int ii[8];
+      float ww[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        ii[u] = si[i + u];
+        ww[u] = sw[i + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += ii[u] == e ? ww[u] : 0.f;
+    }
+    for (; i < hi; ++i) s += si[i] == e ? sw[i] : 0.f;
     part[g * N + e] = s;
   }
   __syncthreads();
@@ -58,7 +84,15 @@ __global__ __launch_bounds__(kAuxThreads) void aux_final_kernel(AuxParams p, int
   if (g < G) {
     const int lo = (int)((int64_t)nb * g / G), hi = (int)((int64_t)nb * (g + 1) / G);
     float s = 0.f;
-    for (int b = lo; b < hi; ++b) s += p.partial[(int64_t)b * N + e];
+    int b = lo;
+    for (; b + 8 <= hi; b += 8) {  // eight loads in flight, added in block order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p.partial[(int64_t)(b + u) * N + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < hi; ++b) s += p.partial[(int64_t)b * N + e];
     part[g * N + e] = s;
   }
   __syncthreads();
