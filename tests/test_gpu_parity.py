@@ -198,6 +198,12 @@ EDGE = {
     "cosine_small_p": workloads.MoESpec("cosine_small_p", T=1111, d=128, h=64, N=100, k=5,
                                         capacity_factor=0.9, gate="cosine", renorm=True, dtype="bf16",
                                         proj_dim=40, temperature=0.1, zipf_s=0.7),
+    # k past 8: the combine's one-row-at-a-time path; k = 32, the largest the
+    # library takes, also fills the load-balance kernel's staging arrays
+    "k12_bf16": workloads.MoESpec("k12_bf16", T=300, d=64, h=96, N=40, k=12, capacity_factor=1.0,
+                                  gate="softmax", renorm=False, dtype="bf16"),
+    "k32_f32": workloads.MoESpec("k32_f32", T=290, d=32, h=64, N=33, k=32, capacity_factor=2.0,
+                                 gate="noisy", renorm=True, dtype="f32", expert_bias=True),
     # N <= 64: the single-pass cosine kernel, with a partly filled expert tile,
     # renormalised weights, a small p and a ragged last block of tokens
     "cosine_n40_renorm": workloads.MoESpec("cosine_n40_renorm", T=777, d=96, h=64, N=40, k=3,
@@ -338,7 +344,7 @@ def _aux(dev, spec, importance=True, losses=True):
     return imp, los
 
 
-@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER + ["single_expert"])
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER + ["single_expert", "k32_f32"])
 def test_aux_loss_matches_oracle(name):
     """moe_aux_loss on the GPU's own routing: the importance against the
     oracle's column sums of the sparse gate matrix, the losses against the
