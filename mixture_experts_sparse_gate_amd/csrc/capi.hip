@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "moe.h"
 #include "kernels.hpp"
 
@@ -309,6 +311,28 @@ int ffn_counters_of(const moe_desc_t* d) {
   return moe::fused_ffn_fits(g1, g2, d->dtype == MOE_BF16, avg_rows) ? moe::fused_ffn_counters(g1) : 0;
 }
 
+// The single-launch FFN deals its work to one queue per XCD of the full
+// chip (256 CUs in 8 XCDs), each queue drained by the blocks whose hardware
+// XCC_ID names it. A device that is a partition of the chip has fewer XCDs,
+// so some queues would have no blocks and their tiles would never run: such
+// a device takes the two grouped-GEMM launches, whose result does not depend
+// on where blocks are placed.
+bool whole_chip_device() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> known[kMaxDevices];  // 0 unknown, 1 whole chip, 2 not
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return false;
+  int v = known[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    const bool ok =
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus == 256;
+    v = ok ? 1 : 2;
+    known[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
 // counters: fused-FFN counters (ffn_counters_of ints; cleared here unless
 // cleared says the dispatch did it) or null for two grouped-GEMM launches.
 // Both give the same bits.
@@ -324,7 +348,7 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of
   moe::GemmParams g1, g2;
   ffn_gemms(d, A1, token_of_row, off, W1, b1, W2, b2, H, y_perm, &g1, &g2);
   const moe::LaunchEvents ev = g_ffn_events;
-  if (counters && moe::fused_ffn_fits(g1, g2, bf, avg_rows))
+  if (counters && moe::fused_ffn_fits(g1, g2, bf, avg_rows) && whole_chip_device())
     return hip_status(moe::launch_fused_ffn(g1, g2, counters, !cleared, s, ev), "expert FFN");
   TRY(hip_status(moe::launch_grouped_gemm(g1, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s, {ev.start, nullptr}),
                  "expert GEMM1"));
