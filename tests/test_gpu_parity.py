@@ -140,6 +140,10 @@ FUSED = {
     # skewed demand over 16 experts: empty, small and capped groups, tails
     "zipf16_top2": workloads.MoESpec("zipf16_top2", T=8192, d=1024, h=1024, N=16, k=2, capacity_factor=2.0,
                                      gate="softmax", renorm=True, dtype="bf16", zipf_s=1.5),
+    # the same skew with fewer GEMM2 tiles than CUs: empty groups, tails
+    "skew16_few_tiles": workloads.MoESpec("skew16_few_tiles", T=3000, d=1024, h=2048, N=16, k=2,
+                                          capacity_factor=2.0, gate="softmax", renorm=True, dtype="bf16",
+                                          zipf_s=1.5),
 }
 
 
