@@ -209,6 +209,51 @@ typedef struct moe_layer_tensors {
 MOE_API moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* tensors, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* Block-FP8 expert weights: FP8 weights shrink the model ("MoE架构：突破单卡
+ * 算力瓶颈的密钥" §1.3), held with a scale per block ("Block FP8" serving on
+ * MI300 in the CUDA-to-ROCm section of "4大技术模块掌握Tutel MoE…").
+ * Quantises a stack W [groups, K, Ncols] of `dtype` values (MOE_F32 or
+ * MOE_BF16; finite) in blocks of 128 x 128:
+ *   scales [groups, K/128, Ncols/128] fp32: s = amax / 448, amax the
+ *   largest |w| of the block (one fp32 division);
+ *   codes: the OCP E4M3 byte (bias 7, 3 mantissa bits, largest 448) of the
+ *   fp32 quotient w / s rounded to nearest, ties to even, with w's sign; an
+ *   all-zero block has s = 0 and zero codes.
+ * codes layout: K-groups of 8, the byte of w[g][k][n] at
+ *   ((g * K/8 + k/8) * Ncols + n) * 8 + k % 8,
+ * so that each column's 8 consecutive K values are contiguous.
+ * K and Ncols positive multiples of 128; W and codes 16-byte aligned,
+ * scales 4-byte. Any other shape: MOE_ERR_INVALID. */
+MOE_API moe_status_t moe_quantize_fp8(const void* W, int32_t dtype, int32_t groups, int32_t K, int32_t Ncols,
+                                      uint8_t* codes, float* scales, void* stream);
+
+/* moe_expert_ffn with block-FP8 expert weights (bf16 layers with d and h
+ * multiples of 128, else MOE_ERR_UNSUPPORTED): W1q / S1 are
+ * moe_quantize_fp8 of W1 [N, d, h], W2q / S2 of W2 [N, h, d]. With W' the
+ * dequantised weights (decoded code times its block's scale):
+ *   H[r] = GELU(x_perm[r] W1'[e] + b1[e]), y_perm[r] = H[r] W2'[e] + b2[e],
+ * each product accumulated in fp32 over each 128-deep block of K, scaled
+ * once and added to the sum in K order; rounded once to bf16. The kernel
+ * streams the weights with 32-row tiles whatever the row count (the shape
+ * of decoding, where the weight bytes bound the layer). */
+MOE_API moe_status_t moe_expert_ffn_fp8(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
+                                        const uint8_t* W1q, const float* S1, const void* b1, const uint8_t* W2q,
+                                        const float* S2, const void* b2, void* H, void* y_perm, void* stream);
+
+/* A layer's block-FP8 expert weights (moe_quantize_fp8 of W1 and W2). */
+typedef struct moe_fp8_weights {
+  const uint8_t* W1q;
+  const float* S1;
+  const uint8_t* W2q;
+  const float* S2;
+} moe_fp8_weights_t;
+
+/* moe_forward with the expert FFN of moe_expert_ffn_fp8: tensors->W1 and
+ * tensors->W2 are not read (they may be NULL); the weights are w8's. The
+ * routing and combine are moe_forward's. ws: MOE_WS_FORWARD bytes. */
+MOE_API moe_status_t moe_forward_fp8(const moe_desc_t* desc, const moe_layer_tensors_t* tensors,
+                                     const moe_fp8_weights_t* w8, void* ws, size_t ws_bytes, void* stream);
+
 /* Load-balance terms of a routing (the topk_idx / topk_w that moe_route or
  * moe_forward produced), for an auxiliary training loss.
  *   importance [N] fp32: importance[e] = the sum over tokens t and choices j

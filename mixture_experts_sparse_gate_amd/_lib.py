@@ -38,6 +38,10 @@ class MoeLayerTensors(ctypes.Structure):
         "logits", "topk_idx", "topk_w", "expert_count", "expert_off", "row_of", "token_of_row")]
 
 
+class MoeFp8Weights(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in ("W1q", "S1", "W2q", "S2")]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "moe_capacity": (c_int64, [POINTER(MoeDesc)]),
@@ -49,6 +53,10 @@ SIGNATURES = {
     "moe_combine": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 4 + [c_void_p]),
     "moe_forward": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p, c_size_t, c_void_p]),
     "moe_time_ffn_launches": (c_int, [c_void_p, c_void_p]),
+    "moe_quantize_fp8": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+    "moe_expert_ffn_fp8": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 10 + [c_void_p]),
+    "moe_forward_fp8": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), POINTER(MoeFp8Weights), c_void_p,
+                                c_size_t, c_void_p]),
     "moe_aux_loss": (c_int, [POINTER(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                              c_void_p]),
     "moe_status_string": (c_char_p, [c_int]),

@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MoeDesc, MoeLayerTensors
+from ._lib import MoeDesc, MoeFp8Weights, MoeLayerTensors
 from .workloads import MoESpec
 
 _GATES = {"softmax": _lib.MOE_GATE_SOFTMAX, "noisy": _lib.MOE_GATE_NOISY, "cosine": _lib.MOE_GATE_COSINE}
@@ -132,6 +132,46 @@ def forward(desc, tensors: dict, ws: torch.Tensor, stream=None):
     _check(st, "moe_forward")
 
 
+FP8_BLOCK = 128
+
+
+def quantize_fp8(W: torch.Tensor, codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Block-FP8 form of a weight stack W [groups, K, Ncols] (fp32 or bf16):
+    (codes uint8 [groups, K/8, Ncols, 8], scales fp32 [groups, K/128, Ncols/128])
+    as moe_quantize_fp8 lays them out."""
+    if W.dim() != 3 or W.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("W must be a [groups, K, Ncols] fp32 or bf16 tensor")
+    G, K, N = W.shape
+    if codes is None:
+        codes = torch.empty(G, K // 8, N, 8, dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty(G, K // FP8_BLOCK, N // FP8_BLOCK, dtype=torch.float32, device=W.device)
+    dt = _lib.MOE_BF16 if W.dtype == torch.bfloat16 else _lib.MOE_F32
+    st = _lib.load().moe_quantize_fp8(_ptr(W), dt, G, K, N, _ptr(codes), _ptr(scales), _stream(stream))
+    _check(st, "moe_quantize_fp8")
+    return codes, scales
+
+
+def expert_ffn_fp8(desc, x_perm, expert_off, W1q, S1, b1, W2q, S2, b2, H, y_perm, stream=None):
+    st = _lib.load().moe_expert_ffn_fp8(ctypes.byref(desc), _ptr(x_perm), _ptr(expert_off), _ptr(W1q), _ptr(S1),
+                                        _ptr(b1), _ptr(W2q), _ptr(S2), _ptr(b2), _ptr(H), _ptr(y_perm),
+                                        _stream(stream))
+    _check(st, "moe_expert_ffn_fp8")
+
+
+def forward_fp8(desc, tensors: dict, w8: dict, ws: torch.Tensor, stream=None):
+    """moe_forward_fp8; w8: W1q, S1, W2q, S2 (quantize_fp8 of W1 and W2)."""
+    unknown = set(tensors) - {f for f, _ in MoeLayerTensors._fields_}
+    if unknown:
+        raise KeyError(f"unknown tensor names {sorted(unknown)}")
+    lt = MoeLayerTensors(**{k: _ptr(v) for k, v in tensors.items() if v is not None})
+    wq = MoeFp8Weights(**{k: _ptr(w8[k]) for k in ("W1q", "S1", "W2q", "S2")})
+    st = _lib.load().moe_forward_fp8(ctypes.byref(desc), ctypes.byref(lt), ctypes.byref(wq), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_forward_fp8")
+
+
 # ---------------------------------------------------------------- convenience
 
 class DeviceLayer:
@@ -202,3 +242,15 @@ class DeviceLayer:
 
     def run_forward(self, inspect: bool = True, stream=None):
         forward(self.desc, self.layer_tensors(inspect), self.ws, stream=stream)
+
+    def quantize_weights_fp8(self, stream=None):
+        """Block-FP8 copies of W1 and W2 (moe_quantize_fp8), kept as self.w8."""
+        W1q, S1 = quantize_fp8(self.W1, stream=stream)
+        W2q, S2 = quantize_fp8(self.W2, stream=stream)
+        self.w8 = dict(W1q=W1q, S1=S1, W2q=W2q, S2=S2)
+        return self.w8
+
+    def run_forward_fp8(self, inspect: bool = True, stream=None):
+        t = self.layer_tensors(inspect)
+        t.update(W1=None, W2=None)
+        forward_fp8(self.desc, t, self.w8, self.ws, stream=stream)

@@ -356,6 +356,28 @@ moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of
                     "expert GEMM2");
 }
 
+// The expert FFN on block-FP8 weights (moe_expert_ffn_fp8): two launches.
+moe_status_t do_ffn_w8(const moe_desc_t* d, const void* A1, const int32_t* token_of_row, const int32_t* off,
+                       const uint8_t* W1q, const float* S1, const void* b1, const uint8_t* W2q, const float* S2,
+                       const void* b2, void* H, void* y_perm, hipStream_t s) {
+  moe::GemmParams g1, g2;
+  ffn_gemms(d, A1, token_of_row, off, W1q, b1, W2q, b2, H, y_perm, &g1, &g2);
+  const moe::LaunchEvents ev = g_ffn_events;
+  TRY(hip_status(moe::launch_grouped_gemm_w8(g1, moe::GemmW8{S1}, moe::GemmKind::kFfn1Gelu, s, {ev.start, nullptr}),
+                 "expert GEMM1 (fp8 weights)"));
+  return hip_status(moe::launch_grouped_gemm_w8(g2, moe::GemmW8{S2}, moe::GemmKind::kFfn2, s, {nullptr, ev.stop}),
+                    "expert GEMM2 (fp8 weights)");
+}
+
+// layers the block-FP8 FFN serves: bf16, d and h whole 128-wide scale blocks
+moe_status_t check_fp8_layer(const moe_desc_t* d) {
+  if (d->dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 expert weights need a bf16 layer");
+  if (d->d % 128 || d->h % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 expert weights need d and h multiples of 128 (d=%d, h=%d)", d->d, d->h);
+  return MOE_OK;
+}
+
 moe_status_t do_combine(const moe_desc_t* d, const void* y_perm, const int32_t* row_of,
                         const float* w, void* y, hipStream_t s) {
   moe::CombineParams c{};
@@ -393,6 +415,62 @@ moe_status_t check_ws(void* ws, size_t have, size_t want) {
   if (!aligned(ws, kAlign)) return fail(MOE_ERR_INVALID, "workspace is not %zu-byte aligned", kAlign);
   if (have < want) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, want);
   return MOE_OK;
+}
+
+// moe_forward, and with w8 non-null moe_forward_fp8
+moe_status_t forward_impl(const moe_desc_t* desc, const moe_layer_tensors_t* t, const moe_fp8_weights_t* w8,
+                          void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_desc(desc));
+  if (!t) return fail(MOE_ERR_INVALID, "tensors is NULL");
+  TRY(check_gate_inputs(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb,
+                        t->logit_bias));
+  if (w8) {
+    TRY(check_fp8_layer(desc));
+    TRY(need(w8->W1q, "W1q", 16));
+    TRY(need(w8->S1, "S1", 4));
+    TRY(need(w8->W2q, "W2q", 16));
+    TRY(need(w8->S2, "S2", 4));
+  } else {
+    TRY(need(t->W1, "W1", 16));
+    TRY(need(t->W2, "W2", 16));
+  }
+  TRY(maybe(t->b1, "b1", 4));
+  TRY(maybe(t->b2, "b2", 4));
+  TRY(need(t->y, "y", 16));
+  TRY(maybe(t->logits, "logits", 4));
+  TRY(maybe(t->topk_idx, "topk_idx", 4));
+  TRY(maybe(t->topk_w, "topk_w", 4));
+  TRY(maybe(t->expert_count, "expert_count", 4));
+  TRY(maybe(t->expert_off, "expert_off", 4));
+  TRY(maybe(t->row_of, "row_of", 4));
+  TRY(maybe(t->token_of_row, "token_of_row", 4));
+  const ForwardWs fw = forward_ws(desc);
+  TRY(check_ws(ws, ws_bytes, fw.bytes));
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* idx = t->topk_idx ? t->topk_idx : at<int32_t>(ws, fw.topk_idx);
+  float* w = t->topk_w ? t->topk_w : at<float>(ws, fw.topk_w);
+  int32_t* count = t->expert_count ? t->expert_count : at<int32_t>(ws, fw.count);
+  int32_t* off = t->expert_off ? t->expert_off : at<int32_t>(ws, fw.off);
+  int32_t* row_of = t->row_of ? t->row_of : at<int32_t>(ws, fw.row_of);
+  int32_t* tor = t->token_of_row ? t->token_of_row : at<int32_t>(ws, fw.token_of_row);
+  void* H = at<char>(ws, fw.H);
+  void* y_perm = at<char>(ws, fw.y_perm);
+  // the gate also counts each 32 tokens' choices where it can, which
+  // spares the dispatch its counting pass
+  const RouteWs rw = route_ws(desc);
+  int32_t* hist = rw.has_hist ? at<int32_t>(ws, fw.route + rw.hist) : nullptr;
+  TRY(do_route(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb, t->logit_bias,
+               t->logits, idx, w, at<char>(ws, fw.route), s, hist));
+  // routing and row maps only: GEMM1 gathers its rows from x itself
+  // (the dispatch also clears the fused FFN's counters)
+  int32_t* counters = fw.n_counters ? at<int32_t>(ws, fw.ffn_counters) : nullptr;
+  TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s, counters,
+                  fw.n_counters, hist));
+  if (w8)
+    TRY(do_ffn_w8(desc, t->x, tor, off, w8->W1q, w8->S1, t->b1, w8->W2q, w8->S2, t->b2, H, y_perm, s));
+  else
+    TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s));
+  return do_combine(desc, y_perm, row_of, w, t->y, s);
 }
 
 }  // namespace
@@ -482,48 +560,50 @@ moe_status_t moe_combine(const moe_desc_t* desc, const void* y_perm, const int32
   return do_combine(desc, y_perm, row_of, topk_w, y, (hipStream_t)stream);
 }
 
-moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, void* ws,
-                         size_t ws_bytes, void* stream) {
+
+moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return forward_impl(desc, t, nullptr, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_forward_fp8(const moe_desc_t* desc, const moe_layer_tensors_t* t, const moe_fp8_weights_t* w8,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!w8) return fail(MOE_ERR_INVALID, "w8 is NULL");
+  return forward_impl(desc, t, w8, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_quantize_fp8(const void* W, int32_t dtype, int32_t groups, int32_t K, int32_t Ncols,
+                              uint8_t* codes, float* scales, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return fail(MOE_ERR_INVALID, "dtype %d is not MOE_F32 or MOE_BF16", dtype);
+  if (groups < 1 || groups > 65535 || K < 128 || Ncols < 128 || K % 128 || Ncols % 128)
+    return fail(MOE_ERR_INVALID, "quantise [%d, %d, %d]: groups in [1, 65535], K and Ncols positive multiples of 128",
+                groups, K, Ncols);
+  if ((int64_t)K * Ncols > ((int64_t)1 << 31) - 1)
+    return fail(MOE_ERR_INVALID, "K * Ncols = %lld exceeds 2^31 - 1", (long long)K * Ncols);
+  TRY(need(W, "W", 16));
+  TRY(need(codes, "codes", 16));
+  TRY(need(scales, "scales", 4));
+  return hip_status(moe::launch_quantize_fp8(W, dtype == MOE_BF16, groups, K, Ncols, codes, scales,
+                                             (hipStream_t)stream),
+                    "fp8 quantisation");
+}
+
+moe_status_t moe_expert_ffn_fp8(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
+                                const uint8_t* W1q, const float* S1, const void* b1, const uint8_t* W2q,
+                                const float* S2, const void* b2, void* H, void* y_perm, void* stream) {
   TRY(check_desc(desc));
-  if (!t) return fail(MOE_ERR_INVALID, "tensors is NULL");
-  TRY(check_gate_inputs(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb,
-                        t->logit_bias));
-  TRY(need(t->W1, "W1", 16));
-  TRY(need(t->W2, "W2", 16));
-  TRY(maybe(t->b1, "b1", 4));
-  TRY(maybe(t->b2, "b2", 4));
-  TRY(need(t->y, "y", 16));
-  TRY(maybe(t->logits, "logits", 4));
-  TRY(maybe(t->topk_idx, "topk_idx", 4));
-  TRY(maybe(t->topk_w, "topk_w", 4));
-  TRY(maybe(t->expert_count, "expert_count", 4));
-  TRY(maybe(t->expert_off, "expert_off", 4));
-  TRY(maybe(t->row_of, "row_of", 4));
-  TRY(maybe(t->token_of_row, "token_of_row", 4));
-  const ForwardWs fw = forward_ws(desc);
-  TRY(check_ws(ws, ws_bytes, fw.bytes));
-  hipStream_t s = (hipStream_t)stream;
-  int32_t* idx = t->topk_idx ? t->topk_idx : at<int32_t>(ws, fw.topk_idx);
-  float* w = t->topk_w ? t->topk_w : at<float>(ws, fw.topk_w);
-  int32_t* count = t->expert_count ? t->expert_count : at<int32_t>(ws, fw.count);
-  int32_t* off = t->expert_off ? t->expert_off : at<int32_t>(ws, fw.off);
-  int32_t* row_of = t->row_of ? t->row_of : at<int32_t>(ws, fw.row_of);
-  int32_t* tor = t->token_of_row ? t->token_of_row : at<int32_t>(ws, fw.token_of_row);
-  void* H = at<char>(ws, fw.H);
-  void* y_perm = at<char>(ws, fw.y_perm);
-  // the gate also counts each 32 tokens' choices where it can, which
-  // spares the dispatch its counting pass
-  const RouteWs rw = route_ws(desc);
-  int32_t* hist = rw.has_hist ? at<int32_t>(ws, fw.route + rw.hist) : nullptr;
-  TRY(do_route(desc, t->x, t->w_gate, t->w_noise, t->noise, t->proj, t->expert_emb, t->logit_bias,
-               t->logits, idx, w, at<char>(ws, fw.route), s, hist));
-  // routing and row maps only: GEMM1 gathers its rows from x itself
-  // (the dispatch also clears the fused FFN's counters)
-  int32_t* counters = fw.n_counters ? at<int32_t>(ws, fw.ffn_counters) : nullptr;
-  TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s, counters,
-                  fw.n_counters, hist));
-  TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s));
-  return do_combine(desc, y_perm, row_of, w, t->y, s);
+  TRY(check_fp8_layer(desc));
+  TRY(need(x_perm, "x_perm", 16));
+  TRY(need(expert_off, "expert_off", 4));
+  TRY(need(W1q, "W1q", 16));
+  TRY(need(S1, "S1", 4));
+  TRY(need(W2q, "W2q", 16));
+  TRY(need(S2, "S2", 4));
+  TRY(maybe(b1, "b1", 4));
+  TRY(maybe(b2, "b2", 4));
+  TRY(need(H, "H", 16));
+  TRY(need(y_perm, "y_perm", 16));
+  return do_ffn_w8(desc, x_perm, nullptr, expert_off, W1q, S1, b1, W2q, S2, b2, H, y_perm, (hipStream_t)stream);
 }
 
 moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_idx, const float* topk_w,

@@ -128,10 +128,13 @@ __device__ inline void wait_vmcnt_lds() {
 constexpr int kNumXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 constexpr int kGroupN = 4;   // n-tiles per run of the tile order
 
-template <typename E, typename O, int BM_, int BN_, int WM_, int WN_, int KC_, int S_, bool GELU_>
+// W8_: the weights are block-FP8 codes in K-groups of 8 (GemmW8) instead of
+// E values; the activations stay E.
+template <typename E, typename O, int BM_, int BN_, int WM_, int WN_, int KC_, int S_, bool GELU_, bool W8_ = false>
 struct Cfg {
   using Elem = E;
   using Out = O;
+  static constexpr bool W8 = W8_;
   static constexpr int ES = sizeof(E);
   static constexpr int CE = ElemTraits<E>::kPerChunk;   // elements per 16-byte chunk
   static constexpr int KC = KC_;                         // 16-byte chunks of K per activation row per stage
@@ -149,11 +152,13 @@ struct Cfg {
   // 128-byte rows, while the weight tile keeps its ring of S stages.
   static constexpr int AP = (KC == 4 && S == 4) ? 2 : 1;  // K-steps per activation stage
   static constexpr int KCA = KC * AP;                    // 16-byte chunks per activation row per stage
-  static constexpr int B_CPR = BN * ES / 16;             // 16-byte chunks per weight row
+  // weight tile rows: K rows of BN values, or (W8) K-groups of BN x 8 codes
+  static constexpr int B_ROWS = W8 ? BK / 8 : BK;
+  static constexpr int B_CPR = W8 ? BN * 8 / 16 : BN * ES / 16;  // 16-byte chunks per weight tile row
   static constexpr int A_STAGE = BM * KCA * 16;          // activation tile, K-contiguous rows
-  static constexpr int B_STAGE = BK * B_CPR * 16;        // weight tile, N-contiguous rows
+  static constexpr int B_STAGE = B_ROWS * B_CPR * 16;    // weight tile
   static constexpr int A_INST = BM * KCA / THREADS;      // 16-byte loads per thread per activation stage
-  static constexpr int B_INST = BK * B_CPR / THREADS;    // ... per weight stage
+  static constexpr int B_INST = B_ROWS * B_CPR / THREADS;  // ... per weight stage
   static constexpr int LOADS = A_INST + B_INST;
   static constexpr int LDS_BYTES = AP == 1 ? S * (A_STAGE + B_STAGE) : 2 * A_STAGE + S * B_STAGE;
   // Ragged tails: the rows of a group past its last full BM-row tile go to
@@ -164,7 +169,9 @@ struct Cfg {
   static constexpr int A_INST_T = HAS_TAIL ? TBM * KCA / THREADS : A_INST;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(KC == 4 || KC == 8, "activation rows of 4 or 8 chunks");
-  static_assert(BM * KCA % THREADS == 0 && BK * B_CPR % THREADS == 0, "loads must divide evenly");
+  static_assert(BM * KCA % THREADS == 0 && B_ROWS * B_CPR % THREADS == 0, "loads must divide evenly");
+  static_assert(!W8 || (std::is_same_v<E, bf16> && AP == 1 && !HAS_TAIL && (128 / BK) * BK == 128 && WTN <= 128),
+                "block-FP8 weights: bf16 activations, whole K-steps per 128-deep scale block, a wave's columns in one block");
   static_assert(B_CPR >= (ES == 2 ? 16 : 8) && WTN % 64 == 0, "weight rows of at least 256 (bf16) or 128 (fp32) bytes, wave tiles of 64 columns");
   static_assert(S >= 2 && S <= 4 && LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS * (S - 2) < 64 && A_INST + 2 * B_INST < 64, "vmcnt range");
@@ -228,11 +235,12 @@ template <> struct Pack<float> {
 // n0; TBM rows if tail_tile): the K loop and the epilogue, GELU'd if gelu.
 // All threads of the block call it with the same arguments; the LDS
 // objects are the block's (MOE_GEMM_LDS). at_k_end() runs between the K
-// loop and the epilogue.
+// loop and the epilogue. bscale: the block scales of W8 weights (GemmW8),
+// else unused.
 template <class C, class AtKEnd>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* st0, char* st1, char* st2,
                                           char* st3, char* sa0, char* sa1, int g, int row_lo, int row_hi,
-                                          int n0, bool tail_tile, AtKEnd&& at_k_end) {
+                                          int n0, bool tail_tile, const float* bscale, AtKEnd&& at_k_end) {
   using E = typename C::Elem;
   using O = typename C::Out;
   constexpr int CE = C::CE, KC = C::KC, BK = C::BK, BM = C::BM, BN = C::BN, ES = C::ES, S = C::S;
@@ -248,10 +256,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
   const int rows = row_hi - row_lo;
   // A rows of the tile: contiguous from row_lo, or gathered (then the
   // descriptor spans all of A and each lane's offsets name its rows)
+  // weight bytes per element, and per column of a weight tile row (W8:
+  // the 8 codes of a K-group; moving k0 rows down moves k0 * Ncols bytes
+  // in both layouts, k0 a multiple of 8)
+  constexpr int WES = C::W8 ? 1 : ES, WCB = C::W8 ? 8 : ES;
   const char* At = static_cast<const char*>(p.A) + (p.gather ? 0 : (int64_t)row_lo * p.lda * ES);
-  const char* Bt = static_cast<const char*>(p.B) + ((int64_t)g * p.strideB + n0) * ES;
+  const char* Bt = static_cast<const char*>(p.B) + (int64_t)g * p.strideB * WES + (int64_t)n0 * WCB;
   const int64_t a_bytes = (int64_t)(p.gather ? p.a_rows : rows) * lda * ES;
-  const int64_t b_bytes = (int64_t)K * Ncols * ES - (int64_t)n0 * ES;
+  const int64_t b_bytes = (int64_t)K * Ncols * WES - (int64_t)n0 * WCB;
 
   // ---- asynchronous global -> LDS loads. Each 16-byte load of a wave lands
   // at (wave's slot base + lane) * 16 in the stage; the lane fetches whichever
@@ -278,12 +290,18 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 #pragma unroll
   for (int i = 0; i < C::B_INST; ++i) {
     const int slot = i * C::THREADS + tid;
-    const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_b<ES>(k);
-    b_off[i] = (k * Ncols + c * CE) * ES;
+    if constexpr (C::W8) {
+      // K-group rows of BN x 8 codes, stored as in memory (the fragment
+      // reads of one pass cover 256 contiguous bytes: no swizzle needed)
+      b_off[i] = (slot / C::B_CPR) * Ncols * 8 + (slot % C::B_CPR) * 16;
+    } else {
+      const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_b<ES>(k);
+      b_off[i] = (k * Ncols + c * CE) * ES;
+    }
   }
   auto issue_b = [&](char* sb, int k0) {
-    const int64_t bb = b_bytes - (int64_t)k0 * Ncols * ES;
-    const __amdgpu_buffer_rsrc_t br = make_rsrc(Bt + (int64_t)k0 * Ncols * ES, (uint32_t)(bb > 0 ? bb : 0));
+    const int64_t bb = b_bytes - (int64_t)k0 * Ncols * WES;
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(Bt + (int64_t)k0 * Ncols * WES, (uint32_t)(bb > 0 ? bb : 0));
 #pragma unroll
     for (int i = 0; i < C::B_INST; ++i)
       lds_load16(br, (lds_void*)(sb + (i * C::THREADS + wave * kWave) * 16), b_off[i]);
@@ -323,6 +341,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       for (int j = 0; j < FM; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    // W8: acc holds the current 128-deep block of K; acc8 the scaled total
+    f32x16 acc8[C::W8 ? C::FN : 1][C::W8 ? FM : 1];
+    if constexpr (C::W8) {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc8[i][j][r] = 0.f;
+    }
 
     // ---- per-lane fragment offsets within a stage
     const int lrow = lane & 31, lhalf = lane >> 5;
@@ -354,7 +382,20 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 #pragma unroll
       for (int j = 0; j < FM; ++j)
         fb[buf][j] = *(lds_u32x4*)(sa + (fa_off[ss] ^ hi) + j * 32 * KCA * 16);
-      if constexpr (ES == 2) {
+      if constexpr (C::W8) {
+        // the lane's 8 codes: K-group 2ss + lane/32 of column lane%32 of
+        // fragment i, converted exactly to bf16 (E4M3 values fit bf16)
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+          const u32x2 raw =
+              *(const __attribute__((address_space(3))) u32x2*)(sb + ((2 * ss + lhalf) * C::BN + wn * C::WTN +
+                                                                      32 * i + lrow) * 8);
+          fa[buf][i] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[0], 1.f, false)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[0], 1.f, true)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[1], 1.f, false)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[1], 1.f, true))};
+        }
+      } else if constexpr (ES == 2) {
 #pragma unroll
         for (int i = 0; i < C::FN; ++i) {
           const char* w = sb + fw[i];
@@ -420,6 +461,26 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       else if constexpr (cur % 2 == 0) issue_a(a_stage(std::integral_constant<int, (cur + 2) % 4>{}), (kt + 2) * BK);
       issue_b(b_stage(std::integral_constant<int, nxt>{}), kn);
       compute(a_stage(st), b_stage(st), (AP == 2 && (cur & 1)) ? 64 : 0);
+      if constexpr (C::W8) {
+        constexpr int SPB = 128 / BK;  // K-steps per scale block
+        static_assert(S % SPB == 0, "scale blocks end on fixed stages");
+        if constexpr ((cur + 1) % SPB == 0) {
+          // the end of a 128-deep block of K: its sums, scaled once, join
+          // the total (one scale per wave: its columns lie in one block)
+          const int wn_u = __builtin_amdgcn_readfirstlane(wn);
+          const float sc =
+              bscale[((int64_t)g * (K / 128) + kt / SPB) * (Ncols / 128) + (n0 + wn_u * C::WTN) / 128];
+#pragma unroll
+          for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                acc8[i][j][r] = fmaf(sc, acc[i][j][r], acc8[i][j][r]);
+                acc[i][j][r] = 0.f;
+              }
+        }
+      }
       if constexpr (ES == 2 && C::THREADS == 512) {
         // (8-wave tiles) instruction order for the step: the first substep's LDS reads, then
         // each MFMA followed by one of the next substep's LDS reads and, after
@@ -452,6 +513,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     if (kt < nk) step(std::integral_constant<int, 0>{}, kt);
     if constexpr (S > 2) if (kt + 1 < nk) step(std::integral_constant<int, 1>{}, kt + 1);
     if constexpr (S > 3) if (kt + 2 < nk) step(std::integral_constant<int, 2 % S>{}, kt + 2);
+    if constexpr (C::W8) {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = acc8[i][j];
+    }
     wait_vmcnt<0>();
     at_k_end();
 
@@ -552,7 +619,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 }
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p, const float* bscale) {
   using E = typename C::Elem;
   using O = typename C::Out;
   constexpr int BM = C::BM, BN = C::BN;
@@ -652,7 +719,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p) 
   const int row_hi = __builtin_amdgcn_readfirstlane(sched[2]);
   const int n0 = __builtin_amdgcn_readfirstlane(sched[3]);
   const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[4]) != 0;
-  gemm_tile<C>(p, C::GELU, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0, tail_tile, [] {});
+  gemm_tile<C>(p, C::GELU, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0, tail_tile, bscale, [] {});
 }
 
 // ---- the expert FFN (GEMM1 + GELU, then GEMM2) as one persistent launch.
@@ -822,7 +889,7 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
     const __attribute__((address_space(4))) GemmParams* pp = kind == 1 ? &fp->g1 : &fp->g2;
     int next = 0;
     gemm_tile<C>(*(const GemmParams*)pp, kind == 1, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0,
-                 tail_tile, [&] {
+                 tail_tile, nullptr, [&] {
                    if (tid == 0)
                      next = __hip_atomic_fetch_add(fp->counters + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                  });
@@ -836,7 +903,7 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
 }
 
 template <class C>
-hipError_t launch_cfg(const GemmParams& p, hipStream_t s, LaunchEvents ev) {
+hipError_t launch_cfg(const GemmParams& p, hipStream_t s, LaunchEvents ev, const float* bscale = nullptr) {
   // upper bounds on the row tiles of each phase: per group, the full-height
   // tiles plus at most one partial one, and at most BM/(2 TBM) tail tiles;
   // each phase's blocks are a multiple of the XCD count
@@ -849,9 +916,9 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s, LaunchEvents ev) {
   const int64_t blocks = xcd_round(full_max * ntiles) + xcd_round(tail_max * ntiles);
   if (ev.start || ev.stop)
     hipExtLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, ev.start,
-                          ev.stop, 0, p);
+                          ev.stop, 0, p, bscale);
   else
-    hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p);
+    hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p, bscale);
   return hipGetLastError();
 }
 
@@ -918,6 +985,14 @@ hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t*
   else
     hipLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, f);
   return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, hipStream_t s, LaunchEvents ev) {
+  // the decode tile (32 rows, 4 waves of 64 columns, 64-deep K-steps, 4
+  // stages): the layer's bytes are the weights, streamed once per 32 rows
+  if (kind == GemmKind::kFfn1Gelu)
+    return launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, true, true>>(p, s, ev, w8.bscale);
+  return launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, false, true>>(p, s, ev, w8.bscale);
 }
 
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16_, int avg_rows,

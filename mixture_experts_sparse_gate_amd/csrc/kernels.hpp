@@ -85,11 +85,26 @@ struct GemmParams {
   int groups, K, Ncols;
 };
 enum class GemmKind { kFfn1Gelu, kFfn2, kProjF32 };
+// Block-FP8 weights (launch_grouped_gemm_w8): B holds E4M3 codes in K-groups
+// of 8 (the byte of B[k][n] at (k/8 * Ncols + n) * 8 + k % 8, strideB bytes
+// per group) and bscale one fp32 scale per 128 x 128 block,
+// [groups, K/128, Ncols/128]; K a multiple of 128.
+struct GemmW8 {
+  const float* bscale;
+};
 // Events a launch records when its kernel starts and when it ends executing
 // (hipExtLaunchKernel), each or both null for none.
 struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
+// bf16 activations times block-FP8 weights (GELU for kFfn1Gelu), in 32-row
+// tiles that stream the weights; K and Ncols multiples of 128.
+hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, hipStream_t s,
+                                  LaunchEvents ev = {});
+// E4M3 block quantisation (quant.hip): W [groups, K, Ncols] fp32 or bf16,
+// K and Ncols multiples of 128
+hipError_t launch_quantize_fp8(const void* W, bool bf16, int groups, int K, int Ncols, uint8_t* codes,
+                               float* scales, hipStream_t s);
 // avg_rows / max_rows: expected and largest rows per group (tile choice only)
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, int avg_rows,
                                int max_rows, hipStream_t s, LaunchEvents ev = {});

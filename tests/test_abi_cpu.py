@@ -32,7 +32,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_five_stage_entry_points():
@@ -184,6 +184,45 @@ def test_stage_argument_checks(lib):
     assert lib.moe_aux_loss(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_aux_loss(ctypes.byref(d), FAKE, FAKE, FAKE + 2, None, FAKE, 1 << 20, None) == _lib.MOE_ERR_INVALID
     assert lib.moe_aux_loss(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == _lib.MOE_ERR_WORKSPACE
+
+
+@no_gpu
+def test_fp8_argument_checks(lib):
+    q = lib.moe_quantize_fp8
+    for G, K, N in ((0, 256, 256), (1, 200, 256), (1, 256, 100), (1, 0, 128), (70000, 128, 128)):
+        assert q(FAKE, _lib.MOE_BF16, G, K, N, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID, (G, K, N)
+    assert q(FAKE, 7, 1, 128, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID          # dtype
+    assert q(FAKE + 8, _lib.MOE_BF16, 1, 128, 128, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID  # W misaligned
+    assert q(FAKE, _lib.MOE_BF16, 1, 128, 128, None, FAKE, None) == _lib.MOE_ERR_INVALID
+    assert q(FAKE, _lib.MOE_BF16, 1, 128, 128, FAKE, FAKE + 2, None) == _lib.MOE_ERR_INVALID
+    assert q(FAKE, _lib.MOE_BF16, 1, 1 << 16, 1 << 15, FAKE, FAKE, None) == _lib.MOE_ERR_INVALID  # K*Ncols >= 2^31
+    dec = desc_from_spec(workloads.get("decode_top8_bf16"))
+    ffn = lib.moe_expert_ffn_fp8
+    args = [FAKE] * 10
+    for i in (0, 1, 2, 3, 5, 6, 8, 9):  # x_perm, expert_off, W1q, S1, W2q, S2, H, y_perm required
+        a = list(args)
+        a[i] = None
+        assert ffn(ctypes.byref(dec), *a, None) == _lib.MOE_ERR_INVALID, i
+    # fp32 layers, and d or h not a multiple of 128, are not served
+    for spec in (workloads.get("tiny_top1_f32"), workloads.get("decode_top8_bf16").with_(h=2000)):
+        d = desc_from_spec(spec)
+        assert ffn(ctypes.byref(d), *args, None) == _lib.MOE_ERR_UNSUPPORTED
+        t = _lib.MoeLayerTensors(x=FAKE, w_gate=FAKE, y=FAKE)
+        w8 = _lib.MoeFp8Weights(W1q=FAKE, S1=FAKE, W2q=FAKE, S2=FAKE)
+        assert lib.moe_forward_fp8(ctypes.byref(d), ctypes.byref(t), ctypes.byref(w8), FAKE, 1 << 40, None) \
+            == _lib.MOE_ERR_UNSUPPORTED
+    # moe_forward_fp8 reads the weights from w8 (W1/W2 may be NULL), and needs all four
+    t = _lib.MoeLayerTensors(x=FAKE, w_gate=FAKE, y=FAKE)
+    need = ctypes.c_size_t()
+    lib.moe_workspace_size(ctypes.byref(dec), _lib.MOE_WS_FORWARD, ctypes.byref(need))
+    assert lib.moe_forward_fp8(ctypes.byref(dec), ctypes.byref(t), None, FAKE, need.value, None) == _lib.MOE_ERR_INVALID
+    w8 = _lib.MoeFp8Weights(W1q=FAKE, S1=FAKE, W2q=None, S2=FAKE)
+    assert lib.moe_forward_fp8(ctypes.byref(dec), ctypes.byref(t), ctypes.byref(w8), FAKE, need.value, None) \
+        == _lib.MOE_ERR_INVALID
+    assert b"W2q" in lib.moe_last_error()
+    w8.W2q = FAKE
+    assert lib.moe_forward_fp8(ctypes.byref(dec), ctypes.byref(t), ctypes.byref(w8), FAKE, need.value - 256, None) \
+        == _lib.MOE_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("kw", [dict(T=1 << 20, d=1024, h=8192), dict(T=64, d=65536, h=32768),
