@@ -97,6 +97,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="noisy_top2_bf16")
+    ap.add_argument("--weights", choices=["layer", "fp8"], default="layer",
+                    help="expert weights in the layer's dtype, or block-FP8 (moe_forward_fp8; bf16 layers)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--skip-extras", action="store_true",
@@ -131,6 +133,12 @@ def main() -> int:
     t_gen = time.perf_counter()
     inp = make_inputs(spec, seed)
     dev = api.DeviceLayer(inp)
+    fp8 = args.weights == "fp8"
+    if fp8:
+        if spec.dtype != "bf16":
+            print("--weights fp8 needs a bf16 workload", file=sys.stderr)
+            return 2
+        dev.quantize_weights_fp8()  # model preparation, outside every timed region
     torch.cuda.synchronize()
     log(f"[bench] {spec.name}: inputs ready in {time.perf_counter() - t_gen:.1f}s")
 
@@ -145,7 +153,10 @@ def main() -> int:
         del src, dst
 
     def forward():
-        dev.run_forward(inspect=False)
+        if fp8:
+            dev.run_forward_fp8(inspect=False)
+        else:
+            dev.run_forward(inspect=False)
 
     def step(ev=None):
         if ev:
@@ -158,8 +169,12 @@ def main() -> int:
                      dev.token_of_row, dev.x_perm, ws=dev.ws)
         if ev:
             ev[2].record(stream)
-        api.expert_ffn(dev.desc, dev.x_perm, dev.expert_off, dev.W1, dev.b1, dev.W2, dev.b2, dev.H,
-                       dev.y_perm, ws=dev.ws)
+        if fp8:
+            api.expert_ffn_fp8(dev.desc, dev.x_perm, dev.expert_off, dev.w8["W1q"], dev.w8["S1"], dev.b1,
+                               dev.w8["W2q"], dev.w8["S2"], dev.b2, dev.H, dev.y_perm)
+        else:
+            api.expert_ffn(dev.desc, dev.x_perm, dev.expert_off, dev.W1, dev.b1, dev.W2, dev.b2, dev.H,
+                           dev.y_perm, ws=dev.ws)
         if ev:
             ev[3].record(stream)
         api.combine(dev.desc, dev.y_perm, dev.row_of, dev.topk_w, dev.y)
@@ -265,7 +280,10 @@ def main() -> int:
     s = 2 if spec.dtype == "bf16" else 4
     T, d, h, N, k = spec.T, spec.d, spec.h, spec.N, spec.k
     ffn_flops = 4.0 * A * d * h
-    touched_weight_bytes = float(U) * 2 * d * h * s
+    if fp8:  # one byte per weight plus one fp32 scale per 128 x 128 block, both matrices
+        touched_weight_bytes = float(U) * 2 * (d * h + (d // 128) * (h // 128) * 4)
+    else:
+        touched_weight_bytes = float(U) * 2 * d * h * s
     ffn_s = ffn_kernel_ms * 1e-3
     avg_rows = (T * k) / N
     if avg_rows < 64:  # weight streaming: bound by HBM
@@ -275,7 +293,11 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": ffn_flops / ffn_s / 1e12, "peak": MFMA_PEAK_TFLOPS[spec.dtype],
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    if api.workspace_size(dev.desc, _lib.MOE_WS_FFN) > 0:
+    if fp8:
+        roof["kernel"] = ("grouped_gemm_kernel with block-FP8 weights (32-row tiles streaming E4M3 codes), "
+                          "launched twice per step (GEMM1+GELU, GEMM2); duration from the HIP events the "
+                          "launches record (GEMM1's start to GEMM2's end), mean over moe_forward_fp8 steps")
+    elif api.workspace_size(dev.desc, _lib.MOE_WS_FFN) > 0:
         roof["kernel"] = ("fused_ffn_kernel: GEMM1+GELU and GEMM2 in one persistent launch; duration from the "
                           "HIP events its launch records at the start and end of execution, mean over "
                           "moe_forward steps")
@@ -285,7 +307,7 @@ def main() -> int:
                           "moe_forward steps")
     roof["kernel_ms"] = ffn_kernel_ms
     roof["algorithmic"] = {"flops": ffn_flops, "touched_weight_bytes": touched_weight_bytes}
-    traffic, tsrc = read_traffic(spec.name)
+    traffic, tsrc = read_traffic(spec.name + ("_fp8w" if fp8 else ""))
     roof["traffic"] = traffic
     roof["traffic_source"] = tsrc
 
@@ -317,6 +339,9 @@ def main() -> int:
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(spec, inp, args.cpu_seconds)
+        if fp8:
+            cpu["sample"] += ("; the oracle's FFN on the layer's own weights, whose cost does not depend on "
+                              "the weights' storage format")
 
     out = {
         "metric": "MoE layer fwd tokens/s; expert GEMM % bf16 MFMA peak; dispatch/combine GB/s",
@@ -333,7 +358,8 @@ def main() -> int:
         "data": "synthetic (seeded normal inputs and random-init expert weights)",
         "config": {"workload": spec.name, "T": T, "d": d, "h": h, "N": N, "k": k, "gate": spec.gate,
                    "capacity_factor": spec.capacity_factor, "renorm": spec.renorm,
-                   "capacity": int(dev.C), "kept_rows": A, "experts_touched": U},
+                   "capacity": int(dev.C), "kept_rows": A, "experts_touched": U,
+                   "weights": "fp8_e4m3_block128" if fp8 else spec.dtype},
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages": stages,
