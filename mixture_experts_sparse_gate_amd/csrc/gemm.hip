@@ -466,10 +466,12 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         static_assert(S % SPB == 0, "scale blocks end on fixed stages");
         if constexpr ((cur + 1) % SPB == 0) {
           // the end of a 128-deep block of K: its sums, scaled once, join
-          // the total (one scale per wave: its columns lie in one block)
+          // the total (one scale per wave: its columns lie in one block; a
+          // wave wholly past Ncols, whose outputs are never stored, takes
+          // the last block's, so that the read stays in the array)
           const int wn_u = __builtin_amdgcn_readfirstlane(wn);
-          const float sc =
-              bscale[((int64_t)g * (K / 128) + kt / SPB) * (Ncols / 128) + (n0 + wn_u * C::WTN) / 128];
+          const int cb = min((n0 + wn_u * C::WTN) / 128, Ncols / 128 - 1);
+          const float sc = bscale[((int64_t)g * (K / 128) + kt / SPB) * (Ncols / 128) + cb];
 #pragma unroll
           for (int i = 0; i < C::FN; ++i)
 #pragma unroll
