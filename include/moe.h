@@ -217,8 +217,9 @@ MOE_API moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors
  *   scales [groups, K/128, Ncols/128] fp32: s = amax / 448, amax the
  *   largest |w| of the block (one fp32 division);
  *   codes: the OCP E4M3 byte (bias 7, 3 mantissa bits, largest 448) of the
- *   fp32 quotient w / s rounded to nearest, ties to even, with w's sign; an
- *   all-zero block has s = 0 and zero codes.
+ *   fp32 quotient w / s rounded to nearest, ties to even, with w's sign
+ *   (saturated at 448, which only a block whose scale is an fp32 subnormal
+ *   can reach); an all-zero block has s = 0 and zero codes.
  * codes layout: K-groups of 8, the byte of w[g][k][n] at
  *   ((g * K/8 + k/8) * Ncols + n) * 8 + k % 8,
  * so that each column's 8 consecutive K values are contiguous.

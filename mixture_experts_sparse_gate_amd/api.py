@@ -251,6 +251,8 @@ class DeviceLayer:
         return self.w8
 
     def run_forward_fp8(self, inspect: bool = True, stream=None):
+        if getattr(self, "w8", None) is None:
+            raise RuntimeError("no fp8 weights: call quantize_weights_fp8() first")
         t = self.layer_tensors(inspect)
         t.update(W1=None, W2=None)
         forward_fp8(self.desc, t, self.w8, self.ws, stream=stream)

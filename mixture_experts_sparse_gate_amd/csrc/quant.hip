@@ -19,7 +19,9 @@ namespace {
 constexpr int kQBlock = 128;
 constexpr int kQThreads = 256;
 
-// E4M3 code of q (|q| <= 464, which rounds to at most 448): below 2^-6 the
+// E4M3 code of q, saturated at 448 (|q| can exceed 448 only when the scale
+// itself is an inexact fp32 subnormal; up to 464 it rounds to 448 anyway):
+// below 2^-6 the
 // codes are the multiples of 2^-9, so the code is q * 512 rounded to the
 // nearest integer, ties to even (8 is 2^-6, the first normal code, so the
 // two ranges meet); above, the fp32 mantissa is rounded to 3 bits, ties to
@@ -27,7 +29,7 @@ constexpr int kQThreads = 256;
 // moves to the next exponent, as it should).
 __device__ inline uint32_t e4m3_code(float q) {
   const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  const float a = fabsf(q);
+  const float a = fminf(fabsf(q), 448.f);
   uint32_t mag;
   if (a < 0.015625f) {
     mag = (uint32_t)rintf(a * 512.f);

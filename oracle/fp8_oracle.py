@@ -21,7 +21,9 @@ section). They fix neither the FP8 encoding nor the block shape. Readings
             of the block (w widened exactly to fp32); an all-zero block has
             s = 0 and zero codes
   codes     q = E4M3(w / s): the fp32 quotient rounded to the nearest E4M3
-            value, ties to the even code; the sign bit is w's
+            value, ties to the even code; the sign bit is w's. A quotient
+            above 448 in magnitude (possible only when s is an inexact fp32
+            subnormal) saturates to 448
   dequant   w' = decode(q) * s, exact in float64
 
 Both decisions (each scale and each code) are taken in fp32, the precision
@@ -89,6 +91,7 @@ def quantize_blocks(W: np.ndarray, block: int = BLOCK):
     s = scales[:, :, None, :, None]
     with np.errstate(invalid="ignore", divide="ignore"):
         q = np.where(s > 0, blocks / s, np.float32(0)).astype(np.float32)  # fp32 division
+    q = np.clip(q, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
     codes = e4m3_encode(q).reshape(G, K, N)
     # an all-zero block: zero codes (w / s would be 0 / 0)
     codes = np.where(np.repeat(np.repeat(scales == 0, block, 1), block, 2), np.uint8(0), codes)

@@ -90,6 +90,19 @@ def test_block_quantiser_properties():
     assert np.array_equal(c1[0], codes[0, 128:256, 256:384]) and s1[0, 0, 0] == scales[0, 1, 2]
 
 
+def test_quantiser_saturates_with_a_subnormal_scale():
+    """amax / 448 below fp32's normal range rounds coarsely: w / s may pass 448 and saturates there."""
+    W = np.zeros((1, 128, 128), np.float32)
+    # multiples of the smallest fp32 subnormal, up to 667: s = 667/448 * 2^-149 rounds to 2^-149
+    W[0, 0, :] = (np.linspace(1, 667, 128).round() * 2.0 ** -149).astype(np.float32)
+    codes, scales = F.quantize_blocks(W)
+    s = scales[0, 0, 0]
+    assert 0 < s < np.finfo(np.float32).tiny
+    q = (W[0, 0] / s).astype(np.float32)
+    assert np.abs(q).max() > 464  # the plain quotient leaves the E4M3 range
+    assert (codes[0, 0] & 0x7F).max() == 0x7E and not np.isin(codes, [0x7F, 0xFF]).any()
+
+
 def test_quantiser_brute_force_tiny():
     """Each code is the nearest finite E4M3 value to w / s (brute force over all codes)."""
     rng = np.random.default_rng(9)

@@ -51,7 +51,9 @@ def test_quantize_edge_values():
     blk[6, :] = -np.float32(2.0 ** -12)
     blk[7, 3] = -0.0
     W[1, 128:256, 128:256] = 0.0  # an all-zero block
-    for dtype in (torch.float32, torch.bfloat16):
+    W[1, 0:128, 256:384] = 0.0  # a block of fp32 subnormals: a subnormal scale, saturated codes
+    W[1, 0, 256:384] = (np.linspace(1, 667, 128).round() * 2.0 ** -149).astype(np.float32)
+    for dtype in (torch.float32, torch.bfloat16):  # (in bf16 those subnormals are zeros: a zero block)
         Wd = torch.from_numpy(W).cuda().to(dtype).contiguous()
         Wh = Wd.float().cpu().numpy()
         say(f"[case] quantise edge values {dtype}")
