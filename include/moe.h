@@ -234,9 +234,10 @@ MOE_API moe_status_t moe_quantize_fp8(const void* W, int32_t dtype, int32_t grou
  * dequantised weights (decoded code times its block's scale):
  *   H[r] = GELU(x_perm[r] W1'[e] + b1[e]), y_perm[r] = H[r] W2'[e] + b2[e],
  * each product accumulated in fp32 over each 128-deep block of K, scaled
- * once and added to the sum in K order; rounded once to bf16. The kernel
- * streams the weights with 32-row tiles whatever the row count (the shape
- * of decoding, where the weight bytes bound the layer). */
+ * once and added to the sum in K order; rounded once to bf16. Below 64
+ * rows per expert (decoding, where the weight bytes bound the layer) the
+ * kernel streams the weights with 32-row tiles; above, it takes 128 x 128
+ * tiles. */
 MOE_API moe_status_t moe_expert_ffn_fp8(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
                                         const uint8_t* W1q, const float* S1, const void* b1, const uint8_t* W2q,
                                         const float* S2, const void* b2, void* H, void* y_perm, void* stream);

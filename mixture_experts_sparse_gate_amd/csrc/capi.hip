@@ -363,9 +363,12 @@ moe_status_t do_ffn_w8(const moe_desc_t* d, const void* A1, const int32_t* token
   moe::GemmParams g1, g2;
   ffn_gemms(d, A1, token_of_row, off, W1q, b1, W2q, b2, H, y_perm, &g1, &g2);
   const moe::LaunchEvents ev = g_ffn_events;
-  TRY(hip_status(moe::launch_grouped_gemm_w8(g1, moe::GemmW8{S1}, moe::GemmKind::kFfn1Gelu, s, {ev.start, nullptr}),
+  const int avg_rows = (int)((d->T * d->k) / d->N);
+  TRY(hip_status(moe::launch_grouped_gemm_w8(g1, moe::GemmW8{S1}, moe::GemmKind::kFfn1Gelu, avg_rows, s,
+                                             {ev.start, nullptr}),
                  "expert GEMM1 (fp8 weights)"));
-  return hip_status(moe::launch_grouped_gemm_w8(g2, moe::GemmW8{S2}, moe::GemmKind::kFfn2, s, {nullptr, ev.stop}),
+  return hip_status(moe::launch_grouped_gemm_w8(g2, moe::GemmW8{S2}, moe::GemmKind::kFfn2, avg_rows, s,
+                                                {nullptr, ev.stop}),
                     "expert GEMM2 (fp8 weights)");
 }
 

@@ -170,7 +170,7 @@ struct Cfg {
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(KC == 4 || KC == 8, "activation rows of 4 or 8 chunks");
   static_assert(BM * KCA % THREADS == 0 && B_ROWS * B_CPR % THREADS == 0, "loads must divide evenly");
-  static_assert(!W8 || (std::is_same_v<E, bf16> && AP == 1 && !HAS_TAIL && (128 / BK) * BK == 128 && WTN <= 128),
+  static_assert(!W8 || (std::is_same_v<E, bf16> && (128 / BK) * BK == 128 && WTN <= 128),
                 "block-FP8 weights: bf16 activations, whole K-steps per 128-deep scale block, a wave's columns in one block");
   static_assert(B_CPR >= (ES == 2 ? 16 : 8) && WTN % 64 == 0, "weight rows of at least 256 (bf16) or 128 (fp32) bytes, wave tiles of 64 columns");
   static_assert(S >= 2 && S <= 4 && LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -488,7 +488,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         // each MFMA followed by one of the next substep's LDS reads and, after
         // every second MFMA, one of the step's global->LDS loads, so that the
         // loads reach the address unit evenly spread over the step
-        constexpr int DSR = FM + 2 * C::FN;
+        constexpr int DSR = FM + (C::W8 ? 1 : 2) * C::FN;  // LDS reads per substep
         constexpr int MF = FM * C::FN;
         constexpr int VM = (AP == 1 || cur % 2 == 0) ? (AI + C::B_INST) : C::B_INST;
         __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);
@@ -989,12 +989,20 @@ hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t*
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, hipStream_t s, LaunchEvents ev) {
-  // the decode tile (32 rows, 4 waves of 64 columns, 64-deep K-steps, 4
-  // stages): the layer's bytes are the weights, streamed once per 32 rows
-  if (kind == GemmKind::kFfn1Gelu)
-    return launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, true, true>>(p, s, ev, w8.bscale);
-  return launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, false, true>>(p, s, ev, w8.bscale);
+hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, int avg_rows, hipStream_t s,
+                                  LaunchEvents ev) {
+  // Few rows per group (decoding): the decode tile (32 rows, 4 waves of 64
+  // columns, 64-deep K-steps, 4 stages), the layer's bytes being the
+  // weights, streamed once per 32 rows. Otherwise 128 x 128 tiles (4 waves
+  // of 64 x 64, paired activation stages, tail tiles): the per-block scale
+  // needs a second accumulator set, which the 256 x 256 tile's registers
+  // cannot hold.
+  const bool gelu = kind == GemmKind::kFfn1Gelu;
+  if (avg_rows < 64)
+    return gelu ? launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, true, true>>(p, s, ev, w8.bscale)
+                : launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, false, true>>(p, s, ev, w8.bscale);
+  return gelu ? launch_cfg<Cfg<bf16, bf16, 128, 128, 2, 2, 4, 4, true, true>>(p, s, ev, w8.bscale)
+              : launch_cfg<Cfg<bf16, bf16, 128, 128, 2, 2, 4, 4, false, true>>(p, s, ev, w8.bscale);
 }
 
 hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16_, int avg_rows,

@@ -97,9 +97,10 @@ struct GemmW8 {
 struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
-// bf16 activations times block-FP8 weights (GELU for kFfn1Gelu), in 32-row
-// tiles that stream the weights; K and Ncols multiples of 128.
-hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, hipStream_t s,
+// bf16 activations times block-FP8 weights (GELU for kFfn1Gelu); K and
+// Ncols multiples of 128. avg_rows: expected rows per group (tile choice:
+// 32-row tiles that stream the weights below 64, else 256 x 256).
+hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, int avg_rows, hipStream_t s,
                                   LaunchEvents ev = {});
 // E4M3 block quantisation (quant.hip): W [groups, K, Ncols] fp32 or bf16,
 // K and Ncols multiples of 128

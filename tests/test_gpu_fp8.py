@@ -93,9 +93,12 @@ class Dequantised:
 
 SCALED = {
     "decode_scaled": workloads.scaled(workloads.get("decode_top8_bf16"), T=64, d=512, h=256),
-    # more rows per expert than a tile, ragged groups, drops
+    # more rows per expert than a tile, ragged groups, drops (128 x 128 tiles; d = 384: GEMM2's last
+    # column tile has waves wholly past Ncols)
     "rows_ragged": workloads.MoESpec("rows_ragged", T=700, d=384, h=256, N=6, k=2, capacity_factor=1.1,
                                      gate="softmax", renorm=True, dtype="bf16"),
+    # the noisy gate scaled down: tail tiles, 2 and 4 scale blocks along K
+    "noisy_scaled": workloads.scaled(workloads.get("noisy_top2_bf16"), T=1500, d=256, h=512),
 }
 
 
@@ -127,13 +130,15 @@ def test_expert_ffn_fp8_matches_oracle(name):
     assert not dev.H[A:].any() and not dev.y_perm[A:].any()
 
 
-def test_forward_fp8_full_size_decode():
-    """The decode workload at its own size through moe_forward_fp8, as bench.py runs it."""
-    spec = workloads.get("decode_top8_bf16")
+@pytest.mark.parametrize("name", ["decode_top8_bf16", "noisy_top2_bf16"])
+def test_forward_fp8_full_size(name):
+    """The workload at its own size through moe_forward_fp8, as bench.py --weights fp8 runs it
+    (decode: 32-row tiles; noisy: 128 x 128 tiles)."""
+    spec = workloads.get(name)
     inp = make_inputs(spec, workloads.WORKLOAD_SEED[spec.name])
     dev = api.DeviceLayer(inp)
     dev.quantize_weights_fp8()
-    say("[case] full-size fp8 forward decode_top8_bf16")
+    say(f"[case] full-size fp8 forward {name}")
     dev.run_forward_fp8(inspect=True)
     torch.cuda.synchronize()
     lg = host(dev.logits)
