@@ -60,3 +60,44 @@ def test_graph_replays_match_eager(name):
         torch.cuda.synchronize()
         for n in OUTPUTS:
             assert torch.equal(getattr(dev, n), eager[n]), f"eager call after replay {rep}: {n} differs"
+
+
+FP8_CASES = {
+    "decode_top8_bf16": CASES["decode_top8_bf16"],           # 32-row tiles
+    "noisy_top2_bf16": CASES["noisy_top2_bf16"],             # 128 x 128 tiles
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_CASES))
+def test_fp8_graph_replays_match_eager(name):
+    """moe_forward_fp8 under a HIP graph: the same replay discipline."""
+    spec = FP8_CASES[name]
+    dev = api.DeviceLayer(make_inputs(spec, 12))
+    dev.quantize_weights_fp8()
+    say(f"[case] fp8 graph {spec.name} T={spec.T} d={spec.d} h={spec.h} N={spec.N} k={spec.k}")
+    dev.run_forward_fp8(inspect=True)
+    torch.cuda.synchronize()
+    eager = {n: getattr(dev, n).clone() for n in OUTPUTS}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dev.run_forward_fp8(inspect=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dev.run_forward_fp8(inspect=True)
+
+    for rep in range(4):
+        for n in OUTPUTS:
+            getattr(dev, n).fill_(-3)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in OUTPUTS:
+            assert torch.equal(getattr(dev, n), eager[n]), f"replay {rep}: {n} differs from the eager call"
+        dev.run_forward_fp8(inspect=True)
+        torch.cuda.synchronize()
+        for n in OUTPUTS:
+            assert torch.equal(getattr(dev, n), eager[n]), f"eager call after replay {rep}: {n} differs"
