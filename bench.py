@@ -6,7 +6,10 @@ One step is one pass of the whole layer (gate, dispatch, expert FFN,
 combine) over one batch of seeded synthetic tokens, through the single
 moe_forward entry point, with every input already resident in HBM. W warmup
 steps, then exactly K timed steps bracketed by torch.cuda.synchronize(); the
-headline value is T tokens over the mean step time.
+headline value is T tokens over the mean step time. The default workload is
+the largest of the five that fits one GPU: the large-expert top-2 layer
+(T = 8192, d = 4096, h = 14336, N = 8 experts), whose expert GEMMs are
+compute bound; --workload names any of the others.
 
 Besides the headline:
   - stages: the same layer through the four stage entry points, with HIP
@@ -16,7 +19,12 @@ Besides the headline:
   - graph_ms_per_step: moe_forward captured once in a HIP graph and replayed
     (no host launch cost per kernel);
   - cold: each step timed alone by events after writing a 512 MiB buffer
-    (twice the last-level cache), median / p10 / p90.
+    (twice the last-level cache), median / p10 / p90;
+  - measured_peaks: the chip's own ceilings in the same run, a 1 GiB device
+    copy with 16-byte loads and stores (HBM, read + write bytes) and a loop
+    of bf16 MFMAs on registers over every CU (moe_probe_copy, moe_probe_mfma);
+    the roofline object gives the FFN's fraction of the measured ceiling
+    beside its fraction of the published one.
 The roofline object describes the expert FFN kernel of moe_forward (the
 single persistent launch of GEMM1+GELU and GEMM2 where the shapes allow it,
 else the two grouped-GEMM launches), against the bf16 MFMA peak, or against
@@ -96,7 +104,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="noisy_top2_bf16")
+    ap.add_argument("--workload", default="large_expert_top2_bf16")
     ap.add_argument("--weights", choices=["layer", "fp8"], default="layer",
                     help="expert weights in the layer's dtype, or block-FP8 (moe_forward_fp8; bf16 layers)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -262,6 +270,9 @@ def main() -> int:
         api.time_ffn_launches(None, None)
     ffn_kernel_ms = float(np.mean(ffn_kernel_ms))
 
+    # ---- the chip's measured ceilings, in this run
+    peaks = None if args.skip_extras else measured_peaks(api, torch, stream)
+
     # ---- headline: W warm-up steps, then exactly K timed steps of moe_forward
     for _ in range(args.warmup):
         forward()
@@ -306,6 +317,10 @@ def main() -> int:
                           "HIP events the launches record (GEMM1's start to GEMM2's end), mean over "
                           "moe_forward steps")
     roof["kernel_ms"] = ffn_kernel_ms
+    if peaks:
+        mp = peaks["hbm_copy_GB/s"] if roof["bound"] == "hbm" else peaks["mfma_bf16_TFLOP/s"]
+        roof["measured_peak"] = mp
+        roof["frac_of_measured_peak"] = roof["achieved"] / mp
     roof["algorithmic"] = {"flops": ffn_flops, "touched_weight_bytes": touched_weight_bytes}
     traffic, tsrc = read_traffic(spec.name + ("_fp8w" if fp8 else ""))
     roof["traffic"] = traffic
@@ -366,9 +381,41 @@ def main() -> int:
         "staged_ms_per_step": staged_ms,
         "graph_ms_per_step": graph_ms,
         "cold": cold_ms,
+        "measured_peaks": peaks,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def measured_peaks(api, torch, stream):
+    """HBM copy bandwidth (read + write bytes over 1 GiB, beyond the 256 MB
+    last-level cache) and the bf16 MFMA rate with register operands only,
+    each the best of 5 timed launches after 2 untimed ones."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+
+    def best(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    t_copy = best(lambda: api.probe_copy(src, dst))
+    del src, dst
+    iters = 40000
+    flops, sink = api.probe_mfma(iters)
+    t_mfma = best(lambda: api.probe_mfma(iters, sink))
+    return {"hbm_copy_GB/s": 2 * n / t_copy / 1e9, "hbm_copy_bytes": 2 * n,
+            "mfma_bf16_TFLOP/s": flops / t_mfma / 1e12, "mfma_flops": flops}
 
 
 def cpu_baseline(spec, inp, target_s: float):
@@ -427,7 +474,9 @@ def _short(name: str) -> str:
         return "fused_ffn_kernel<" + m.group(1) + ">"
     for key in ("gate_logits_kernel", "gate_select_kernel", "cosine_select_kernel", "count_kernel",
                 "scan_kernel", "slots_kernel", "permute_kernel", "combine_kernel", "fill_kernel",
-                "gate_fused_kernel", "gate_partial_kernel", "gate_finish_kernel", "rows_kernel"):
+                "gate_fused_kernel", "gate_partial_kernel", "gate_finish_kernel", "rows_kernel",
+                "copy_kernel", "mfma_kernel", "ffn_status_kernel", "cosine_gate_kernel", "aux_partial_kernel",
+                "aux_final_kernel", "quantize_fp8_kernel"):
         if key in name:
             return key
     return name[:70]

@@ -28,8 +28,9 @@
  *    noise, expert_emb, logit_bias, logits and topk_w are always fp32; index
  *    arrays are int32.
  *  - The caller owns every buffer, including the workspace. The library
- *    never allocates, frees or synchronises, and keeps no pointer after a
- *    call returns.
+ *    never allocates, frees or synchronises (the one exception is the debug
+ *    build's check of caller routing in moe_dispatch), and keeps no pointer
+ *    after a call returns.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL is the default
  *    stream) and runs asynchronously; the call does not wait for it.
  *  - All arguments are checked on the host before anything is enqueued; on
@@ -118,7 +119,14 @@ MOE_API int64_t moe_rows_bound(const moe_desc_t* desc);
 /* Bytes of device workspace `kind` needs (a multiple of 256). Host only. */
 MOE_API moe_status_t moe_workspace_size(const moe_desc_t* desc, moe_ws_kind_t kind, size_t* bytes);
 
-/* Gate: logits, top-k selection and weights.
+/* Gate: logits, top-k selection and weights. The noisy logits and the
+ * top-k with a softmax over the selected logits follow the noisy top-k
+ * gating code of "MoE稀疏计算加速技术解析与应用实践" §2.1 (and of
+ * "MoE架构：稀疏激活机制如何提升模型计算效率" §2.1); the full-softmax weight of
+ * each selected expert (renorm = 0) is the top-1 MOELayer example of
+ * "PyTorch-CUDA-v2.6镜像是否支持MoE稀疏激活架构" (section "PyTorch v2.6：为动态
+ * 计算而生"); the cosine gate is the cosine_top router named on
+ * "4大技术模块掌握Tutel MoE…" (dynamic routing section).
  *   x [T, d] X-dtype; w_gate [d, N] (SOFTMAX, NOISY); w_noise [d, N] and
  *   noise [T, N] fp32 (NOISY); proj [d, p] X-dtype and expert_emb [N, p] fp32
  *   (COSINE); logit_bias [N] fp32 or NULL (any gate).
@@ -133,9 +141,18 @@ MOE_API moe_status_t moe_route(const moe_desc_t* desc, const void* x, const void
                        int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
                        void* stream);
 
-/* Capacity-limited dispatch in token order.
- *   topk_idx [T, k] int32: each token's experts, distinct, in [0, N); an
- *   out-of-range entry is treated as dropped.
+/* Capacity-limited dispatch in token order: tokens grouped by their chosen
+ * expert before one batched matmul per group ("MoE架构：稀疏激活机制如何提升
+ * 模型计算效率" §3.1), each expert holding at most C = capacity_factor * T*k/N
+ * of them (capacity_factor on "MoE稀疏计算加速技术解析与应用实践" §3.2 and the
+ * Tutel guide's dynamic routing section).
+ *   topk_idx [T, k] int32: each token's experts, which must be distinct and
+ *   in [0, N). In a release build an entry outside [0, N), or one that
+ *   repeats an earlier expert of the same token, is treated as dropped
+ *   (row -1) and counts for no expert. The debug build
+ *   (libmoe_gfx950_debug.so, compiled with MOE_DEBUG_CHECKS) copies topk_idx
+ *   to the host, synchronising the stream, and returns MOE_ERR_INVALID with
+ *   a message naming the first offending (t, j) instead.
  * Outputs: expert_count [N] (demand: choices per expert before the capacity
  *   limit); expert_off [N+1] (exclusive scan of kept = min(count, C);
  *   expert_off[N] = A, the number of kept choices); row_of [T*k] (row of
@@ -149,7 +166,10 @@ MOE_API moe_status_t moe_dispatch(const moe_desc_t* desc, const void* x, const i
                           int32_t* token_of_row, void* x_perm, void* ws, size_t ws_bytes,
                           void* stream);
 
-/* Grouped expert FFN on the expert-contiguous rows.
+/* Grouped expert FFN on the expert-contiguous rows: one batched matmul per
+ * group of tokens ("MoE架构：稀疏激活机制如何提升模型计算效率" §3.1), the expert
+ * being the Linear-GELU-Linear block of "MoE稀疏计算加速技术解析与应用实践"
+ * §3.2.
  *   x_perm [R, d]; expert_off [N+1] (device); W1 [N, d, h]; b1 [N, h] or NULL;
  *   W2 [N, h, d]; b2 [N, d] or NULL. All X-dtype except expert_off.
  * For e < N and off[e] <= r < off[e+1]:
@@ -162,12 +182,17 @@ MOE_API moe_status_t moe_dispatch(const moe_desc_t* desc, const void* x, const i
  * single-launch form of the two GEMMs (bf16 layers with enough rows and
  * columns for 256x256 tiles), in which GEMM2's tiles wait for the rows of H
  * they read; with NULL the two GEMMs always run as two launches. The values
- * do not depend on which form runs. */
+ * do not depend on which form runs. In the single-launch form a GEMM2 tile's
+ * wait for its rows of H is bounded (about 0.1 s); it has never been seen to
+ * expire, but if it does, that tile's y_perm values are set to NaN rather
+ * than computed from an incomplete H, and moe_ffn_status reports it. */
 MOE_API moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
                             const void* W1, const void* b1, const void* W2, const void* b2,
                             void* H, void* y_perm, void* ws, size_t ws_bytes, void* stream);
 
-/* Gate-weighted combine: y[t] = sum over j with row_of[t*k+j] >= 0, in j order,
+/* Gate-weighted combine, the layer output y = sum_i g_i(x) E_i(x) of
+ * "MoE架构：突破单卡算力瓶颈的密钥" §1.2:
+ * y[t] = sum over j with row_of[t*k+j] >= 0, in j order,
  * of topk_w[t, j] * y_perm[row_of[t*k+j]], accumulated in fp32 and rounded once;
  * a token with every choice dropped gets a zero row. y [T, d] X-dtype. */
 MOE_API moe_status_t moe_combine(const moe_desc_t* desc, const void* y_perm, const int32_t* row_of,
@@ -275,6 +300,18 @@ MOE_API moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_id
                                   float* importance, float* losses, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* Status of the expert FFN's single-launch form in the most recent
+ * moe_forward (kind MOE_WS_FORWARD) or moe_expert_ffn (kind MOE_WS_FFN) call
+ * made with this workspace: enqueues on `stream` a copy of its status word
+ * into *status (a DEVICE int32; read it after the stream has reached this
+ * point). 0: no GEMM2 tile's wait for its rows of H expired (also where the
+ * layer does not use that form); bit 0 set: at least one did, and those
+ * tiles' y_perm values (and so y) are NaN. The next layer call on the
+ * workspace clears the word. Callers who capture the layer in a graph can
+ * capture this call after it. */
+MOE_API moe_status_t moe_ffn_status(const moe_desc_t* desc, moe_ws_kind_t kind, const void* ws, size_t ws_bytes,
+                                    int32_t* status, void* stream);
+
 /* Profiling aid. While set, the expert FFN's kernel launches (in
  * moe_expert_ffn and moe_forward) record start_event (a hipEvent_t) when the
  * FFN's first kernel begins executing and stop_event when its last kernel
@@ -285,6 +322,20 @@ MOE_API moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_id
  * process-wide and unsynchronised: change it while no other thread enqueues
  * layers. Always returns MOE_OK. */
 MOE_API moe_status_t moe_time_ffn_launches(void* start_event, void* stop_event);
+
+/* Measurement aids, to judge the layer's kernels against the chip's measured
+ * ceilings as well as its published ones (run in the same process, timed by
+ * the caller with events around the call).
+ * moe_probe_copy: copies `bytes` (a positive multiple of 16) from src to dst
+ * (device, 16-byte aligned, not overlapping) with 16-byte loads and stores;
+ * moved bytes = 2 * bytes (read + write).
+ * moe_probe_mfma: `iters` rounds of bf16 32x32x16 MFMAs on register operands
+ * over the whole chip, no memory traffic; *flops (host) receives the flops it
+ * performs; sink: a device array of moe_probe_mfma_sink_floats() floats that
+ * receives meaningless sums (so that the work cannot be removed). */
+MOE_API moe_status_t moe_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+MOE_API moe_status_t moe_probe_mfma(int32_t iters, float* sink, int64_t* flops, void* stream);
+MOE_API int64_t moe_probe_mfma_sink_floats(void);
 
 /* Static name of a status code. */
 MOE_API const char* moe_status_string(moe_status_t status);

@@ -7,6 +7,8 @@ from ctypes import POINTER, c_char_p, c_double, c_float, c_int, c_int32, c_int64
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_gfx950.so")
+# the same library with the debug checks of caller routing (MOE_DEBUG_CHECKS)
+DEBUG_LIB_PATH = os.path.join(HERE, "libmoe_gfx950_debug.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
@@ -53,6 +55,10 @@ SIGNATURES = {
     "moe_combine": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 4 + [c_void_p]),
     "moe_forward": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p, c_size_t, c_void_p]),
     "moe_time_ffn_launches": (c_int, [c_void_p, c_void_p]),
+    "moe_ffn_status": (c_int, [POINTER(MoeDesc), c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "moe_probe_copy": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
+    "moe_probe_mfma": (c_int, [c_int32, c_void_p, POINTER(c_int64), c_void_p]),
+    "moe_probe_mfma_sink_floats": (c_int64, []),
     "moe_quantize_fp8": (c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "moe_expert_ffn_fp8": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 10 + [c_void_p]),
     "moe_forward_fp8": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), POINTER(MoeFp8Weights), c_void_p,
@@ -64,14 +70,14 @@ SIGNATURES = {
     "moe_version": (c_char_p, []),
 }
 
-_lib = None
+_libs = {}
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Loads the HIP library once. Raises if it has not been built: there is no
-    other implementation to fall back to."""
-    global _lib
-    if _lib is None:
+    """Loads a build of the HIP library once (the release build by default).
+    Raises if it has not been built: there is no other implementation to fall
+    back to."""
+    if path not in _libs:
         if not os.path.exists(path):
             raise RuntimeError(
                 f"{path} is missing: build it with `python -m mixture_experts_sparse_gate_amd.build` "
@@ -81,5 +87,5 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]

@@ -48,9 +48,9 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check(status: int, what: str) -> None:
+def _check(status: int, what: str, lib_path: str = _lib.LIB_PATH) -> None:
     if status != _lib.MOE_OK:
-        lib = _lib.load()
+        lib = _lib.load(lib_path)
         raise RuntimeError(f"{what}: {lib.moe_status_string(status).decode()}: "
                            f"{lib.moe_last_error().decode()}")
 
@@ -84,12 +84,14 @@ def route(desc, x, w_gate=None, w_noise=None, noise=None, proj=None, expert_emb=
 
 
 def dispatch(desc, x, topk_idx, expert_count, expert_off, row_of, token_of_row, x_perm, ws=None,
-             stream=None):
-    st = _lib.load().moe_dispatch(ctypes.byref(desc), _ptr(x), _ptr(topk_idx), _ptr(expert_count),
+             stream=None, lib_path=_lib.LIB_PATH):
+    """moe_dispatch; lib_path=_lib.DEBUG_LIB_PATH calls the debug build, which
+    checks the caller's routing on the host first."""
+    st = _lib.load(lib_path).moe_dispatch(ctypes.byref(desc), _ptr(x), _ptr(topk_idx), _ptr(expert_count),
                                   _ptr(expert_off), _ptr(row_of), _ptr(token_of_row), _ptr(x_perm),
                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream))
-    _check(st, "moe_dispatch")
+    _check(st, "moe_dispatch", lib_path)
 
 
 def expert_ffn(desc, x_perm, expert_off, W1, b1, W2, b2, H, y_perm, ws=None, stream=None):
@@ -106,6 +108,35 @@ def aux_loss(desc, topk_idx, topk_w, importance=None, losses=None, ws=None, stre
                                   _ptr(losses), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream))
     _check(st, "moe_aux_loss")
+
+
+def ffn_status(desc, ws, kind=_lib.MOE_WS_FORWARD, stream=None) -> torch.Tensor:
+    """moe_ffn_status: a device int32 tensor holding the status word of the
+    single-launch expert FFN in the last layer call made with workspace ws
+    (0: every GEMM2 tile's wait for H completed)."""
+    out = torch.full((1,), -1, dtype=torch.int32, device=ws.device if ws is not None else "cuda")
+    st = _lib.load().moe_ffn_status(ctypes.byref(desc), kind, _ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(), _ptr(out), _stream(stream))
+    _check(st, "moe_ffn_status")
+    return out
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """moe_probe_copy of all of src's bytes into dst (the HBM copy probe)."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst is smaller than src")
+    _check(_lib.load().moe_probe_copy(_ptr(src), _ptr(dst), n, _stream(stream)), "moe_probe_copy")
+
+
+def probe_mfma(iters: int, sink: Optional[torch.Tensor] = None, stream=None):
+    """moe_probe_mfma: returns (flops, sink)."""
+    lib = _lib.load()
+    if sink is None:
+        sink = torch.empty(int(lib.moe_probe_mfma_sink_floats()), dtype=torch.float32, device="cuda")
+    flops = ctypes.c_int64(0)
+    _check(lib.moe_probe_mfma(int(iters), _ptr(sink), ctypes.byref(flops), _stream(stream)), "moe_probe_mfma")
+    return int(flops.value), sink
 
 
 def time_ffn_launches(start_event=None, stop_event=None):

@@ -2,8 +2,12 @@
 
     python -m mixture_experts_sparse_gate_amd.build [-j JOBS]
 
-Objects go to <repo>/_build/ and the library next to this file. Every call
-recompiles, so a call always checks that the current sources compile.
+Objects go to <repo>/_build/ and the libraries next to this file:
+libmoe_gfx950.so, and libmoe_gfx950_debug.so, the same library with the
+debug checks of caller-supplied routing (-DMOE_DEBUG_CHECKS: moe_dispatch
+copies topk_idx to the host and rejects indices outside [0, N) or repeated
+within a token). Every call recompiles, so a call always checks that the
+current sources compile.
 """
 from __future__ import annotations
 
@@ -23,7 +27,10 @@ LIB_NAME = "libmoe_gfx950.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["gate.hip", "dispatch.hip", "gemm.hip", "combine.hip", "aux.hip", "quant.hip", "capi.hip"]
+SOURCES = ["gate.hip", "dispatch.hip", "gemm.hip", "combine.hip", "aux.hip", "quant.hip", "probe.hip", "capi.hip"]
+HOST_SOURCES = ["routing_check.cpp"]
+DEBUG_LIB_NAME = "libmoe_gfx950_debug.so"
+DEBUG_LIB_PATH = os.path.join(HERE, DEBUG_LIB_NAME)
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -40,9 +47,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP kernels)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden"]
+
+
+def _compile(job) -> str:
+    src, debug = job if isinstance(job, tuple) else (job, False)
+    stem = os.path.splitext(src)[0] + ("_debug" if debug else "")
+    obj = os.path.join(BUILD_DIR, stem + ".o")
+    if src.endswith(".cpp"):
+        cmd = ["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc(), *HIP_FLAGS, *(["-DMOE_DEBUG_CHECKS"] if debug else []), "-c", os.path.join(CSRC, src),
+               "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -53,19 +69,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1), 16)
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(jobs: int = 0, verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs_list = SOURCES + HOST_SOURCES + [("capi.hip", True)]
+    jobs = jobs or min(len(jobs_list), max(1, os.cpu_count() or 1), 16)
+    with ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, jobs_list))
+    release = objs[:len(SOURCES) + len(HOST_SOURCES)]
+    debug = [o for o in release if not o.endswith(os.sep + "capi.o")] + [objs[-1]]
+    _link(release, LIB_PATH)
+    _link(debug, DEBUG_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {DEBUG_LIB_NAME}")
     return LIB_PATH
 
 

@@ -8,8 +8,11 @@
 
 #include <atomic>
 
+#include <vector>
+
 #include "moe.h"
 #include "kernels.hpp"
+#include "routing_check.h"
 
 namespace {
 
@@ -128,14 +131,18 @@ RouteWs route_ws(const moe_desc_t* d) {
   return w;
 }
 
+// per-tile counts, and (for large count tables) the scan's per-tile
+// prefixes and totals
 struct DispatchWs {
-  size_t tile_counts, bytes;
+  size_t tile_counts, tile_start, totals, bytes;
 };
 DispatchWs dispatch_ws(const moe_desc_t* d) {
   DispatchWs w{};
   const size_t t = (size_t)ntiles_of(d) * d->N * 4;
   w.tile_counts = 0;
-  w.bytes = align_up(t);
+  w.tile_start = align_up(t);
+  w.totals = w.tile_start + align_up(t);
+  w.bytes = w.totals + align_up((size_t)d->N * 4);
   return w;
 }
 
@@ -236,15 +243,19 @@ moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, co
 // zero, zero_n: ints for the dispatch to clear on the way (the fused FFN's
 // counters), or null
 // hist32: the gate's per-32-token choice counts, or null (counted here)
+// caller_routing: idx comes from the caller (moe_dispatch), not the gate
 moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx, int32_t* count,
                          int32_t* off, int32_t* row_of, int32_t* token_of_row, void* x_perm,
                          void* ws, hipStream_t s, int32_t* zero = nullptr, int zero_n = 0,
-                         const int32_t* hist32 = nullptr) {
+                         const int32_t* hist32 = nullptr, bool caller_routing = false) {
   const DispatchWs dw = dispatch_ws(d);
   moe::DispatchParams p{};
   p.x = x;
   p.topk_idx = idx;
   p.tile_counts = at<int32_t>(ws, dw.tile_counts);
+  p.tile_start = at<int32_t>(ws, dw.tile_start);
+  p.totals = at<int32_t>(ws, dw.totals);
+  p.caller_routing = caller_routing ? 1 : 0;
   p.expert_count = count;
   p.expert_off = off;
   p.row_of = row_of;
@@ -476,6 +487,21 @@ moe_status_t forward_impl(const moe_desc_t* desc, const moe_layer_tensors_t* t, 
   return do_combine(desc, y_perm, row_of, w, t->y, s);
 }
 
+#ifdef MOE_DEBUG_CHECKS
+// Debug builds: the caller's routing is copied to the host (synchronising
+// the stream) and checked: every index in [0, N), distinct per token.
+moe_status_t debug_check_routing(const moe_desc_t* d, const int32_t* idx, hipStream_t s) {
+  const size_t n = (size_t)d->T * d->k;
+  std::vector<int32_t> h(n);
+  TRY(hip_status(hipMemcpyAsync(h.data(), idx, n * 4, hipMemcpyDeviceToHost, s), "debug routing copy"));
+  TRY(hip_status(hipStreamSynchronize(s), "debug routing copy"));
+  char msg[256];
+  if (moe_check_routing_host(h.data(), d->T, d->k, d->N, msg, sizeof(msg)) != 0)
+    return fail(MOE_ERR_INVALID, "topk_idx: %s", msg);
+  return MOE_OK;
+}
+#endif
+
 }  // namespace
 
 extern "C" {
@@ -530,8 +556,11 @@ moe_status_t moe_dispatch(const moe_desc_t* desc, const void* x, const int32_t* 
   TRY(need(token_of_row, "token_of_row", 4));
   TRY(need(x_perm, "x_perm", 16));
   TRY(check_ws(ws, ws_bytes, dispatch_ws(desc).bytes));
+#ifdef MOE_DEBUG_CHECKS
+  TRY(debug_check_routing(desc, topk_idx, (hipStream_t)stream));
+#endif
   return do_dispatch(desc, x, topk_idx, expert_count, expert_off, row_of, token_of_row, x_perm, ws,
-                     (hipStream_t)stream);
+                     (hipStream_t)stream, nullptr, 0, nullptr, true);
 }
 
 moe_status_t moe_expert_ffn(const moe_desc_t* desc, const void* x_perm, const int32_t* expert_off,
@@ -630,6 +659,42 @@ moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_idx, const
   p.k = desc->k;
   return hip_status(moe::launch_aux_loss(p, (hipStream_t)stream), "load-balance terms");
 }
+
+moe_status_t moe_ffn_status(const moe_desc_t* desc, moe_ws_kind_t kind, const void* ws, size_t ws_bytes,
+                            int32_t* status, void* stream) {
+  TRY(check_desc(desc));
+  TRY(need(status, "status", 4));
+  const int32_t* counters = nullptr;
+  if (kind == MOE_WS_FORWARD) {
+    const ForwardWs fw = forward_ws(desc);
+    TRY(check_ws(const_cast<void*>(ws), ws_bytes, fw.bytes));
+    if (fw.n_counters) counters = reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + fw.ffn_counters);
+  } else if (kind == MOE_WS_FFN) {
+    const int n = ffn_counters_of(desc);
+    TRY(check_ws(const_cast<void*>(ws), ws_bytes, align_up((size_t)n * 4)));
+    if (n) counters = static_cast<const int32_t*>(ws);
+  } else {
+    return fail(MOE_ERR_INVALID, "moe_ffn_status: kind must be MOE_WS_FORWARD or MOE_WS_FFN");
+  }
+  return hip_status(moe::launch_ffn_status(counters, status, (hipStream_t)stream), "FFN status");
+}
+
+moe_status_t moe_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 16 || bytes % 16) return fail(MOE_ERR_INVALID, "moe_probe_copy: bytes must be a positive multiple of 16");
+  TRY(need(src, "src", 16));
+  TRY(need(dst, "dst", 16));
+  return hip_status(moe::launch_probe_copy(src, dst, bytes, (hipStream_t)stream), "probe copy");
+}
+
+moe_status_t moe_probe_mfma(int32_t iters, float* sink, int64_t* flops, void* stream) {
+  if (iters < 1) return fail(MOE_ERR_INVALID, "moe_probe_mfma: iters must be >= 1");
+  TRY(need(sink, "sink", 4));
+  if (!flops) return fail(MOE_ERR_INVALID, "flops is NULL");
+  *flops = moe::probe_mfma_flops_per_iter() * iters;
+  return hip_status(moe::launch_probe_mfma(iters, sink, (hipStream_t)stream), "probe mfma");
+}
+
+int64_t moe_probe_mfma_sink_floats(void) { return (int64_t)moe::probe_mfma_blocks() * 8; }
 
 moe_status_t moe_time_ffn_launches(void* start_event, void* stop_event) {
   g_ffn_events.start = static_cast<hipEvent_t>(start_event);

@@ -733,19 +733,32 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p, 
 // all of H's columns): after storing its H tile, a GEMM1 block waits for its
 // stores to complete and counts the tile in ready[row tile]; a GEMM2 block
 // waits for that count. H is produced and consumed under one XCD's L2, so
-// completed stores are what the consumer reads. No block waits on a tile
-// that no running block holds: every GEMM1 tile of an XCD is dequeued before
-// any of its GEMM2 tiles, by a block that computes it without waiting. The
-// wait is bounded all the same. A block's XCD is read from the hardware, so
-// the placement of blocks does not matter for correctness; every XCD gets
-// blocks as the grid is a multiple of the XCD count.
+// completed stores are what the consumer reads there; the consumer's own
+// vector L1 is not coherent with other CUs' stores, so after the wait every
+// wave of the block invalidates it (an agent-scope acquire fence, which on
+// gfx950 invalidates the L1 and leaves the L2's lines of device memory in
+// place) before any H load is issued. No block waits on a tile that no
+// running block holds: every GEMM1 tile of an XCD is dequeued before any of
+// its GEMM2 tiles, by a block that computes it without waiting. The wait is
+// bounded all the same; if it ever expires, the GEMM2 tile is not computed
+// from an incomplete H: its outputs are set to NaN and the launch's status
+// word records the expiry (moe_ffn_status reads it). A block's XCD is read
+// from the hardware, so the placement of blocks does not matter for
+// correctness; every XCD gets blocks as the grid is a multiple of the XCD
+// count.
 struct FusedFfn {
   GemmParams g1, g2;  // GEMM1 (GELU) and GEMM2, as for two launches
-  int32_t* counters;  // [kNumXcds] queues, then ready[row tiles]: zero at launch
+  // [kNumXcds] queues, the status word (bit 0: a wait for H expired), then
+  // ready[row tiles]: zero at launch
+  int32_t* counters;
 };
 
 constexpr uint32_t kHwRegXccId = (3u << 11) | 20u;  // s_getreg: XCC_ID[3:0]
 constexpr int kFusedMaxGroups = 256;
+constexpr int kFusedStatus = kNumXcds;      // index of the status word in the counters
+constexpr int kFusedReady = kNumXcds + 1;   // index of ready[0]
+// polls of a GEMM2 tile's wait (s_sleep 4 each, about 0.1 s in all)
+constexpr int kFusedMaxPolls = 1 << 20;
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
@@ -756,7 +769,7 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
   // come before the group's (exclusive prefixes)
   __shared__ int g_lo[kFusedMaxGroups], g_hi[kFusedMaxGroups], g_ef[kFusedMaxGroups], g_et[kFusedMaxGroups];
   __shared__ int tot[2];
-  __shared__ int sched[8];
+  __shared__ int sched[9];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int xcc = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kNumXcds - 1));
   if (wave == 0) {
@@ -821,7 +834,7 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
         (const __attribute__((address_space(4))) FusedFfn*)__builtin_amdgcn_kernarg_segment_ptr();
     __asm__ volatile("" : "+s"(fp));
     const int NT1 = (fp->g1.Ncols + BN - 1) / BN, NT2 = (fp->g2.Ncols + BN - 1) / BN;
-    int32_t* const ready = fp->counters + kNumXcds;
+    int32_t* const ready = fp->counters + kFusedReady;
     __syncthreads();  // sched[0]: this item's index
     if (wave == 0) {
       const int groups = fp->g1.groups;
@@ -878,23 +891,45 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
     const int n0 = __builtin_amdgcn_readfirstlane(sched[5]);
     const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[6]) != 0;
     const int rid = __builtin_amdgcn_readfirstlane(sched[7]);
+    int expired = 0;
     if (kind == 2) {
       if (tid == 0) {
-        for (int spin = 0; spin < (1 << 20); ++spin) {
+        int spin = 0;
+        for (; spin < kFusedMaxPolls; ++spin) {
           if (__hip_atomic_load(ready + rid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= NT1) break;
           __builtin_amdgcn_s_sleep(4);
         }
+        sched[8] = spin == kFusedMaxPolls;
+        if (spin == kFusedMaxPolls)
+          __hip_atomic_fetch_or(fp->counters + kFusedStatus, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();
+      // the H lines this CU's L1 may hold from before they were written are
+      // dropped before the tile loads H
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      expired = __builtin_amdgcn_readfirstlane(sched[8]);
     }
-    // one copy of the tile code for both GEMMs
-    const __attribute__((address_space(4))) GemmParams* pp = kind == 1 ? &fp->g1 : &fp->g2;
     int next = 0;
-    gemm_tile<C>(*(const GemmParams*)pp, kind == 1, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0,
-                 tail_tile, nullptr, [&] {
-                   if (tid == 0)
-                     next = __hip_atomic_fetch_add(fp->counters + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                 });
+    if (expired) {
+      // H of these rows may be incomplete: the tile's outputs become NaN
+      // (bf16 0x7FC0) instead of a silently wrong product
+      const __attribute__((address_space(4))) GemmParams* pp = &fp->g2;
+      const int cols = min(BN, pp->Ncols - n0), cpr = cols / 8, rows = row_hi - row_lo;
+      bf16* out = static_cast<bf16*>(pp->C);
+      for (int i = tid; i < rows * cpr; i += C::THREADS)
+        store16(out + (int64_t)(row_lo + i / cpr) * pp->ldc + n0 + (i % cpr) * 8,
+                u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u});
+      if (tid == 0) next = __hip_atomic_fetch_add(fp->counters + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // one copy of the tile code for both GEMMs
+      const __attribute__((address_space(4))) GemmParams* pp = kind == 1 ? &fp->g1 : &fp->g2;
+      gemm_tile<C>(*(const GemmParams*)pp, kind == 1, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0,
+                   tail_tile, nullptr, [&] {
+                     if (tid == 0)
+                       next = __hip_atomic_fetch_add(fp->counters + xcc, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                   });
+    }
     if (kind == 1) {
       wait_vmcnt<0>();  // this thread's H stores are in the L2
       __syncthreads();  // ... and every thread's
@@ -958,10 +993,22 @@ __global__ __launch_bounds__(256) void fill_kernel(int32_t* p, int n) {
 
 }  // namespace
 
+namespace {
+// *out = the fused launch's status word (0 where the layer has none)
+__global__ void ffn_status_kernel(const int32_t* counters, int32_t* out) {
+  if (threadIdx.x == 0) *out = counters ? counters[kFusedStatus] : 0;
+}
+}  // namespace
+
+hipError_t launch_ffn_status(const int32_t* counters, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(ffn_status_kernel, dim3(1), dim3(64), 0, s, counters, out);
+  return hipGetLastError();
+}
+
 int fused_ffn_counters(const GemmParams& g1) {
   const int64_t full_max = (int64_t)g1.M / FusedCfg::BM + g1.groups;
   const int64_t tail_max = (int64_t)g1.groups * (FusedCfg::BM / (2 * FusedCfg::TBM));
-  return (int)(kNumXcds + full_max + tail_max);
+  return (int)(kFusedReady + full_max + tail_max);
 }
 
 bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16_, int avg_rows) {

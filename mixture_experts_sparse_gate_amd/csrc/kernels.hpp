@@ -63,8 +63,19 @@ struct DispatchParams {
   // the gate's per-32-token choice counts (GateParams::hist), or null: then
   // the dispatch counts them itself
   const int32_t* hist32;
+  // [nTiles, N] and [N] workspace for the scan of a large count table
+  // (used where dispatch_scans())
+  int32_t* tile_start;
+  int32_t* totals;
   int T, d, N, k, C, elem_bytes, zero_n;
+  // 1: the routing comes from the caller, and a choice that repeats an
+  // earlier choice of the same token is dropped like an out-of-range one
+  int caller_routing;
 };
+// Count tables of more entries than this are scanned by their own kernel
+// (one block per expert) instead of by every rows block.
+constexpr int64_t kDispatchDirectMax = 8192;
+bool dispatch_scans(int64_t T, int N, bool hist32);
 hipError_t launch_dispatch(const DispatchParams& p, hipStream_t s);
 hipError_t launch_permute(const DispatchParams& p, hipStream_t s);
 
@@ -117,6 +128,18 @@ bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16, int a
 int fused_ffn_counters(const GemmParams& g1);
 hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
                             hipStream_t s, LaunchEvents ev = {});
+// *out = the status word of the fused launch that last used `counters`
+// (bit 0: a GEMM2 tile's wait for its rows of H expired and its outputs were
+// set to NaN); counters null: *out = 0
+hipError_t launch_ffn_status(const int32_t* counters, int32_t* out, hipStream_t s);
+
+// ---- measurement aids (probe.hip)
+// copies bytes / 16 16-byte chunks from src to dst
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+// iters rounds of MFMAs on registers; sink: probe_mfma_blocks() * 8 floats
+hipError_t launch_probe_mfma(int iters, float* sink, hipStream_t s);
+int probe_mfma_blocks();
+int64_t probe_mfma_flops_per_iter();
 
 // ---- load-balance terms (aux.hip)
 constexpr int kAuxTok = 256;  // tokens per partial-sum block

@@ -1,0 +1,88 @@
+// Measurement aids: the chip's own ceilings, timed in the same run as the
+// layer, so that the layer's kernels can be judged against measured peaks
+// as well as published ones.
+//   copy_kernel  a plain device copy with 16-byte loads and stores (the
+//                STREAM "copy" pattern): HBM bandwidth for mixed read/write
+//                traffic once the buffers exceed the 256 MB last-level cache
+//   mfma_kernel  bf16 32x32x16 MFMAs on register operands only, four
+//                independent accumulators per wave: the matrix cores' rate
+//                with no memory traffic at all
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kCopyBlock = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyBlock) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                          int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * kCopyBlock * kCopyUnroll;
+  for (int64_t i0 = (int64_t)blockIdx.x * kCopyBlock * kCopyUnroll + threadIdx.x; i0 < n16; i0 += stride) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * kCopyBlock;
+      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = i0 + u * kCopyBlock;
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
+    }
+  }
+}
+
+constexpr int kMfmaWaves = 8;  // per block: two waves per SIMD
+
+__global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(int iters, float* sink) {
+  const int lane = lane_id();
+  // operands that the compiler cannot fold: built from the lane index
+  u32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = 0x3F803F80u ^ (uint32_t)(lane * (i + 1));
+    b[i] = 0x3F003F00u ^ (uint32_t)(lane + i);
+  }
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                       acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if (lane == 0) sink[blockIdx.x * kMfmaWaves + threadIdx.x / kWave] = s;
+}
+
+}  // namespace
+
+hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  if (n16 <= 0) return hipSuccess;
+  const int64_t per_block = (int64_t)kCopyBlock * kCopyUnroll;
+  const int64_t want = (n16 + per_block - 1) / per_block;
+  const int blocks = (int)(want < 256 * 16 ? want : 256 * 16);
+  hipLaunchKernelGGL(copy_kernel, dim3(blocks), dim3(kCopyBlock), 0, s, static_cast<const u32x4*>(src),
+                     static_cast<u32x4*>(dst), n16);
+  return hipGetLastError();
+}
+
+int probe_mfma_blocks() { return 256; }
+int64_t probe_mfma_flops_per_iter() { return (int64_t)probe_mfma_blocks() * kMfmaWaves * 4 * 2 * 32 * 32 * 16; }
+
+hipError_t launch_probe_mfma(int iters, float* sink, hipStream_t s) {
+  hipLaunchKernelGGL(mfma_kernel, dim3(probe_mfma_blocks()), dim3(kMfmaWaves * kWave), 0, s, iters, sink);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -47,7 +47,7 @@ added after the 1/tau scaling.
 from __future__ import annotations
 
 import math
-from typing import Dict, Iterable, Optional
+from typing import Dict, Optional
 
 import numpy as np
 import torch
@@ -300,48 +300,3 @@ def forward(spec, inp, logits_override: Optional[np.ndarray] = None) -> Dict[str
     y = combine(Y, r["row_of"], r["topk_w"], spec.T, k)
     r.update(x_perm=x_perm, H=H, y_perm=Y, y=y)
     return r
-
-
-def token_outputs(spec, inp, r: Dict[str, np.ndarray], tokens: Iterable[int]) -> np.ndarray:
-    """y[t] for selected tokens only, straight from the definition
-    y_t = sum over kept j of g_j(x_t) E_j(x_t), given a routing ``r`` from
-    ``route``. Used at full sizes where the whole layer is too slow on a CPU.
-    Each expert's weights are widened once for all the sampled tokens that
-    keep it; the terms of each y_t are still added in j order."""
-    k = spec.k
-    tokens = list(tokens)
-    terms = {}  # (i, j) -> g_j(x_t) E_j(x_t)
-    by_expert: Dict[int, list] = {}
-    for i, t in enumerate(tokens):
-        for j in range(k):
-            if r["row_of"][t * k + j] >= 0:
-                by_expert.setdefault(int(r["topk_idx"][t, j]), []).append((i, t, j))
-    for e, uses in by_expert.items():
-        xs = np.stack([inp.x[t] for _, t, _ in uses])
-        _, ye = expert_ffn(xs, inp.W1[e], inp.W2[e],
-                           None if inp.b1 is None else inp.b1[e],
-                           None if inp.b2 is None else inp.b2[e])
-        for (i, t, j), row in zip(uses, ye):
-            terms[(i, j)] = r["topk_w"][t, j] * row
-    out = np.zeros((len(tokens), spec.d), np.float64)
-    for i in range(len(tokens)):
-        for j in range(k):
-            if (i, j) in terms:
-                out[i] += terms[(i, j)]
-    return out
-
-
-def row_outputs(inp, r: Dict[str, np.ndarray], rows: Iterable[int], k: int):
-    """(H[row], y_perm[row]) for selected rows of the expert-grouped buffers."""
-    rows = list(rows)
-    off = r["off"]
-    Hs, Ys = [], []
-    for row in rows:
-        e = int(np.searchsorted(off, row, side="right") - 1)
-        t = int(r["token_of_row"][row]) // k
-        hh, yy = expert_ffn(inp.x[t:t + 1], inp.W1[e], inp.W2[e],
-                            None if inp.b1 is None else inp.b1[e],
-                            None if inp.b2 is None else inp.b2[e])
-        Hs.append(hh[0])
-        Ys.append(yy[0])
-    return np.array(Hs), np.array(Ys)

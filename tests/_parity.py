@@ -107,17 +107,3 @@ def check_output(spec, inp, dev, r, Y):
     tol = ROW_TOL[spec.dtype]
     assert e <= tol, f"y row error {e:.3g} > {tol}"
     return e
-
-
-def sample_tokens(spec, r, n=12, seed=0):
-    """First, last, random tokens, plus (if any) fully and partly dropped ones."""
-    rng = np.random.default_rng(seed)
-    T, k = spec.T, spec.k
-    kept = (r["row_of"].reshape(T, k) >= 0).sum(axis=1)
-    picks = {0, T - 1}
-    picks.update(rng.choice(T, size=min(T, n), replace=False).tolist())
-    for cond in (kept == 0, (kept > 0) & (kept < k)):
-        cand = np.nonzero(cond)[0]
-        if cand.size:
-            picks.update(rng.choice(cand, size=min(cand.size, 3), replace=False).tolist())
-    return sorted(picks)

@@ -5,7 +5,7 @@ take each decision in fp32). The FFN and the whole layer on FP8 weights are
 compared with the oracle's FFN on the oracle's own dequantised weights
 (decode(code) * scale, exact in float64), to the bf16 row tolerance.
 """
-import types
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -16,7 +16,7 @@ from mixture_experts_sparse_gate_amd.inputs import make_inputs
 from oracle import fp8_oracle as F
 from oracle import moe_oracle as O
 
-from _parity import ROW_TOL, check_logits, check_routing, host, row_rel_err, sample_tokens, say
+from _parity import ROW_TOL, check_logits, check_routing, host, row_rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -144,11 +144,26 @@ def test_forward_fp8_full_size(name):
     lg = host(dev.logits)
     check_logits(spec, inp, lg)
     r = check_routing(spec, inp, dev, lg)
-    toks = sample_tokens(spec, r, n=0)  # the first and last tokens: 16 experts, ~1 s of oracle each
-    ref_inp = types.SimpleNamespace(x=inp.x, W1=Dequantised(inp.W1), W2=Dequantised(inp.W2), b1=inp.b1, b2=inp.b2)
-    y_ref = O.token_outputs(spec, ref_inp, r, toks)
-    e = row_rel_err(host(dev.y[torch.as_tensor(toks, device=dev.y.device)]), y_ref)
-    say(f"   sampled {len(toks)} tokens, y err {e:.2e}")
+    # every token: each touched expert's weights quantised and dequantised by
+    # the oracle (threads over experts, one expert's float64 weights at a
+    # time), its rows through the oracle's FFN, then the oracle's combine
+    off = r["off"]
+    A = int(off[-1])
+    x_perm = O.f64(inp.x)[r["token_of_row"] // spec.k]
+    Y = np.zeros((A, spec.d), np.float64)
+
+    def expert(e):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            W1e, W2e = Dequantised(inp.W1)[e], Dequantised(inp.W2)[e]
+            _, Y[lo:hi] = O.expert_ffn(x_perm[lo:hi], W1e, W2e, None if inp.b1 is None else inp.b1[e],
+                                       None if inp.b2 is None else inp.b2[e])
+
+    with ThreadPoolExecutor(16) as ex:
+        list(ex.map(expert, range(spec.N)))
+    y_ref = O.combine(Y, r["row_of"], r["topk_w"], spec.T, spec.k)
+    e = row_rel_err(host(dev.y), y_ref)
+    say(f"   all {spec.T} tokens, y err {e:.2e}")
     assert e <= ROW_TOL["bf16"]
     # the same layer with bf16 weights differs by the quantisation only
     y8 = dev.y.clone()

@@ -25,6 +25,9 @@ CASES = {
     "cosine_zipf_top4_bf16": workloads.scaled(W["cosine_zipf_top4_bf16"], T=3000, d=256, h=128),
     "decode_top8_bf16": workloads.scaled(W["decode_top8_bf16"], T=64, d=512, h=256),
     "tiny_top1_f32": W["tiny_top1_f32"],
+    # full size: the expert FFN is the single persistent launch, whose work
+    # counters the captured dispatch clears on every replay
+    "noisy_top2_bf16_full": W["noisy_top2_bf16"],
 }
 OUTPUTS = ("y", "topk_idx", "topk_w", "row_of", "expert_off")
 

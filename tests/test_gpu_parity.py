@@ -3,9 +3,9 @@
 Scaled workloads (same routing parameters as the five named workloads, at
 shapes the oracle finishes in seconds, with several tiles and ragged tails)
 check every stage; the full-size workloads run moe_forward in the same
-launch configuration bench.py times and are checked on everything that is
-cheap to check exactly (routing, slots, offsets, row maps) and on sampled
-rows and tokens otherwise."""
+launch configuration bench.py times, and the stage calls on the same
+routing, and every row of y, H and y_perm is compared with the oracle's
+whole fp64 layer (seconds on the host even for the large-expert layer)."""
 import math
 
 import numpy as np
@@ -17,7 +17,7 @@ from mixture_experts_sparse_gate_amd.inputs import make_inputs
 from oracle import moe_oracle as O
 
 from _parity import (check_ffn, check_logits, check_output, check_routing, check_x_perm, host,
-                     row_rel_err, sample_tokens, say, ROW_TOL)
+                     row_rel_err, say, ROW_TOL)
 
 pytestmark = pytest.mark.gpu
 
@@ -89,17 +89,29 @@ def test_forward_equals_stages(name):
     assert torch.equal(dev.y, y_st)
 
 
+def assert_ffn_status_clear(dev, kind=_lib.MOE_WS_FORWARD, ws=None):
+    """The single-launch FFN's status word: no GEMM2 tile's wait for H expired."""
+    st = api.ffn_status(dev.desc, dev.ws if ws is None else ws, kind)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, f"fused FFN status word {int(st.item())}"
+
+
 @pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
 def test_full_size_forward(name):
-    """The workload at its own size, one moe_forward call as bench.py makes it."""
+    """The workload at its own size: one moe_forward call as bench.py makes
+    it, then the stage calls on the same routing; every row of y, H and
+    y_perm against the oracle's fp64 layer on the GPU's fp32 logits."""
     spec = W[name]
     inp = make_inputs(spec, workloads.WORKLOAD_SEED[name])
     dev = api.DeviceLayer(inp)
     say(f"[case] full-size forward {name}")
     dev.run_forward(inspect=True)
     torch.cuda.synchronize()
+    assert_ffn_status_clear(dev)
     lg = host(dev.logits)
     ref_l = check_logits(spec, inp, lg)
+    say("   oracle forward on the GPU's logits")
+    ref = O.forward(spec, inp, logits_override=lg)
     r = check_routing(spec, inp, dev, lg)
     # routing from the oracle's own fp64 logits agrees except at near-ties
     _, idx_ref = O.top_k(ref_l, spec.k)
@@ -107,21 +119,31 @@ def test_full_size_forward(name):
     say(f"   tokens routed differently from fp64 logits: {differ} of {spec.T}")
     assert differ <= max(1, spec.T // 1000)
     A = int(r["off"][-1])
-    # moe_forward keeps x_perm in its workspace: rebuild it with moe_dispatch
-    # on the same routing, which must reproduce forward's row maps exactly
+    e = row_rel_err(host(dev.y), ref["y"])
+    say(f"   A={A}: all {spec.T} rows of y, error {e:.2e}")
+    assert e <= ROW_TOL[spec.dtype]
+    y_fwd = dev.y.clone()
+    # the stage calls on the same routing: moe_dispatch must reproduce
+    # forward's row maps exactly; then every row of x_perm (bitwise), H and
+    # y_perm (the expert FFN as moe_expert_ffn runs it with a workspace: the
+    # single persistent launch where the shapes allow it)
     row_of_fwd, tor_fwd = dev.row_of.clone(), dev.token_of_row.clone()
     api.dispatch(dev.desc, dev.x, dev.topk_idx, dev.expert_count, dev.expert_off, dev.row_of,
                  dev.token_of_row, dev.x_perm, ws=dev.ws)
+    ffn_ws = api.workspace(dev.desc, _lib.MOE_WS_FFN)
+    api.expert_ffn(dev.desc, dev.x_perm, dev.expert_off, dev.W1, dev.b1, dev.W2, dev.b2, dev.H, dev.y_perm,
+                   ws=ffn_ws)
+    api.combine(dev.desc, dev.y_perm, dev.row_of, dev.topk_w, dev.y)
     torch.cuda.synchronize()
+    assert_ffn_status_clear(dev, _lib.MOE_WS_FFN, ffn_ws)
     assert torch.equal(dev.row_of, row_of_fwd) and torch.equal(dev.token_of_row[:A], tor_fwd[:A])
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, A - 1], rng.choice(A, size=min(A, 64), replace=False)]))
-    check_x_perm(spec, inp, dev, r, rows)
-    toks = sample_tokens(spec, r)
-    y_ref = O.token_outputs(spec, inp, r, toks)
-    e = row_rel_err(host(dev.y[torch.as_tensor(toks, device=dev.y.device)]), y_ref)
-    say(f"   A={A} sampled {len(toks)} tokens, y err {e:.2e}")
-    assert e <= ROW_TOL[spec.dtype]
+    check_x_perm(spec, inp, dev, r)
+    eh = row_rel_err(host(dev.H[:A]), ref["H"])
+    ey = row_rel_err(host(dev.y_perm[:A]), ref["y_perm"])
+    say(f"   all {A} rows: H error {eh:.2e}, y_perm error {ey:.2e}")
+    assert eh <= ROW_TOL[spec.dtype] and ey <= ROW_TOL[spec.dtype]
+    # the stage calls give moe_forward's bits
+    assert torch.equal(dev.y, y_fwd)
     # every token with all choices dropped has an exactly zero row
     dropped = np.nonzero((r["row_of"].reshape(spec.T, spec.k) < 0).all(axis=1))[0]
     if dropped.size:
@@ -144,6 +166,11 @@ FUSED = {
     "skew16_few_tiles": workloads.MoESpec("skew16_few_tiles", T=3000, d=1024, h=2048, N=16, k=2,
                                           capacity_factor=2.0, gate="softmax", renorm=True, dtype="bf16",
                                           zipf_s=1.5),
+    # rows of H that are not a whole number of 128-byte lines (h * 2 bytes =
+    # 2064): a line holds the end of one row tile's last row and the start of
+    # the next row tile's first row, which a GEMM2 tile must not read stale
+    "zipf16_h1032": workloads.MoESpec("zipf16_h1032", T=8192, d=1024, h=1032, N=16, k=2, capacity_factor=2.0,
+                                      gate="softmax", renorm=True, dtype="bf16", zipf_s=1.5),
 }
 
 
@@ -151,9 +178,13 @@ FUSED = {
 def test_fused_ffn_forward_equals_stages(name):
     spec = FUSED[name]
     inp, dev = run_staged(spec, 11)
+    assert int(api.workspace_size(dev.desc, _lib.MOE_WS_FFN)) > 0, "the shape takes the single launch"
+    assert_ffn_status_clear(dev, _lib.MOE_WS_FFN)
     y_st = dev.y.clone()
     counts = host(dev.expert_count)
     say(f"   expert demand: min {counts.min()} max {counts.max()} zero {(counts == 0).sum()}")
+    # the single launch against the oracle, on every row
+    full_check(spec, inp, dev)
     # the stage call ran the single launch (it had a workspace); the two
     # launches (no workspace) give the same H and y_perm bit for bit
     A = int(host(dev.expert_off)[-1])
@@ -173,12 +204,14 @@ def test_fused_ffn_forward_equals_stages(name):
         api.expert_ffn(dev.desc, dev.x_perm, dev.expert_off, dev.W1, dev.b1, dev.W2, dev.b2, dev.H, dev.y_perm,
                        ws=dev.ws)
         torch.cuda.synchronize()
+        assert_ffn_status_clear(dev, _lib.MOE_WS_FFN)
         assert torch.equal(dev.H[:A], H1) and torch.equal(dev.y_perm[:A], Y1), f"single launch, call {rep}"
     for rep in range(2):
         dev.y.zero_()
         say(f"[case] fused forward {spec.name} call {rep}")
         dev.run_forward(inspect=True)
         torch.cuda.synchronize()
+        assert_ffn_status_clear(dev)
         assert torch.equal(dev.y, y_st)
 
 
@@ -305,6 +338,112 @@ def test_dispatch_with_caller_routing():
     A = int(o[-1])
     assert np.array_equal(host(tor)[:A], t_o_r)
     assert torch.equal(x_perm[:A].view(torch.int16), x[torch.from_numpy(t_o_r // spec.k).cuda()].view(torch.int16))
+
+
+def expected_slots_with_invalid(idx, N, C):
+    """Slots by the counting definition for a caller's routing in which an
+    entry outside [0, N), or a repeat of an earlier expert of the same token,
+    occupies no slot (moe_dispatch's documented treatment)."""
+    T, k = idx.shape
+    valid = np.zeros((T, k), bool)
+    for t in range(T):
+        seen = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            valid[t, j] = 0 <= e < N and e not in seen
+            seen.add(e)
+    fill = np.zeros(N, np.int64)
+    slot = np.full((T, k), -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if valid[t, j]:
+                e = int(idx[t, j])
+                slot[t, j] = fill[e]
+                fill[e] += 1
+    kept = np.minimum(fill, C)
+    off = np.concatenate([[0], np.cumsum(kept)])
+    row_of = np.full(T * k, -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if valid[t, j] and slot[t, j] < C:
+                row_of[t * k + j] = off[int(idx[t, j])] + slot[t, j]
+    return fill, off, row_of
+
+
+def _dispatch_caller(spec, idx, lib_path=_lib.LIB_PATH):
+    desc = api.desc_from_spec(spec)
+    R = api.rows_bound(desc)
+    dv = dict(dtype=torch.int32, device="cuda")
+    x = torch.randn(spec.T, spec.d, device="cuda").to(torch.bfloat16)
+    count, off = torch.empty(spec.N, **dv), torch.empty(spec.N + 1, **dv)
+    row_of, tor = torch.empty(spec.T * spec.k, **dv), torch.full((R,), -1, **dv)
+    x_perm = torch.zeros(R, spec.d, dtype=torch.bfloat16, device="cuda")
+    ws = api.workspace(desc, _lib.MOE_WS_DISPATCH)
+    api.dispatch(desc, x, torch.from_numpy(idx.astype(np.int32)).cuda(), count, off, row_of, tor, x_perm, ws=ws,
+                 lib_path=lib_path)
+    torch.cuda.synchronize()
+    return host(count), host(off), host(row_of), host(tor)
+
+
+def test_dispatch_caller_routing_with_invalid_entries():
+    """A caller's routing with out-of-range entries and repeated experts: the
+    release build drops exactly those choices; the debug build rejects the
+    call with a message naming the entry."""
+    spec = workloads.MoESpec("caller_invalid", T=1500, d=64, h=64, N=12, k=4, capacity_factor=0.8,
+                             gate="softmax", renorm=False, dtype="bf16")
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.choice(spec.N, size=spec.k, replace=False) for _ in range(spec.T)])
+    idx[5, 2] = idx[5, 0]        # a repeat
+    idx[17, 3] = spec.N          # out of range
+    idx[40, 1] = -1
+    idx[99, 1:] = idx[99, 0]     # three repeats
+    idx[rng.choice(spec.T, 50, replace=False), 3] = idx[rng.choice(spec.T, 50, replace=False), 0]
+    C = O.capacity(spec.T, spec.k, spec.N, spec.capacity_factor)
+    say("[case] caller routing with invalid entries (release build)")
+    count, off, row_of, tor = _dispatch_caller(spec, idx)
+    want_count, want_off, want_row = expected_slots_with_invalid(idx, spec.N, C)
+    assert np.array_equal(count, want_count) and np.array_equal(off, want_off)
+    assert np.array_equal(row_of, want_row)
+    A = int(want_off[-1])
+    kept = np.nonzero(want_row >= 0)[0]
+    assert np.array_equal(np.sort(tor[:A]), np.sort(kept)) and np.array_equal(tor[want_row[kept]], kept)
+    say("[case] caller routing with a repeated expert (debug build)")
+    with pytest.raises(RuntimeError, match="token 5 names expert"):
+        _dispatch_caller(spec, idx, _lib.DEBUG_LIB_PATH)
+    ok = np.stack([rng.choice(spec.N, size=spec.k, replace=False) for _ in range(spec.T)])
+    c2, o2, r2, _ = _dispatch_caller(spec, ok, _lib.DEBUG_LIB_PATH)
+    wc, wo, wr = expected_slots_with_invalid(ok, spec.N, C)
+    assert np.array_equal(c2, wc) and np.array_equal(o2, wo) and np.array_equal(r2, wr)
+
+
+def test_dispatch_scan_path_large_T():
+    """Large count tables go through the scan kernel (one block per expert)
+    instead of every rows block summing the table: caller routing over 70,000
+    tokens (274 tiles x 64 experts), then moe_forward with the bf16 noisy gate
+    on 262,144 tokens (8,192 groups of 32 tokens x 8 experts); both against
+    the oracle's slots."""
+    spec = workloads.MoESpec("scan_caller", T=70000, d=64, h=64, N=64, k=2, capacity_factor=1.1,
+                             gate="softmax", renorm=False, dtype="bf16")
+    rng = np.random.default_rng(9)
+    p = 1.0 / np.arange(1, spec.N + 1) ** 0.8
+    p /= p.sum()
+    idx = np.stack([rng.choice(spec.N, size=spec.k, replace=False, p=p) for _ in range(spec.T)])
+    C = O.capacity(spec.T, spec.k, spec.N, spec.capacity_factor)
+    say("[case] dispatch scan path, caller routing T=70000 N=64")
+    count, off, row_of, tor = _dispatch_caller(spec, idx)
+    cnt, kept, o, ro, t_o_r = O.assign_slots(idx, spec.N, C)
+    assert np.array_equal(count, cnt) and np.array_equal(off, o) and np.array_equal(row_of, ro)
+    assert np.array_equal(tor[:int(o[-1])], t_o_r)
+    spec2 = workloads.MoESpec("scan_gate", T=262144, d=64, h=64, N=8, k=2, capacity_factor=1.0,
+                              gate="noisy", renorm=True, dtype="bf16")
+    inp = make_inputs(spec2, 19)
+    dev = api.DeviceLayer(inp)
+    say("[case] dispatch scan path, moe_forward with the noisy gate's counts, T=262144")
+    dev.run_forward(inspect=True)
+    torch.cuda.synchronize()
+    lg = host(dev.logits)
+    r = check_routing(spec2, inp, dev, lg)
+    assert int(r["off"][-1]) < spec2.T * spec2.k  # drops
 
 
 @pytest.mark.parametrize("name", ["noisy_top2_bf16", "decode_top8_bf16"])

@@ -187,18 +187,6 @@ def test_fully_dropped_tokens_output_zero():
     np.testing.assert_allclose(out["y"][kept_tokens], ref, rtol=1e-12, atol=1e-12)
 
 
-def test_sampled_token_outputs_agree_with_full_layer():
-    s = _small("noisy", T=40, N=6, k=3, capacity_factor=0.8, renorm=True)
-    inp = make_inputs(s, seed=14)
-    out = O.forward(s, inp)
-    toks = [0, 3, 17, 39]
-    np.testing.assert_allclose(O.token_outputs(s, inp, out, toks), out["y"][toks], rtol=1e-12, atol=1e-12)
-    rows = [0, 5, int(out["off"][-1]) - 1]
-    H, Y = O.row_outputs(inp, out, rows, s.k)
-    np.testing.assert_allclose(H, out["H"][rows], rtol=1e-12, atol=1e-12)
-    np.testing.assert_allclose(Y, out["y_perm"][rows], rtol=1e-12, atol=1e-12)
-
-
 # ---------------------------------------------------------------- the pages' own code, re-expressed
 
 def test_top1_layer_of_the_pages():
