@@ -234,6 +234,24 @@ typedef struct moe_layer_tensors {
 MOE_API moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* tensors, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same results as moe_forward, with the workspace
+ * taken from a fixed device array inside the library instead of the
+ * caller's. The array holds moe_noalloc_scratch_bytes() bytes (64 MiB) on
+ * each GPU the library's code is loaded on, until the process ends. A layer
+ * whose moe_workspace_size(MOE_WS_FORWARD) exceeds that gets
+ * MOE_ERR_UNSUPPORTED before anything is enqueued (among the standard
+ * shapes: the tiny, noisy top-2 and decode layers fit; the large-expert and
+ * cosine layers do not). The call allocates nothing and frees nothing;
+ * outputs and inspection outputs are the caller's, as for moe_forward.
+ * Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (each call clears what it needs cleared), so calls that overlap in
+ * time on one GPU (other streams, other threads) race: serialise them. */
+MOE_API moe_status_t moe_forward_noalloc(const moe_desc_t* desc, const moe_layer_tensors_t* tensors,
+                                         void* stream);
+MOE_API size_t moe_noalloc_scratch_bytes(void);
+
 /* Block-FP8 expert weights: FP8 weights shrink the model ("MoE架构：突破单卡
  * 算力瓶颈的密钥" §1.3), held with a scale per block ("Block FP8" serving on
  * MI300 in the CUDA-to-ROCm section of "4大技术模块掌握Tutel MoE…").

@@ -55,6 +55,8 @@ SIGNATURES = {
     "moe_combine": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 4 + [c_void_p]),
     "moe_forward": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p, c_size_t, c_void_p]),
     "moe_time_ffn_launches": (c_int, [c_void_p, c_void_p]),
+    "moe_forward_noalloc": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p]),
+    "moe_noalloc_scratch_bytes": (c_size_t, []),
     "moe_ffn_status": (c_int, [POINTER(MoeDesc), c_int, c_void_p, c_size_t, c_void_p, c_void_p]),
     "moe_probe_copy": (c_int, [c_void_p, c_void_p, c_int64, c_void_p]),
     "moe_probe_mfma": (c_int, [c_int32, c_void_p, POINTER(c_int64), c_void_p]),

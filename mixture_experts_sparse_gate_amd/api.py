@@ -163,6 +163,18 @@ def forward(desc, tensors: dict, ws: torch.Tensor, stream=None):
     _check(st, "moe_forward")
 
 
+def forward_noalloc(desc, tensors: dict, stream=None):
+    """moe_forward_noalloc: moe_forward on the library's fixed scratch array
+    (no workspace argument; layers whose workspace exceeds
+    moe_noalloc_scratch_bytes() are rejected)."""
+    unknown = set(tensors) - {f for f, _ in MoeLayerTensors._fields_}
+    if unknown:
+        raise KeyError(f"unknown tensor names {sorted(unknown)}")
+    lt = MoeLayerTensors(**{k: _ptr(v) for k, v in tensors.items() if v is not None})
+    _check(_lib.load().moe_forward_noalloc(ctypes.byref(desc), ctypes.byref(lt), _stream(stream)),
+           "moe_forward_noalloc")
+
+
 FP8_BLOCK = 128
 
 

@@ -7,7 +7,7 @@
 #include <string.h>
 
 #include <atomic>
-
+#include <mutex>
 #include <vector>
 
 #include "moe.h"
@@ -487,6 +487,36 @@ moe_status_t forward_impl(const moe_desc_t* desc, const moe_layer_tensors_t* t, 
   return do_combine(desc, y_perm, row_of, w, t->y, s);
 }
 
+// ---------------------------------------------------------------- no-allocation forward
+
+// moe_forward_noalloc's workspace: a file-scope device array, one copy per
+// GPU (held from when the library's code is loaded on that GPU until the
+// process ends). Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): it uses the device address
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// The scratch array's device address on the current device, fetched once
+// per device (with that device current) and kept.
+moe_status_t scratch_on_current_device(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+
 #ifdef MOE_DEBUG_CHECKS
 // Debug builds: the caller's routing is copied to the host (synchronising
 // the stream) and checked: every index in [0, N), distinct per token.
@@ -597,6 +627,21 @@ moe_status_t moe_forward(const moe_desc_t* desc, const moe_layer_tensors_t* t, v
                          void* stream) {
   return forward_impl(desc, t, nullptr, ws, ws_bytes, stream);
 }
+
+moe_status_t moe_forward_noalloc(const moe_desc_t* desc, const moe_layer_tensors_t* t, void* stream) {
+  TRY(check_desc(desc));
+  const size_t need_bytes = forward_ws(desc).bytes;
+  if (need_bytes > kNoAllocScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_forward_noalloc: the layer needs %zu bytes of workspace, above the %zu-byte scratch array; "
+                "call moe_forward with a workspace instead",
+                need_bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  TRY(scratch_on_current_device(&ws));
+  return forward_impl(desc, t, nullptr, ws, kNoAllocScratchBytes, stream);
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 moe_status_t moe_forward_fp8(const moe_desc_t* desc, const moe_layer_tensors_t* t, const moe_fp8_weights_t* w8,
                              void* ws, size_t ws_bytes, void* stream) {

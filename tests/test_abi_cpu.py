@@ -232,3 +232,14 @@ def test_layers_past_the_32bit_buffer_ranges_are_unsupported(lib, kw):
     n = ctypes.c_size_t()
     assert lib.moe_workspace_size(ctypes.byref(d), _lib.MOE_WS_FORWARD, ctypes.byref(n)) == _lib.MOE_ERR_UNSUPPORTED
     assert b"2^31" in lib.moe_last_error()
+
+
+def test_noalloc_rejects_layers_above_its_scratch_array(lib):
+    """moe_forward_noalloc checks the layer's workspace against its fixed
+    scratch array before any HIP call: the large-expert layer (580 MiB of
+    workspace) is refused with a message; no tensor is touched."""
+    assert lib.moe_noalloc_scratch_bytes() == 64 << 20
+    d = desc_from_spec(workloads.get("large_expert_top2_bf16"))
+    st = lib.moe_forward_noalloc(ctypes.byref(d), ctypes.byref(_lib.MoeLayerTensors()), None)
+    assert st == _lib.MOE_ERR_UNSUPPORTED
+    assert b"scratch array" in lib.moe_last_error()
