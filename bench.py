@@ -114,14 +114,15 @@ def main() -> int:
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
     ap.add_argument("--summarize", default=None, help="rocprofv3 results.db to condense (no GPU)")
-    ap.add_argument("--kind", choices=["stats", "traffic"], default="stats")
+    ap.add_argument("--kind", choices=["stats", "traffic", "pmc"], default="stats")
+    ap.add_argument("--pmc-dbs", nargs="*", default=[], help="with --kind pmc: results.db files of counter passes")
     ap.add_argument("--fetch-db", default=None, help="with --kind traffic: the FETCH_SIZE results.db")
     ap.add_argument("--write-db", default=None, help="with --kind traffic: the WRITE_SIZE results.db")
     ap.add_argument("--command", default="", help="command line recorded in the summary")
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
 
-    if args.summarize or args.kind == "traffic" and args.fetch_db:
+    if args.summarize or args.kind == "traffic" and args.fetch_db or args.kind == "pmc" and args.pmc_dbs:
         return summarize(args)
 
     if args.gpus != 1:
@@ -489,8 +490,43 @@ def _pmc_per_kernel(db, counter):
     return [(d, n, g, v) for d, n, g, v in rows]
 
 
+def _pmc_all(db):
+    """{counter: [(dispatch_id, kernel_name, value summed over the dispatch's instances)]}"""
+    c = sqlite3.connect(db)
+    rows = c.execute("select counter_name, dispatch_id, kernel_name, sum(value) from counters_collection "
+                     "group by counter_name, dispatch_id")
+    out = {}
+    for name, d, k, v in rows:
+        out.setdefault(name, []).append((d, k, v))
+    return out
+
+
 def summarize(args):
     lines = [f"command: {args.command}"] if args.command else []
+    if args.kind == "pmc":
+        # per-dispatch averages of each counter over the expert FFN's launches
+        # (the later half of them: warm steps), from one or more passes
+        lines.append("source: rocprofv3 --pmc passes (one results.db per pass); values per dispatch, "
+                     "mean over the later half of the FFN kernel's dispatches")
+        lines.append(f"workload: {args.workload}")
+        for db in args.pmc_dbs:
+            for name, rows in sorted(_pmc_all(db).items()):
+                sel = [v for d, k, v in rows if "fused_ffn_kernel" in k]
+                kern = "fused_ffn_kernel"
+                if not sel:
+                    sel = [v for d, k, v in rows if "grouped_gemm_kernel" in k and "DF16bfLi" not in k]
+                    kern = "grouped_gemm_kernel (both GEMMs, per launch)"
+                if not sel:
+                    continue
+                steady = sel[len(sel) // 2:]
+                lines.append(f"{name}: {sum(steady) / len(steady):.6g}   [{kern}, {len(steady)} dispatches]")
+        lines.append(f"gemm_source_sha256_16: {gemm_source_hash()}")
+        text = "\n".join(lines) + "\n"
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        print(text)
+        return 0
     if args.kind == "stats":
         lines.append(f"source: rocprofv3 --kernel-trace --stats (top_kernels of {os.path.basename(args.summarize)})")
         lines.append(f"{'kernel':70s} {'calls':>6s} {'total_us':>12s} {'avg_us':>10s} {'%':>7s}")

@@ -206,8 +206,10 @@ def test_fused_ffn_forward_equals_stages(name):
         torch.cuda.synchronize()
         assert_ffn_status_clear(dev, _lib.MOE_WS_FFN)
         assert torch.equal(dev.H[:A], H1) and torch.equal(dev.y_perm[:A], Y1), f"single launch, call {rep}"
+    # moe_forward folds the combine into the same launch (k <= 8): every row
+    # of y is written by it (NaN before the call), bit for bit moe_combine's
     for rep in range(2):
-        dev.y.zero_()
+        dev.y.fill_(float("nan"))
         say(f"[case] fused forward {spec.name} call {rep}")
         dev.run_forward(inspect=True)
         torch.cuda.synchronize()
