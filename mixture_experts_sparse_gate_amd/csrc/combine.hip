@@ -2,8 +2,7 @@
 // (the weighted sum of expert outputs on "MoE架构：突破单卡算力瓶颈的密钥" §1.2).
 //
 // One wave per token. The k rows of y_perm are read with 16-byte loads and
-// accumulated in fp32 in j order (one fma per term), then rounded once; the
-// single-launch FFN's folded combine takes the same sequence. Dropped choices add
+// accumulated in fp32 in j order (one fma per term), then rounded once. Dropped choices add
 // nothing; a token with every choice dropped gets zeros. Row indices outside
 // [0, R) are treated as dropped, so a bad row map cannot read out of bounds.
 // For k <= 8 the wave reads its row indices and weights first and then has

@@ -166,12 +166,29 @@ FUSED = {
     "skew16_few_tiles": workloads.MoESpec("skew16_few_tiles", T=3000, d=1024, h=2048, N=16, k=2,
                                           capacity_factor=2.0, gate="softmax", renorm=True, dtype="bf16",
                                           zipf_s=1.5),
-    # rows of H that are not a whole number of 128-byte lines (h * 2 bytes =
-    # 2064): a line holds the end of one row tile's last row and the start of
-    # the next row tile's first row, which a GEMM2 tile must not read stale
+}
+
+# H rows that are not a whole number of 256-byte lines (h * 2 = 2064 bytes):
+# a line would hold the end of one row tile's last row and the start of the
+# next, so these shapes take the two launches (no GEMM2 tile can then read a
+# line of H before it is complete)
+NOT_FUSED = {
     "zipf16_h1032": workloads.MoESpec("zipf16_h1032", T=8192, d=1024, h=1032, N=16, k=2, capacity_factor=2.0,
                                       gate="softmax", renorm=True, dtype="bf16", zipf_s=1.5),
 }
+
+
+@pytest.mark.parametrize("name", list(NOT_FUSED))
+def test_partial_line_rows_take_two_launches(name):
+    spec = NOT_FUSED[name]
+    inp, dev = run_staged(spec, 11)
+    assert int(api.workspace_size(dev.desc, _lib.MOE_WS_FFN)) == 0, "the shape takes the two launches"
+    full_check(spec, inp, dev)
+    y_st = dev.y.clone()
+    dev.y.fill_(float("nan"))
+    dev.run_forward(inspect=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dev.y, y_st)
 
 
 @pytest.mark.parametrize("name", list(FUSED))
@@ -206,8 +223,6 @@ def test_fused_ffn_forward_equals_stages(name):
         torch.cuda.synchronize()
         assert_ffn_status_clear(dev, _lib.MOE_WS_FFN)
         assert torch.equal(dev.H[:A], H1) and torch.equal(dev.y_perm[:A], Y1), f"single launch, call {rep}"
-    # moe_forward folds the combine into the same launch (k <= 8): every row
-    # of y is written by it (NaN before the call), bit for bit moe_combine's
     for rep in range(2):
         dev.y.fill_(float("nan"))
         say(f"[case] fused forward {spec.name} call {rep}")
