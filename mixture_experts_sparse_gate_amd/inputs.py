@@ -18,6 +18,7 @@ Recipe (every stream is its own PCG64 generator keyed by (seed, tag, expert)):
   tag 7  W2[e]      [h, d]      N(0, 1/h)
   tag 8  b1[e]      [h]         N(0, 0.01)         only when spec.expert_bias
   tag 9  b2[e]      [d]         N(0, 0.01)         only when spec.expert_bias
+  tag 10 dy         [T, d]      N(0, 1)            the upstream gradient of y (make_output_grad)
   logit_bias [N] fp32: 2 * log(Zipf(s) weight of rank e+1), when spec.zipf_s > 0
 
 The second parameter of N(., .) is the variance.
@@ -33,7 +34,7 @@ import numpy as np
 
 from .workloads import MoESpec
 
-TAG_X, TAG_WG, TAG_WN, TAG_EPS, TAG_P, TAG_E, TAG_W1, TAG_W2, TAG_B1, TAG_B2 = range(10)
+TAG_X, TAG_WG, TAG_WN, TAG_EPS, TAG_P, TAG_E, TAG_W1, TAG_W2, TAG_B1, TAG_B2, TAG_DY = range(11)
 
 
 def _rng(seed: int, tag: int, expert: int = 0) -> np.random.Generator:
@@ -133,3 +134,9 @@ def make_inputs(spec: MoESpec, seed: int, with_experts: bool = True) -> MoEInput
         b1 = _normal((N, h), 0.1, seed, TAG_B1, bf16=bf)
         b2 = _normal((N, d), 0.1, seed, TAG_B2, bf16=bf)
     return MoEInputs(spec, seed, x, w_gate, w_noise, noise, proj, emb, bias, W1, W2, b1, b2)
+
+
+def make_output_grad(spec: MoESpec, seed: int) -> np.ndarray:
+    """dy [T, d]: the gradient a following layer hands back for y (float32;
+    bf16-exact for bf16 workloads)."""
+    return _normal((spec.T, spec.d), 1.0, seed, TAG_DY, bf16=spec.dtype == "bf16")
