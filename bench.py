@@ -66,7 +66,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, MI355X published figures
 
 
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_sparse_gate_amd", "csrc", "gemm.hip")
+GEMM_SRCS = [os.path.join(ROOT, "mixture_experts_sparse_gate_amd", "csrc", f) for f in ("gemm.hip", "gelu.hpp")]
 
 
 def log(*a):
@@ -74,8 +74,12 @@ def log(*a):
 
 
 def gemm_source_hash() -> str:
-    with open(GEMM_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the expert FFN kernel's sources (the tile code and its GELU)."""
+    h = hashlib.sha256()
+    for path in GEMM_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_path(workload: str) -> str:
@@ -271,6 +275,35 @@ def main() -> int:
         api.time_ffn_launches(None, None)
     ffn_kernel_ms = float(np.mean(ffn_kernel_ms))
 
+    # ---- the backward pass (bf16 layers with the plain or noisy gate) on
+    # the routing of a forward call with inspection outputs
+    backward = None
+    if not args.skip_extras and spec.dtype == "bf16" and spec.gate != "cosine" and not fp8:
+        from mixture_experts_sparse_gate_amd.inputs import make_output_grad
+        dy = torch.from_numpy(make_output_grad(spec, seed)).cuda().to(torch.bfloat16)
+        dev.run_forward(inspect=True)
+        dev.backward_buffers()
+        for _ in range(2):
+            dev.run_backward(dy)
+        reps = max(3, min(K, 20))
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record(stream)
+        for _ in range(reps):
+            dev.run_backward(dy)
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / reps
+        A_b = int(dev.expert_off[-1].item())
+        # five grouped GEMMs of 2 A d h flops each: U (recomputed), dU,
+        # dx rows, dW1, dW2
+        bwd_flops = 10.0 * A_b * spec.d * spec.h
+        backward = {"ms": bwd_ms, "tokens_per_s": spec.T / (bwd_ms * 1e-3), "flops": bwd_flops,
+                    "TFLOP/s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+                    "frac_of_bf16_peak": bwd_flops / (bwd_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"],
+                    "reps": reps}
+        del dev.grads, dev.ws_bwd
+        dev.grads = None
+
     # ---- the chip's measured ceilings, in this run
     peaks = None if args.skip_extras else measured_peaks(api, torch, stream)
 
@@ -383,6 +416,7 @@ def main() -> int:
         "graph_ms_per_step": graph_ms,
         "cold": cold_ms,
         "measured_peaks": peaks,
+        "backward": backward,
     }
     print(json.dumps(out), flush=True)
     return 0

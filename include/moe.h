@@ -105,7 +105,8 @@ typedef enum moe_ws_kind {
   MOE_WS_DISPATCH = 1,
   MOE_WS_FORWARD = 2,
   MOE_WS_FFN = 3,
-  MOE_WS_AUX = 4
+  MOE_WS_AUX = 4,
+  MOE_WS_BACKWARD = 5
 } moe_ws_kind_t;
 
 /* Expert capacity C = min(T, ceil((capacity_factor * (T*k)) / N)), evaluated
@@ -329,6 +330,66 @@ MOE_API moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_id
  * capture this call after it. */
 MOE_API moe_status_t moe_ffn_status(const moe_desc_t* desc, moe_ws_kind_t kind, const void* ws, size_t ws_bytes,
                                     int32_t* status, void* stream);
+
+/* Tensors of one backward call: the layer's inputs, the routing its forward
+ * call produced (moe_forward's inspection outputs), the gradient dy of the
+ * output, and the gradients to write. */
+typedef struct moe_backward_tensors {
+  /* inputs, as for moe_forward (logit_bias is not needed: its gradient does
+     not depend on it) */
+  const void* x;
+  const void* w_gate;
+  const void* w_noise;       /* NOISY */
+  const float* noise;        /* NOISY */
+  const void* W1;
+  const void* b1;            /* or NULL */
+  const void* W2;
+  const void* b2;            /* or NULL */
+  /* the forward's routing */
+  const float* logits;       /* [T, N] (read when renorm = 0) */
+  const int32_t* topk_idx;   /* [T, k] */
+  const float* topk_w;       /* [T, k] */
+  const int32_t* expert_off; /* [N+1] */
+  const int32_t* row_of;     /* [T*k] */
+  const int32_t* token_of_row; /* [R] */
+  const void* dy;            /* [T, d] X-dtype: dL/dy */
+  /* outputs */
+  void* dx;                  /* [T, d] X-dtype */
+  float* dW1;                /* [N, d, h] */
+  float* dW2;                /* [N, h, d] */
+  float* db1;                /* [N, h] or NULL (not computed) */
+  float* db2;                /* [N, d] or NULL */
+  float* dw_gate;            /* [d, N] */
+  float* dw_noise;           /* [d, N] (NOISY) */
+  float* dlogit_bias;        /* [N] or NULL */
+} moe_backward_tensors_t;
+
+/* Backward pass of the layer: the gradients of
+ *   L = sum(dy * y) + aux_coef[0] * load_balance_loss + aux_coef[1] * importance_loss
+ * (the two losses of moe_aux_loss, on the importance of the same routing)
+ * with respect to x, W1, b1, W2, b2, w_gate, w_noise and logit_bias, the
+ * routing held fixed: gradients flow only through the selected experts' gate
+ * weights and outputs ("MoE稀疏计算加速技术解析与应用实践" §2.1: sparse gating
+ * keeps only the Top-K experts' gradient; the auxiliary losses are added to
+ * the total loss on its §4.1 and on "MoE架构：突破单卡算力瓶颈的密钥" §3.1). A
+ * choice dropped by the capacity limit contributes nothing to y, so its
+ * weight gets no gradient from y, but it still counts in the importance.
+ * The noise tensor is an input, not a parameter.
+ * Per kept row (token t, choice j, expert e, weight w): the expert's
+ * pre-activation U = x W1_e + b1_e and H = GELU(U) are recomputed (bf16);
+ * dU = bf16(w (dy_t W2_e^T) GELU'(U)); the weight's gradient is
+ * (dy_t W2_e^T) . H (+ dy_t . b2_e); dW2_e = sum H^T bf16(w dy_t),
+ * dW1_e = sum x^T dU, dx = sum over kept j of dU W1_e^T plus the gate's
+ * part (through the softmax over the selected logits, renorm = 1, or over
+ * all logits, renorm = 0; through softplus for the noisy gate). All
+ * products on bf16 MFMA with fp32 accumulation; every reduction in a fixed
+ * order (repeated calls give the same bits).
+ * bf16 layers with the SOFTMAX or NOISY gate; others get MOE_ERR_UNSUPPORTED,
+ * as do layers with R * max(d, h) * 2 bytes at or above 2^31 (R = the row
+ * bound). aux_coef: two host floats, or NULL for none.
+ * ws: MOE_WS_BACKWARD bytes. */
+MOE_API moe_status_t moe_backward(const moe_desc_t* desc, const moe_backward_tensors_t* tensors,
+                                  const float* aux_coef, void* ws, size_t ws_bytes, void* stream);
 
 /* Profiling aid. While set, the expert FFN's kernel launches (in
  * moe_expert_ffn and moe_forward) record start_event (a hipEvent_t) when the

@@ -13,7 +13,7 @@ DEBUG_LIB_PATH = os.path.join(HERE, "libmoe_gfx950_debug.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_NOISY, MOE_GATE_COSINE = 0, 1, 2
-MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_FORWARD, MOE_WS_FFN, MOE_WS_AUX = 0, 1, 2, 3, 4
+MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_FORWARD, MOE_WS_FFN, MOE_WS_AUX, MOE_WS_BACKWARD = 0, 1, 2, 3, 4, 5
 
 
 class MoeDesc(ctypes.Structure):
@@ -40,6 +40,13 @@ class MoeLayerTensors(ctypes.Structure):
         "logits", "topk_idx", "topk_w", "expert_count", "expert_off", "row_of", "token_of_row")]
 
 
+class MoeBackwardTensors(ctypes.Structure):
+    _fields_ = [(name, c_void_p) for name in (
+        "x", "w_gate", "w_noise", "noise", "W1", "b1", "W2", "b2",
+        "logits", "topk_idx", "topk_w", "expert_off", "row_of", "token_of_row", "dy",
+        "dx", "dW1", "dW2", "db1", "db2", "dw_gate", "dw_noise", "dlogit_bias")]
+
+
 class MoeFp8Weights(ctypes.Structure):
     _fields_ = [(name, c_void_p) for name in ("W1q", "S1", "W2q", "S2")]
 
@@ -55,6 +62,7 @@ SIGNATURES = {
     "moe_combine": (c_int, [POINTER(MoeDesc)] + [c_void_p] * 4 + [c_void_p]),
     "moe_forward": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p, c_size_t, c_void_p]),
     "moe_time_ffn_launches": (c_int, [c_void_p, c_void_p]),
+    "moe_backward": (c_int, [POINTER(MoeDesc), POINTER(MoeBackwardTensors), c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_forward_noalloc": (c_int, [POINTER(MoeDesc), POINTER(MoeLayerTensors), c_void_p]),
     "moe_noalloc_scratch_bytes": (c_size_t, []),
     "moe_ffn_status": (c_int, [POINTER(MoeDesc), c_int, c_void_p, c_size_t, c_void_p, c_void_p]),

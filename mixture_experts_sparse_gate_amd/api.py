@@ -15,7 +15,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import MoeDesc, MoeFp8Weights, MoeLayerTensors
+from ._lib import MoeBackwardTensors, MoeDesc, MoeFp8Weights, MoeLayerTensors
 from .workloads import MoESpec
 
 _GATES = {"softmax": _lib.MOE_GATE_SOFTMAX, "noisy": _lib.MOE_GATE_NOISY, "cosine": _lib.MOE_GATE_COSINE}
@@ -163,6 +163,20 @@ def forward(desc, tensors: dict, ws: torch.Tensor, stream=None):
     _check(st, "moe_forward")
 
 
+def backward(desc, tensors: dict, ws: torch.Tensor, aux_coef=None, stream=None):
+    """moe_backward; tensors: the fields of moe_backward_tensors_t by name
+    (missing = NULL); aux_coef: the two load-balance losses' coefficients."""
+    unknown = set(tensors) - {f for f, _ in MoeBackwardTensors._fields_}
+    if unknown:
+        raise KeyError(f"unknown tensor names {sorted(unknown)}")
+    bt = MoeBackwardTensors(**{k: _ptr(v) for k, v in tensors.items() if v is not None})
+    coef = None if aux_coef is None else (ctypes.c_float * 2)(*[float(c) for c in aux_coef])
+    st = _lib.load().moe_backward(ctypes.byref(desc), ctypes.byref(bt),
+                                  None if coef is None else ctypes.cast(coef, ctypes.c_void_p), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_backward")
+
+
 def forward_noalloc(desc, tensors: dict, stream=None):
     """moe_forward_noalloc: moe_forward on the library's fixed scratch array
     (no workspace argument; layers whose workspace exceeds
@@ -285,6 +299,33 @@ class DeviceLayer:
 
     def run_forward(self, inspect: bool = True, stream=None):
         forward(self.desc, self.layer_tensors(inspect), self.ws, stream=stream)
+
+    def backward_buffers(self, device="cuda"):
+        """Gradient outputs of moe_backward (fp32 weight gradients) and its workspace."""
+        spec, dt = self.spec, TORCH_DTYPE[self.spec.dtype]
+        f32 = dict(dtype=torch.float32, device=device)
+        N, d, h = spec.N, spec.d, spec.h
+        self.grads = dict(
+            dx=torch.empty(spec.T, d, dtype=dt, device=device),
+            dW1=torch.empty(N, d, h, **f32), dW2=torch.empty(N, h, d, **f32),
+            db1=torch.empty(N, h, **f32) if self.b1 is not None else None,
+            db2=torch.empty(N, d, **f32) if self.b2 is not None else None,
+            dw_gate=torch.empty(d, N, **f32),
+            dw_noise=torch.empty(d, N, **f32) if self.w_noise is not None else None,
+            dlogit_bias=torch.empty(N, **f32) if self.logit_bias is not None else None)
+        self.ws_bwd = workspace(self.desc, _lib.MOE_WS_BACKWARD, device)
+        return self.grads
+
+    def run_backward(self, dy, aux_coef=None, stream=None):
+        """moe_backward on the routing the last inspected forward call left in
+        this object's buffers; gradients land in self.grads."""
+        if getattr(self, "grads", None) is None:
+            self.backward_buffers(dy.device)
+        t = dict(x=self.x, w_gate=self.w_gate, w_noise=self.w_noise, noise=self.noise, W1=self.W1, b1=self.b1,
+                 W2=self.W2, b2=self.b2, logits=self.logits, topk_idx=self.topk_idx, topk_w=self.topk_w,
+                 expert_off=self.expert_off, row_of=self.row_of, token_of_row=self.token_of_row, dy=dy)
+        t.update(self.grads)
+        backward(self.desc, t, self.ws_bwd, aux_coef, stream=stream)
 
     def quantize_weights_fp8(self, stream=None):
         """Block-FP8 copies of W1 and W2 (moe_quantize_fp8), kept as self.w8."""

@@ -27,7 +27,8 @@ LIB_NAME = "libmoe_gfx950.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["gate.hip", "dispatch.hip", "gemm.hip", "combine.hip", "aux.hip", "quant.hip", "probe.hip", "capi.hip"]
+SOURCES = ["gate.hip", "dispatch.hip", "gemm.hip", "combine.hip", "aux.hip", "quant.hip", "probe.hip", "backward.hip",
+           "capi.hip"]
 HOST_SOURCES = ["routing_check.cpp"]
 DEBUG_LIB_NAME = "libmoe_gfx950_debug.so"
 DEBUG_LIB_PATH = os.path.join(HERE, DEBUG_LIB_NAME)

@@ -1,0 +1,680 @@
+// Backward pass of the MoE layer (bf16 layers; plain and noisy gates).
+//
+// The gradients of L = sum(dy * y) (+ the load-balance losses) with the
+// routing held fixed: gradients flow only through the selected experts'
+// gate weights and outputs (sparse gating keeps only the Top-K experts'
+// gradient, "MoE稀疏计算加速技术解析与应用实践" §2.1; the auxiliary losses join
+// the total loss on the same page's §4.1 and on "MoE架构：突破单卡算力瓶颈的
+// 密钥" §3.1). Per kept row r of expert e (token t, choice j, weight w):
+//   U = x_perm W1_e + b1_e, H = GELU(U)                 (recomputed)
+//   G = dy_t W2_e^T,  dU = w G GELU'(U),  g_tj = G . H (+ dy_t . b2_e)
+//   dY = w dy_t, dW2_e = sum H^T dY, dW1_e = sum x^T dU, dx_perm = dU W1_e^T
+// and per token: the gate weights' gradients g through the softmax to the
+// logits, through the gate to x, w_gate and w_noise.
+//
+// Kernels:
+//   bwd_gemm_kernel    grouped bf16 MFMA GEMM, 128 x 128 tiles of four waves,
+//                      four LDS stages filled by direct-to-LDS loads. Either
+//                      operand may hold K contiguous (rows of K) or K strided
+//                      (rows of M or N): K-contiguous fragments are plain
+//                      16-byte LDS reads, K-strided ones gfx950's transposing
+//                      LDS reads. Ragged M (groups of output rows, the data
+//                      gradients) or ragged K (groups of contraction rows, the
+//                      weight gradients, one [M, N] output per group).
+//   scale_rows_kernel  dY rows: bf16(w * dy_t) into each kept row of t
+//   bwd_token_kernel   one block per token: gate-weight gradients (partial
+//                      dots in a fixed order), softmax and softplus backward,
+//                      dx = sum of the token's dx_perm rows + the gate's part
+//   gate_grad_kernels  dW_g = x^T dl, dW_n = x^T dz, d logit_bias: per
+//                      256-token partial sums, then added in chunk order
+//   colsum_kernel      db1, db2: per expert column sums in row order
+// Every reduction runs in a fixed order; no floating-point atomics.
+#include "common.hpp"
+#include "gelu.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTile = 128;     // output tile rows and columns
+constexpr int kBK = 32;        // K per step
+constexpr int kThreads = 256;  // 2 x 2 waves of 64 x 64
+constexpr int kStages = 4;
+constexpr int kOpBytes = 8192;  // one operand's tile of one stage, either layout
+constexpr int kLoads = kOpBytes / 16 / kThreads;  // 16-byte loads per thread per operand and stage
+constexpr int kNumXcd = 8;
+
+// 16-byte chunk swizzles (gfx950 LDS: 64 banks of 4 bytes): rows of 4 chunks
+// (K-contiguous tiles, 64-byte rows) and rows of 16 chunks (K-strided tiles,
+// 256-byte rows), each making its fragment reads conflict-free
+__device__ inline int swz_rows4(int r) { return (r >> 2) & 3; }
+__device__ inline int swz_rows16(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)); }
+
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_void* dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
+}
+
+template <int N>
+__device__ inline void wait_loads_and_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+template <BwdLayout L> struct Operand;
+
+// Tile of 128 rows (of M or N) x 32 K, K contiguous: row x at byte
+// x * 64, chunk c of it at position c ^ swz_rows4(x).
+template <> struct Operand<BwdLayout::kKContig> {
+  // slot i of this thread: row and global chunk
+  __device__ static void slot(int s, int& row, int& chunk) {
+    row = s >> 2;
+    chunk = (s & 3) ^ swz_rows4(row);
+  }
+  // the lane's fragment (8 consecutive K of row base + 32 f + lane % 32, K
+  // half lane / 32 of substep ss)
+  __device__ static u32x4 frag(const char* st, int base, int f, int ss, int lane) {
+    const int x = base + 32 * f + (lane & 31);
+    const int c = 2 * ss + (lane >> 5);
+    return *(lds_u32x4*)(st + x * 64 + ((c ^ swz_rows4(x)) * 16));
+  }
+};
+
+// Tile of 32 K x 128 columns (of M or N), K strided: K row k at byte
+// k * 256, chunk c of it at position c ^ swz_rows16(k). Fragments by
+// transposing reads: in each 16-lane group q, lane r reads the 4 values of
+// K row 8 (q / 2) + r / 4 (+ 4 for the second read, + 16 ss) at columns
+// 32 f + 16 (q % 2) + 4 (r % 4) .. + 3, and the hardware hands each lane 8
+// consecutive K values of one column.
+template <> struct Operand<BwdLayout::kKStrided> {
+  __device__ static void slot(int s, int& row, int& chunk) {
+    row = s >> 4;
+    chunk = (s & 15) ^ swz_rows16(row);
+  }
+  __device__ static u32x4 frag(const char* st, int base, int f, int ss, int lane) {
+    const int q = lane >> 4, r = lane & 15;
+    const int chunk = (base + 32 * f) / 8 + 2 * (q & 1) + ((r & 3) >> 1);
+    const int krow = 8 * (q >> 1) + (r >> 2);
+    const char* p = st + krow * 256 + ((chunk ^ swz_rows16(r >> 2)) * 16) + 8 * (r & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss) * 256));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss + 4) * 256));
+    const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+    return u32x4{a[0], a[1], b[0], b[1]};
+  }
+};
+
+// Ragged-M schedule: the block's (group, first row, end row, column tile)
+// from seg, over row tiles of all groups (column tiles outermost), XCD by
+// XCD in contiguous stretches. Returns false for blocks past the last tile.
+__device__ bool schedule_ragged_m(const BwdGemmParams& p, int* sched) {
+  __shared__ int s_sched[4];
+  const int lane = lane_id();
+  if (threadIdx.x < kWave) {
+    constexpr int GPL = 4;  // groups per lane (<= 256 groups)
+    int lo[GPL], hi[GPL], nt[GPL], sum = 0;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      const int g = lane * GPL + i;
+      lo[i] = hi[i] = 0;
+      if (g < p.groups) {
+        lo[i] = min(max(p.seg[g], 0), p.M);
+        hi[i] = min(max(p.seg[g + 1], lo[i]), p.M);
+      }
+      nt[i] = (hi[i] - lo[i] + kTile - 1) / kTile;
+      sum += nt[i];
+    }
+    int inc = sum;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+      const int o = __shfl_up(inc, m, kWave);
+      if (lane >= m) inc += o;
+    }
+    const int rows_total = __shfl(inc, kWave - 1, kWave);
+    const int NT = (p.N + kTile - 1) / kTile;
+    const int tiles = rows_total * NT;
+    const int per = (tiles + kNumXcd - 1) / kNumXcd;
+    const int b = blockIdx.x;
+    const int tile = (b % kNumXcd) * per + b / kNumXcd;
+    const bool live = b / kNumXcd < per && tile < tiles;
+    if (lane == 0) s_sched[0] = -1;
+    const int q = live ? tile % rows_total : -1, col = live ? tile / rows_total : 0;
+    int start = inc - sum;
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+      if (live && q >= start && q < start + nt[i]) {
+        s_sched[0] = lane * GPL + i;
+        s_sched[1] = lo[i] + (q - start) * kTile;
+        s_sched[2] = hi[i];
+        s_sched[3] = col * kTile;
+      }
+      start += nt[i];
+    }
+  }
+  __syncthreads();
+  for (int i = 0; i < 4; ++i) sched[i] = __builtin_amdgcn_readfirstlane(s_sched[i]);
+  if (sched[0] >= 0) sched[2] = min(sched[2], sched[1] + kTile);
+  return sched[0] >= 0;
+}
+
+template <BwdLayout LA, BwdLayout LB, BwdEpi EPI, typename O, bool RAGGED_K>
+__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
+  // one LDS object per stage (A tile, then B tile), so that the compiler
+  // can tell the stage being filled from the one being read
+  __shared__ __attribute__((aligned(1024))) char st0[2 * kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char st2[2 * kOpBytes];
+  __shared__ __attribute__((aligned(1024))) char st3[2 * kOpBytes];
+  __shared__ float s_dot[2][kTile];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- the tile: group g, output rows [m0, m1) (ragged M: rows of the
+  // concatenated groups; ragged K: rows of the group's own output), columns
+  // from n0, contraction rows [k_lo, k_hi)
+  int g, m0, m1, n0, k_lo, k_hi;
+  if constexpr (RAGGED_K) {
+    const int MT = (p.M + kTile - 1) / kTile, NT = (p.N + kTile - 1) / kTile;
+    const int tiles = p.groups * MT * NT, per = (tiles + kNumXcd - 1) / kNumXcd;
+    const int b = blockIdx.x, tile = (b % kNumXcd) * per + b / kNumXcd;
+    if (b / kNumXcd >= per || tile >= tiles) return;
+    g = tile / (MT * NT);
+    const int rem = tile % (MT * NT);
+    m0 = (rem % MT) * kTile;  // row tiles fastest: consecutive blocks share the B panel
+    n0 = (rem / MT) * kTile;
+    m1 = min(m0 + kTile, p.M);
+    k_lo = min(max(p.seg[g], 0), p.a_rows);
+    k_hi = min(max(p.seg[g + 1], k_lo), p.a_rows);
+  } else {
+    int sc[4];
+    if (!schedule_ragged_m(p, sc)) return;
+    g = sc[0], m0 = sc[1], m1 = sc[2], n0 = sc[3];
+    k_lo = 0;
+    k_hi = p.K;
+  }
+  const int K = k_hi - k_lo;
+
+  // ---- operand addressing: byte offsets of this thread's 16-byte loads,
+  // fixed over K except for the K position, which each step adds
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)p.a_bytes);
+  const char* Bg = static_cast<const char*>(p.B) + (int64_t)g * p.strideB * 2;
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (uint32_t)p.b_bytes);
+  int a_base[kLoads], a_kc[kLoads], b_base[kLoads], b_kc[kLoads];
+  bool a_ok[kLoads], b_ok[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int s = i * kThreads + tid;
+    int row, chunk;
+    Operand<LA>::slot(s, row, chunk);
+    if constexpr (LA == BwdLayout::kKContig) {
+      // row m0 + row of A (gathered: A row gather[m] / gather_div)
+      const int m = m0 + row;
+      a_ok[i] = m < m1;
+      const int arow = p.gather ? (a_ok[i] ? p.gather[m] / p.gather_div : 0) : m;
+      a_base[i] = (int)(((int64_t)arow * p.lda + chunk * 8) * 2);
+      a_kc[i] = chunk * 8;  // K offset of the chunk
+    } else {
+      // K row k_lo + row (+ k0), columns m0 + 8 chunk
+      a_ok[i] = true;
+      a_base[i] = (int)(((int64_t)(k_lo + row) * p.lda + m0 + chunk * 8) * 2);
+      a_kc[i] = row;  // K offset of the row
+    }
+    Operand<LB>::slot(s, row, chunk);
+    if constexpr (LB == BwdLayout::kKContig) {
+      const int n = n0 + row;
+      b_ok[i] = n < p.N;
+      b_base[i] = (int)(((int64_t)n * p.ldb + chunk * 8) * 2);
+      b_kc[i] = chunk * 8;
+    } else {
+      b_ok[i] = true;
+      b_base[i] = (int)(((int64_t)(k_lo + row) * p.ldb + n0 + chunk * 8) * 2);
+      b_kc[i] = row;
+    }
+  }
+  // loads of K step kt into a stage: a load whose K position lies past K
+  // reads zeros (an offset past every range)
+  auto issue = [&](char* st, int kt) {
+    const int k0 = kt * kBK;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const bool ok = a_ok[i] && k0 + a_kc[i] < K;
+      const int off = LA == BwdLayout::kKContig ? a_base[i] + k0 * 2 : a_base[i] + (int)((int64_t)k0 * p.lda * 2);
+      lds_dma16(ra, (lds_void*)(st + (i * kThreads + wave * kWave) * 16), ok ? off : (int)kOutOfRange);
+    }
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const bool ok = b_ok[i] && k0 + b_kc[i] < K;
+      const int off = LB == BwdLayout::kKContig ? b_base[i] + k0 * 2 : b_base[i] + (int)((int64_t)k0 * p.ldb * 2);
+      lds_dma16(rb, (lds_void*)(st + kOpBytes + (i * kThreads + wave * kWave) * 16), ok ? off : (int)kOutOfRange);
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const char* st) {
+    u32x4 fa[2][2], fb[2][2];  // [substep][fragment]: B (columns n), A (rows m)
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        fb[ss][f] = Operand<LB>::frag(st + kOpBytes, wn * 64, f, ss, lane);
+        fa[ss][f] = Operand<LA>::frag(st, wm * 64, f, ss, lane);
+      }
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[ss][i]),
+                                                               __builtin_bit_cast(bf16x8, fa[ss][j]), acc[i][j], 0,
+                                                               0, 0);
+  };
+
+  // ---- four stages, one barrier per step, loads three steps ahead
+  const int nk = (K + kBK - 1) / kBK;
+  issue(st0, 0);
+  issue(st1, 1);
+  issue(st2, 2);
+  auto step = [&](char* cur, char* nxt, int kt) {
+    wait_loads_and_lds<4 * kLoads>();  // this step's loads have landed; the previous stage is read
+    __syncthreads();
+    issue(nxt, kt + 3);
+    compute(cur);
+  };
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    step(st0, st3, kt);
+    step(st1, st0, kt + 1);
+    step(st2, st1, kt + 2);
+    step(st3, st2, kt + 3);
+  }
+  if (kt < nk) step(st0, st3, kt);
+  if (kt + 1 < nk) step(st1, st0, kt + 1);
+  if (kt + 2 < nk) step(st2, st1, kt + 2);
+  wait_loads_and_lds<0>();
+
+  // ---- epilogue: the lane holds D[n][m] for rows m = m0 + 64 wm + 32 j +
+  // lane % 32 and columns n = n0 + 64 wn + 32 i + 8 q + 4 (lane / 32) + 0..3
+  const int mrow = m0 + wm * 64 + (lane & 31);
+  const int ncol = n0 + wn * 64 + 4 * (lane >> 5);
+  const int64_t cbase = RAGGED_K ? (int64_t)g * p.strideC : 0;
+  float dot[2] = {0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = mrow + 32 * j;
+    const bool row_ok = m < m1;
+    float w = 0.f;
+    if constexpr (EPI == BwdEpi::kGeluGrad) w = row_ok ? p.row_w[p.tor[m]] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = ncol + 32 * i + 8 * q;
+        if (!row_ok || n >= p.N) continue;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+        const int64_t at = cbase + (int64_t)m * p.ldc + n;
+        if constexpr (EPI == BwdEpi::kPlain) {
+          if constexpr (std::is_same_v<O, float>)
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.C) + at) = f32x4{v[0], v[1], v[2], v[3]};
+          else
+            Store<bf16>::four(static_cast<bf16*>(p.C) + at, v[0], v[1], v[2], v[3]);
+        } else if constexpr (EPI == BwdEpi::kDualGelu) {
+          if (p.bias) {
+            const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.bias) +
+                                                             (int64_t)g * p.N + n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] += chunk_elem<bf16>(u32x4{bb[0], bb[1], 0u, 0u}, r);
+          }
+          Store<bf16>::four(static_cast<bf16*>(p.C) + at, v[0], v[1], v[2], v[3]);
+          Store<bf16>::four(static_cast<bf16*>(p.C2) + at, gelu_erf_bf16(v[0]), gelu_erf_bf16(v[1]),
+                            gelu_erf_bf16(v[2]), gelu_erf_bf16(v[3]));
+        } else {
+          // G = dy W2^T: dU = bf16(w G GELU'(U)); the row's dot G . H
+          const u32x2 uu = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.U) + at);
+          const u32x2 hh = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.H) + at);
+          float du[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float u = chunk_elem<bf16>(u32x4{uu[0], uu[1], 0u, 0u}, r);
+            const float h = chunk_elem<bf16>(u32x4{hh[0], hh[1], 0u, 0u}, r);
+            du[r] = w * v[r] * gelu_grad(u);
+            dot[j] = fmaf(v[r], h, dot[j]);
+          }
+          Store<bf16>::four(static_cast<bf16*>(p.C) + at, du[0], du[1], du[2], du[3]);
+        }
+      }
+  }
+  if constexpr (EPI == BwdEpi::kGeluGrad) {
+    // the row's dot over the tile's 128 columns, in a fixed order: the lane
+    // pair (lane, lane + 32), then wave column 0 before wave column 1
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dot[j] += __shfl_xor(dot[j], 32, kWave);
+    if (lane < 32)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) s_dot[wn][wm * 64 + 32 * j + lane] = dot[j];
+    __syncthreads();
+    const int NTc = (p.N + kTile - 1) / kTile;
+    if (tid < kTile && m0 + tid < m1)
+      p.pd[(int64_t)(m0 + tid) * NTc + n0 / kTile] = s_dot[0][tid] + s_dot[1][tid];
+  }
+}
+
+// dY rows: for each kept choice (t, j), row row_of[t k + j] = bf16(w_tj dy_t);
+// one wave per token, dy_t read once
+__global__ __launch_bounds__(256) void scale_rows_kernel(const bf16* dy, const int32_t* row_of, const float* w,
+                                                         bf16* out, int T, int d, int k) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  for (int c0 = 0; c0 < d / 8; c0 += kWave) {
+    const int c = c0 + lane;
+    if (c >= d / 8) break;
+    const u32x4 v = load16(dy + (int64_t)t * d + c * 8);
+    for (int j = 0; j < k; ++j) {
+      const int r = row_of[(int64_t)t * k + j];
+      if (r < 0) continue;
+      const float wj = w[(int64_t)t * k + j];
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = f32_to_bf16_bits(wj * chunk_elem<bf16>(v, 2 * i)) |
+               (f32_to_bf16_bits(wj * chunk_elem<bf16>(v, 2 * i + 1)) << 16);
+      store16(out + (int64_t)r * d + c * 8, o);
+    }
+  }
+}
+
+// d(aux_coef[0] * load_balance_loss + aux_coef[1] * importance_loss) / d
+// importance (one wave; N <= 256): 2 (imp - mean) and 0.1 (imp - mean) /
+// ((N - 1) std), the latter 0 where std is 0. Sums in a fixed order.
+__global__ __launch_bounds__(64) void importance_grad_kernel(const float* imp, float* dimp, int N, float c0,
+                                                             float c1) {
+  __shared__ float s_mean, s_std;
+  const int lane = lane_id();
+  if (lane == 0) {
+    float sum = 0.f;
+    for (int e = 0; e < N; ++e) sum += imp[e];
+    const float mean = sum / (float)N;
+    float ss = 0.f;
+    for (int e = 0; e < N; ++e) ss += (imp[e] - mean) * (imp[e] - mean);
+    s_mean = mean;
+    s_std = N > 1 ? sqrtf(ss / (float)(N - 1)) : 0.f;
+  }
+  __syncthreads();
+  for (int e = lane; e < N; e += kWave) {
+    const float dev = imp[e] - s_mean;
+    float gr = c0 * 2.f * dev;
+    if (c1 != 0.f && s_std > 0.f) gr += c1 * 0.1f * dev / ((float)(N - 1) * s_std);
+    dimp[e] = gr;
+  }
+}
+
+constexpr int kTokThreads = 256;
+
+// a fixed-order block sum of one value per thread (tree over LDS)
+__device__ float block_sum(float v, float* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int s = kTokThreads / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+    __syncthreads();
+  }
+  const float out = red[0];
+  __syncthreads();
+  return out;
+}
+
+// One block per token t: the gate weights' gradients g_tj, the logits'
+// gradient dl[t] (softmax backward), for the noisy gate dz[t] = dl eps
+// sigmoid(x W_n), and dx[t] = sum over kept j of dx_perm[row] (j order) +
+// dl W_g^T + dz W_n^T.
+__global__ __launch_bounds__(kTokThreads) void bwd_token_kernel(BwdTokenParams p) {
+  __shared__ float red[kTokThreads];
+  __shared__ float s_g[32], s_w[32];
+  __shared__ int s_e[32], s_row[32];
+  __shared__ float s_dl[kMaxExperts], s_dz[kMaxExperts];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int k = p.k, N = p.N, d = p.d;
+  if (tid < k) {
+    const int64_t i = (int64_t)t * k + tid;
+    s_e[tid] = p.topk_idx[i];
+    s_w[tid] = p.topk_w[i];
+    const int r = p.row_of[i];
+    s_row[tid] = r;
+    float gsum = 0.f;
+    if (r >= 0)
+      for (int c = 0; c < p.ntc; ++c) gsum += p.pd[(int64_t)r * p.ntc + c];
+    s_g[tid] = gsum;
+  }
+  __syncthreads();
+  if (p.b2) {
+    // + dy_t . b2_e for each kept choice
+    for (int j = 0; j < k; ++j) {
+      if (s_row[j] < 0) continue;  // block-uniform
+      float part = 0.f;
+      const bf16* b = p.b2 + (int64_t)s_e[j] * d;
+      for (int i = tid; i < d; i += kTokThreads) part += (float)p.dy[(int64_t)t * d + i] * (float)b[i];
+      const float s = block_sum(part, red);
+      if (tid == 0) s_g[j] += s;
+      __syncthreads();
+    }
+  }
+  if (tid < k && p.dimp) s_g[tid] += p.dimp[s_e[tid]];
+  __syncthreads();
+  // softmax backward (thread n for expert n)
+  if (p.renorm) {
+    if (tid == 0) {
+      float s = 0.f;
+      for (int j = 0; j < k; ++j) s += s_w[j] * s_g[j];
+      red[0] = s;
+    }
+    for (int n = tid; n < N; n += kTokThreads) s_dl[n] = 0.f;
+    __syncthreads();
+    if (tid < k) s_dl[s_e[tid]] = s_w[tid] * (s_g[tid] - red[0]);
+  } else {
+    // p = softmax of the logits (max, exps and their sum in expert order)
+    if (tid == 0) {
+      const float* l = p.logits + (int64_t)t * N;
+      float m = l[0];
+      for (int n = 1; n < N; ++n) m = fmaxf(m, l[n]);
+      float z = 0.f;
+      for (int n = 0; n < N; ++n) z += expf(l[n] - m);
+      red[0] = m;
+      red[1] = z;
+    }
+    for (int n = tid; n < N; n += kTokThreads) s_dz[n] = 0.f;  // G, scattered
+    __syncthreads();
+    if (tid < k) s_dz[s_e[tid]] = s_g[tid];
+    __syncthreads();
+    const float m = red[0], z = red[1];
+    for (int n = tid; n < N; n += kTokThreads) s_dl[n] = expf(p.logits[(int64_t)t * N + n] - m) / z;
+    __syncthreads();
+    if (tid == 0) {
+      float s = 0.f;
+      for (int n = 0; n < N; ++n) s += s_dl[n] * s_dz[n];
+      red[2] = s;
+    }
+    __syncthreads();
+    const float s = red[2];
+    for (int n = tid; n < N; n += kTokThreads) s_dl[n] = s_dl[n] * (s_dz[n] - s);
+  }
+  __syncthreads();
+  // noisy gate: dz = dl eps sigmoid(x W_n), x W_n by block sums per expert
+  if (p.w_noise) {
+    for (int n = 0; n < N; ++n) {
+      float part = 0.f;
+      for (int i = tid; i < d; i += kTokThreads)
+        part += (float)p.x[(int64_t)t * d + i] * (float)p.w_noise[(int64_t)i * N + n];
+      const float z = block_sum(part, red);
+      if (tid == 0) {
+        const float e = expf(-fabsf(z));
+        const float sig = z >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+        s_dz[n] = s_dl[n] * p.noise[(int64_t)t * N + n] * sig;
+      }
+    }
+    __syncthreads();
+  }
+  for (int n = tid; n < N; n += kTokThreads) {
+    p.dl[(int64_t)t * N + n] = s_dl[n];
+    if (p.w_noise) p.dz[(int64_t)t * N + n] = s_dz[n];
+  }
+  // dx
+  for (int i = tid; i < d; i += kTokThreads) {
+    float v = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (s_row[j] >= 0) v += p.dx_perm[(int64_t)s_row[j] * d + i];
+    float gsum = 0.f;
+    for (int n = 0; n < N; ++n) gsum = fmaf(s_dl[n], (float)p.w_gate[(int64_t)i * N + n], gsum);
+    if (p.w_noise)
+      for (int n = 0; n < N; ++n) gsum = fmaf(s_dz[n], (float)p.w_noise[(int64_t)i * N + n], gsum);
+    v += gsum;
+    reinterpret_cast<uint16_t*>(p.dx)[(int64_t)t * d + i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// partial[c][n] = sum over the tokens of chunk c of src[t][n] (t ascending)
+__global__ __launch_bounds__(256) void column_sum_partial_kernel(const float* src, float* partial, int T, int N) {
+  const int c = blockIdx.x;
+  const int t0 = c * 256, t1 = min(T, t0 + 256);
+  for (int n = threadIdx.x; n < N; n += 256) {
+    float s = 0.f;
+    for (int t = t0; t < t1; ++t) s += src[(int64_t)t * N + n];
+    partial[(int64_t)c * N + n] = s;
+  }
+}
+
+constexpr int kGateTok = 256;  // tokens per partial sum of the gate's weight gradients
+
+// partial[c][i][n] = sum over the tokens of chunk c of x[t, i] * src[t, n]
+// (t ascending); one thread per i, experts in groups of 8
+__global__ __launch_bounds__(256) void gate_grad_partial_kernel(const bf16* x, const float* src, float* partial,
+                                                                int T, int d, int N) {
+  __shared__ float s_src[kGateTok * 8];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int c = blockIdx.y;
+  const int t0 = c * kGateTok, t1 = min(T, t0 + kGateTok);
+  for (int n0 = 0; n0 < N; n0 += 8) {
+    __syncthreads();
+    for (int q = threadIdx.x; q < (t1 - t0) * 8; q += 256) {
+      const int tt = q / 8, nn = n0 + q % 8;
+      s_src[q] = nn < N ? src[(int64_t)(t0 + tt) * N + nn] : 0.f;
+    }
+    __syncthreads();
+    if (i >= d) continue;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = t0; t < t1; ++t) {
+      const float xv = (float)x[(int64_t)t * d + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(xv, s_src[(t - t0) * 8 + u], acc[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (n0 + u < N) partial[((int64_t)c * d + i) * N + n0 + u] = acc[u];
+  }
+}
+
+// out[i][n] = the chunks' partial sums added in chunk order
+__global__ __launch_bounds__(256) void gate_grad_final_kernel(const float* partial, float* out, int chunks,
+                                                              int64_t n_out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= n_out) return;
+  float s = 0.f;
+  for (int c = 0; c < chunks; ++c) s += partial[(int64_t)c * n_out + q];
+  out[q] = s;
+}
+
+// out[e][c] = sum over rows [off[e], off[e+1]) of src[row][c], rows in
+// order (per expert column sums for the bias gradients)
+template <typename S>
+__global__ __launch_bounds__(256) void colsum_kernel(const S* src, const int32_t* off, float* out, int cols,
+                                                     int rows_bound) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const int lo = min(max(off[e], 0), rows_bound), hi = min(max(off[e + 1], lo), rows_bound);
+  float s = 0.f;
+  for (int r = lo; r < hi; ++r) s += (float)src[(int64_t)r * cols + c];
+  out[(int64_t)e * cols + c] = s;
+}
+
+template <BwdLayout LA, BwdLayout LB, BwdEpi EPI, typename O, bool RK>
+hipError_t launch_bwd(const BwdGemmParams& p, hipStream_t s) {
+  int64_t tiles;
+  const int64_t NT = (p.N + kTile - 1) / kTile;
+  if (RK) tiles = (int64_t)p.groups * ((p.M + kTile - 1) / kTile) * NT;
+  else tiles = ((int64_t)p.M / kTile + p.groups) * NT;
+  if (tiles <= 0) return hipSuccess;
+  const int64_t blocks = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+  hipLaunchKernelGGL((bwd_gemm_kernel<LA, LB, EPI, O, RK>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_gemm(const BwdGemmParams& p, BwdGemmKind kind, hipStream_t s) {
+  using L = BwdLayout;
+  switch (kind) {
+    case BwdGemmKind::kRecompute:  // U, H = GELU(U): gathered x rows, W1 [K][N]
+      return launch_bwd<L::kKContig, L::kKStrided, BwdEpi::kDualGelu, bf16, false>(p, s);
+    case BwdGemmKind::kGeluGrad:  // dU: gathered dy rows, W2_e rows [N][K]
+      return launch_bwd<L::kKContig, L::kKContig, BwdEpi::kGeluGrad, bf16, false>(p, s);
+    case BwdGemmKind::kDataGrad:  // dx_perm = dU W1_e^T, fp32
+      return launch_bwd<L::kKContig, L::kKContig, BwdEpi::kPlain, float, false>(p, s);
+    case BwdGemmKind::kWeightGrad:  // dW_e = A_e^T B_e over the group's rows, fp32
+      return launch_bwd<L::kKStrided, L::kKStrided, BwdEpi::kPlain, float, true>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_scale_rows(const bf16* dy, const int32_t* row_of, const float* w, bf16* out, int T, int d, int k,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(scale_rows_kernel, dim3((T + 3) / 4), dim3(256), 0, s, dy, row_of, w, out, T, d, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_importance_grad(const float* imp, float* dimp, int N, float c0, float c1, hipStream_t s) {
+  hipLaunchKernelGGL(importance_grad_kernel, dim3(1), dim3(64), 0, s, imp, dimp, N, c0, c1);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_token(const BwdTokenParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_token_kernel, dim3(p.T), dim3(kTokThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+int gate_grad_chunks(int64_t T) { return (int)((T + kGateTok - 1) / kGateTok); }
+
+hipError_t launch_gate_grad(const bf16* x, const float* src, float* partial, float* out, int T, int d, int N,
+                            hipStream_t s) {
+  const int chunks = gate_grad_chunks(T);
+  hipLaunchKernelGGL(gate_grad_partial_kernel, dim3((d + 255) / 256, chunks), dim3(256), 0, s, x, src, partial, T,
+                     d, N);
+  const int64_t n_out = (int64_t)d * N;
+  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, partial, out,
+                     chunks, n_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum_bf16(const bf16* src, const int32_t* off, float* out, int cols, int groups, int rows_bound,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(colsum_kernel<bf16>, dim3((cols + 255) / 256, groups), dim3(256), 0, s, src, off, out, cols,
+                     rows_bound);
+  return hipGetLastError();
+}
+
+hipError_t launch_column_sum(const float* src, float* partial, float* out, int T, int N, hipStream_t s) {
+  const int chunks = gate_grad_chunks(T);
+  hipLaunchKernelGGL(column_sum_partial_kernel, dim3(chunks), dim3(256), 0, s, src, partial, T, N);
+  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((N + 255) / 256), dim3(256), 0, s, partial, out, chunks,
+                     (int64_t)N);
+  return hipGetLastError();
+}
+
+}  // namespace moe

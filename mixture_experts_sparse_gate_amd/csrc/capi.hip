@@ -177,6 +177,53 @@ ForwardWs forward_ws(const moe_desc_t* d) {
   return w;
 }
 
+// the backward pass: expert-ordered rows of x and of w dy, U, H, dU, the
+// partial dots, the fp32 dx rows, dl and dz, the load-balance staging and
+// the gate gradients' partial sums
+struct BackwardWs {
+  size_t x_perm, dY, U, H, dU, pd, dx_perm, dl, dz, imp_part, imp, dimp, gpart, bytes;
+};
+BackwardWs backward_ws(const moe_desc_t* d) {
+  BackwardWs w{};
+  const size_t R = (size_t)rows_bound_of(d), T = (size_t)d->T;
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    const size_t a = o;
+    o += align_up(n);
+    return a;
+  };
+  w.x_perm = take(R * d->d * 2);
+  w.dY = take(R * d->d * 2);
+  w.U = take(R * d->h * 2);
+  w.H = take(R * d->h * 2);
+  w.dU = take(R * d->h * 2);
+  w.pd = take(R * (size_t)((d->h + 127) / 128) * 4);
+  w.dx_perm = take(R * d->d * 4);
+  w.dl = take(T * d->N * 4);
+  w.dz = take(T * d->N * 4);
+  w.imp_part = take((size_t)moe::aux_blocks(d->T) * d->N * 4);
+  w.imp = take((size_t)d->N * 4);
+  w.dimp = take((size_t)d->N * 4);
+  const size_t chunks = (size_t)moe::gate_grad_chunks(d->T);
+  const size_t gp = chunks * d->d * d->N * 4, bp = chunks * d->N * 4;
+  w.gpart = take(gp > bp ? gp : bp);
+  w.bytes = o;
+  return w;
+}
+
+// layers the backward serves: bf16, plain or noisy gate, and row buffers
+// whose byte ranges fit the kernels' 32-bit buffer descriptors
+moe_status_t check_backward(const moe_desc_t* d) {
+  TRY(check_desc(d));
+  if (d->dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "moe_backward needs a bf16 layer");
+  if (d->gate == MOE_GATE_COSINE) return fail(MOE_ERR_UNSUPPORTED, "moe_backward covers the plain and noisy gates");
+  const int64_t R = rows_bound_of(d), wide = d->d > d->h ? d->d : d->h;
+  if (R * wide * 2 >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_backward: R*max(d,h)*2 = %lld bytes must stay below 2^31",
+                (long long)(R * wide * 2));
+  return MOE_OK;
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -555,6 +602,7 @@ moe_status_t moe_workspace_size(const moe_desc_t* desc, moe_ws_kind_t kind, size
     case MOE_WS_FORWARD: *bytes = forward_ws(desc).bytes; return MOE_OK;
     case MOE_WS_FFN: *bytes = align_up((size_t)ffn_counters_of(desc) * 4); return MOE_OK;
     case MOE_WS_AUX: *bytes = align_up((size_t)moe::aux_blocks(desc->T) * desc->N * 4); return MOE_OK;
+    case MOE_WS_BACKWARD: *bytes = backward_ws(desc).bytes; return MOE_OK;
   }
   return fail(MOE_ERR_INVALID, "unknown workspace kind %d", (int)kind);
 }
@@ -703,6 +751,198 @@ moe_status_t moe_aux_loss(const moe_desc_t* desc, const int32_t* topk_idx, const
   p.N = desc->N;
   p.k = desc->k;
   return hip_status(moe::launch_aux_loss(p, (hipStream_t)stream), "load-balance terms");
+}
+
+moe_status_t moe_backward(const moe_desc_t* desc, const moe_backward_tensors_t* t, const float* aux_coef, void* ws,
+                          size_t ws_bytes, void* stream) {
+  TRY(check_backward(desc));
+  if (!t) return fail(MOE_ERR_INVALID, "tensors is NULL");
+  const bool noisy = desc->gate == MOE_GATE_NOISY;
+  TRY(need(t->x, "x", 16));
+  TRY(need(t->w_gate, "w_gate", 16));
+  if (noisy) {
+    TRY(need(t->w_noise, "w_noise", 16));
+    TRY(need(t->noise, "noise", 4));
+    TRY(need(t->dw_noise, "dw_noise", 16));
+  }
+  TRY(need(t->W1, "W1", 16));
+  TRY(need(t->W2, "W2", 16));
+  TRY(maybe(t->b1, "b1", 8));
+  TRY(maybe(t->b2, "b2", 8));
+  if (!desc->renorm) TRY(need(t->logits, "logits", 4));
+  TRY(need(t->topk_idx, "topk_idx", 4));
+  TRY(need(t->topk_w, "topk_w", 4));
+  TRY(need(t->expert_off, "expert_off", 4));
+  TRY(need(t->row_of, "row_of", 4));
+  TRY(need(t->token_of_row, "token_of_row", 4));
+  TRY(need(t->dy, "dy", 16));
+  TRY(need(t->dx, "dx", 16));
+  TRY(need(t->dW1, "dW1", 16));
+  TRY(need(t->dW2, "dW2", 16));
+  TRY(maybe(t->db1, "db1", 4));
+  TRY(maybe(t->db2, "db2", 4));
+  TRY(need(t->dw_gate, "dw_gate", 16));
+  TRY(maybe(t->dlogit_bias, "dlogit_bias", 4));
+  const BackwardWs bw = backward_ws(desc);
+  TRY(check_ws(ws, ws_bytes, bw.bytes));
+  const bool aux = aux_coef && (aux_coef[0] != 0.f || aux_coef[1] != 0.f);
+  hipStream_t s = (hipStream_t)stream;
+  const int T = (int)desc->T, d = desc->d, h = desc->h, N = desc->N, k = desc->k;
+  const int R = (int)rows_bound_of(desc);
+  using moe::bf16;
+  bf16* x_perm = at<bf16>(ws, bw.x_perm);
+  bf16* dY = at<bf16>(ws, bw.dY);
+  bf16* U = at<bf16>(ws, bw.U);
+  bf16* H = at<bf16>(ws, bw.H);
+  bf16* dU = at<bf16>(ws, bw.dU);
+  float* pd = at<float>(ws, bw.pd);
+  float* dx_perm = at<float>(ws, bw.dx_perm);
+  float* dl = at<float>(ws, bw.dl);
+  float* dz = at<float>(ws, bw.dz);
+  // the rows of x in expert order, and the rows bf16(w dy_t)
+  moe::DispatchParams dp{};
+  dp.x = t->x;
+  dp.row_of = const_cast<int32_t*>(t->row_of);  // read only by the permute
+  dp.x_perm = x_perm;
+  dp.T = T;
+  dp.d = d;
+  dp.k = k;
+  dp.elem_bytes = 2;
+  TRY(hip_status(moe::launch_permute(dp, s), "backward: x rows"));
+  TRY(hip_status(moe::launch_scale_rows(static_cast<const bf16*>(t->dy), t->row_of, t->topk_w, dY, T, d, k, s),
+                 "backward: dY rows"));
+  // U and H (recomputed), then dU and the partial dots G . H
+  moe::BwdGemmParams g{};
+  g.A = t->x;
+  g.gather = t->token_of_row;
+  g.gather_div = k;
+  g.lda = d;
+  g.a_bytes = (int64_t)T * d * 2;
+  g.B = t->W1;
+  g.ldb = h;
+  g.strideB = (int64_t)d * h;
+  g.b_bytes = (int64_t)d * h * 2;
+  g.C = U;
+  g.C2 = H;
+  g.ldc = h;
+  g.bias = t->b1;
+  g.seg = t->expert_off;
+  g.M = R;
+  g.N = h;
+  g.K = d;
+  g.groups = N;
+  TRY(hip_status(moe::launch_bwd_gemm(g, moe::BwdGemmKind::kRecompute, s), "backward: U, H"));
+  moe::BwdGemmParams gg = g;
+  gg.A = t->dy;
+  gg.B = t->W2;
+  gg.ldb = d;
+  gg.strideB = (int64_t)h * d;
+  gg.C = dU;
+  gg.C2 = nullptr;
+  gg.bias = nullptr;
+  gg.U = U;
+  gg.H = H;
+  gg.row_w = t->topk_w;
+  gg.tor = t->token_of_row;
+  gg.pd = pd;
+  TRY(hip_status(moe::launch_bwd_gemm(gg, moe::BwdGemmKind::kGeluGrad, s), "backward: dU"));
+  // dx_perm = dU W1_e^T
+  moe::BwdGemmParams gx{};
+  gx.A = dU;
+  gx.lda = h;
+  gx.a_bytes = (int64_t)R * h * 2;
+  gx.B = t->W1;
+  gx.ldb = h;
+  gx.strideB = (int64_t)d * h;
+  gx.b_bytes = (int64_t)d * h * 2;
+  gx.C = dx_perm;
+  gx.ldc = d;
+  gx.seg = t->expert_off;
+  gx.M = R;
+  gx.N = d;
+  gx.K = h;
+  gx.groups = N;
+  TRY(hip_status(moe::launch_bwd_gemm(gx, moe::BwdGemmKind::kDataGrad, s), "backward: dx rows"));
+  // dW2_e = H_e^T dY_e, dW1_e = x_e^T dU_e over each expert's rows
+  moe::BwdGemmParams gw{};
+  gw.A = H;
+  gw.lda = h;
+  gw.a_bytes = (int64_t)R * h * 2;
+  gw.B = dY;
+  gw.ldb = d;
+  gw.b_bytes = (int64_t)R * d * 2;
+  gw.C = t->dW2;
+  gw.ldc = d;
+  gw.strideC = (int64_t)h * d;
+  gw.seg = t->expert_off;
+  gw.a_rows = R;
+  gw.M = h;
+  gw.N = d;
+  gw.groups = N;
+  TRY(hip_status(moe::launch_bwd_gemm(gw, moe::BwdGemmKind::kWeightGrad, s), "backward: dW2"));
+  gw.A = x_perm;
+  gw.lda = d;
+  gw.a_bytes = (int64_t)R * d * 2;
+  gw.B = dU;
+  gw.ldb = h;
+  gw.b_bytes = (int64_t)R * h * 2;
+  gw.C = t->dW1;
+  gw.ldc = h;
+  gw.strideC = (int64_t)d * h;
+  gw.M = d;
+  gw.N = h;
+  TRY(hip_status(moe::launch_bwd_gemm(gw, moe::BwdGemmKind::kWeightGrad, s), "backward: dW1"));
+  // the load-balance losses' gradient per expert
+  float* dimp = nullptr;
+  if (aux) {
+    moe::AuxParams ap{};
+    ap.topk_idx = t->topk_idx;
+    ap.topk_w = t->topk_w;
+    ap.partial = at<float>(ws, bw.imp_part);
+    ap.importance = at<float>(ws, bw.imp);
+    ap.T = T;
+    ap.N = N;
+    ap.k = k;
+    TRY(hip_status(moe::launch_aux_loss(ap, s), "backward: importance"));
+    dimp = at<float>(ws, bw.dimp);
+    TRY(hip_status(moe::launch_importance_grad(ap.importance, dimp, N, aux_coef[0], aux_coef[1], s),
+                   "backward: importance gradient"));
+  }
+  // per token: gate-weight gradients, softmax (and softplus) backward, dx
+  moe::BwdTokenParams tp{};
+  tp.pd = pd;
+  tp.ntc = (h + 127) / 128;
+  tp.topk_idx = t->topk_idx;
+  tp.topk_w = t->topk_w;
+  tp.row_of = t->row_of;
+  tp.logits = t->logits;
+  tp.dimp = dimp;
+  tp.dy = static_cast<const bf16*>(t->dy);
+  tp.b2 = static_cast<const bf16*>(t->b2);
+  tp.x = static_cast<const bf16*>(t->x);
+  tp.w_gate = static_cast<const bf16*>(t->w_gate);
+  tp.w_noise = noisy ? static_cast<const bf16*>(t->w_noise) : nullptr;
+  tp.noise = t->noise;
+  tp.dx_perm = dx_perm;
+  tp.dl = dl;
+  tp.dz = dz;
+  tp.dx = static_cast<bf16*>(t->dx);
+  tp.T = T;
+  tp.d = d;
+  tp.N = N;
+  tp.k = k;
+  tp.renorm = desc->renorm;
+  TRY(hip_status(moe::launch_bwd_token(tp, s), "backward: tokens"));
+  // the gate's weights and logit bias
+  float* part = at<float>(ws, bw.gpart);
+  TRY(hip_status(moe::launch_gate_grad(tp.x, dl, part, t->dw_gate, T, d, N, s), "backward: dw_gate"));
+  if (noisy) TRY(hip_status(moe::launch_gate_grad(tp.x, dz, part, t->dw_noise, T, d, N, s), "backward: dw_noise"));
+  if (t->dlogit_bias)
+    TRY(hip_status(moe::launch_column_sum(dl, part, t->dlogit_bias, T, N, s), "backward: dlogit_bias"));
+  // the expert biases
+  if (t->db1) TRY(hip_status(moe::launch_colsum_bf16(dU, t->expert_off, t->db1, h, N, R, s), "backward: db1"));
+  if (t->db2) TRY(hip_status(moe::launch_colsum_bf16(dY, t->expert_off, t->db2, d, N, R, s), "backward: db2"));
+  return MOE_OK;
 }
 
 moe_status_t moe_ffn_status(const moe_desc_t* desc, moe_ws_kind_t kind, const void* ws, size_t ws_bytes,

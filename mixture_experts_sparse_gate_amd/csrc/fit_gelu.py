@@ -1,4 +1,4 @@
-"""Derives the GELU constants in gemm.hip (run by hand; nothing builds from it).
+"""Derives the GELU constants in gelu.hpp (run by hand; nothing builds from it).
 
 GELU(u) = u * Phi(u) with Phi(u) = erfc(-u / sqrt(2)) / 2. With a = |u| and
 Q(a) = Phi(-a) = erfc(a / sqrt(2)) / 2, GELU(u) = max(u, 0) - a Q(a): u - u Q(u)

@@ -133,6 +133,72 @@ hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t*
 // set to NaN); counters null: *out = 0
 hipError_t launch_ffn_status(const int32_t* counters, int32_t* out, hipStream_t s);
 
+// ---- backward pass (backward.hip), bf16 layers
+typedef __bf16 bf16;
+constexpr int kMaxExperts = 256;
+enum class BwdLayout { kKContig, kKStrided };  // an operand's rows hold K (contiguous) or M / N (K strided)
+enum class BwdEpi { kPlain, kDualGelu, kGeluGrad };
+enum class BwdGemmKind {
+  kRecompute,   // U = x_perm W1 + b1 and H = GELU(U): A gathered rows (K = d), B = W1 [d][h]; C = U, C2 = H
+  kGeluGrad,    // G = dy_perm W2^T: A gathered dy rows, B = W2_e rows [h][d]; C = dU = bf16(w G GELU'(U)),
+                // pd = per-row dots G . H over each 128-column tile
+  kDataGrad,    // dx_perm = dU W1_e^T: A = dU rows (K = h), B = W1_e rows [d][h]; C fp32
+  kWeightGrad,  // per group e: C_e [M, N] = A_e^T B_e over the group's rows; A [rows][M], B [rows][N]; C fp32
+};
+struct BwdGemmParams {
+  const void* A;         // bf16
+  const void* B;         // bf16, group g at B + g * strideB elements
+  void* C;               // output (group g at C + g * strideC elements for kWeightGrad)
+  int64_t lda, ldb, ldc, strideB, strideC;
+  int64_t a_bytes, b_bytes;  // byte ranges of A and of one group of B (< 2^31)
+  const int32_t* seg;    // [groups + 1]: output rows (ragged M) or contraction rows (kWeightGrad)
+  const int32_t* gather; // A row of output row m: gather[m] / gather_div (or null: row m)
+  int gather_div;
+  int a_rows;            // kWeightGrad: rows of A and B (bound of seg)
+  int M, N, K, groups;   // ragged M: M = row bound; kWeightGrad: each group's C is M x N
+  const void* bias;      // kRecompute: [groups, N] bf16 or null
+  void* C2;              // kRecompute: H
+  const void* U;         // kGeluGrad: [rows, N] bf16
+  const void* H;         // kGeluGrad: [rows, N] bf16
+  const float* row_w;    // kGeluGrad: gate weight of choice t*k+j
+  const int32_t* tor;    // kGeluGrad: choice t*k+j of each row
+  float* pd;             // kGeluGrad: [rows, ceil(N / 128)]
+};
+hipError_t launch_bwd_gemm(const BwdGemmParams& p, BwdGemmKind kind, hipStream_t s);
+hipError_t launch_scale_rows(const bf16* dy, const int32_t* row_of, const float* w, bf16* out, int T, int d, int k,
+                             hipStream_t s);
+hipError_t launch_importance_grad(const float* imp, float* dimp, int N, float c0, float c1, hipStream_t s);
+struct BwdTokenParams {
+  const float* pd;        // [R, ntc] partial dots G . H
+  int ntc;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const int32_t* row_of;
+  const float* logits;    // [T, N] (renorm = 0)
+  const float* dimp;      // [N] or null (no auxiliary losses)
+  const bf16* dy;         // [T, d]
+  const bf16* b2;         // [N, d] or null
+  const bf16* x;          // [T, d]
+  const bf16* w_gate;     // [d, N]
+  const bf16* w_noise;    // [d, N] or null (plain gate)
+  const float* noise;     // [T, N]
+  const float* dx_perm;   // [R, d]
+  float* dl;              // [T, N] out
+  float* dz;              // [T, N] out (noisy)
+  bf16* dx;               // [T, d] out
+  int T, d, N, k, renorm;
+};
+hipError_t launch_bwd_token(const BwdTokenParams& p, hipStream_t s);
+int gate_grad_chunks(int64_t T);
+// out [d, N] = x^T src (src [T, N] fp32), through partial [gate_grad_chunks(T), d, N]
+hipError_t launch_gate_grad(const bf16* x, const float* src, float* partial, float* out, int T, int d, int N,
+                            hipStream_t s);
+// out [N] = column sums of src [T, N], through partial [gate_grad_chunks(T), N]
+hipError_t launch_column_sum(const float* src, float* partial, float* out, int T, int N, hipStream_t s);
+// out [groups, cols] = per group the sums of its rows [off[g], off[g+1]) of src [rows, cols]
+hipError_t launch_colsum_bf16(const bf16* src, const int32_t* off, float* out, int cols, int groups, int rows_bound,
+                              hipStream_t s);
+
 // ---- measurement aids (probe.hip)
 // copies bytes / 16 16-byte chunks from src to dst
 hipError_t launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);

@@ -1,4 +1,4 @@
-"""The two GELUs of the expert FFN kernel (gemm.hip; the accurate one for
+"""The two GELUs of the expert FFN kernel (gelu.hpp; the accurate one for
 fp32 results, the cheaper one for bf16 results): their constants are the ones
 fit_gelu.py derives, and each formula, evaluated step by step in fp32, stays
 within its stated error of the exact GELU (scipy's erfc in fp64)."""
@@ -17,9 +17,9 @@ CSRC = os.path.join(ROOT, "mixture_experts_sparse_gate_amd", "csrc")
 
 
 def kernel_constants(decl=r"h\[8\]"):
-    src = open(os.path.join(CSRC, "gemm.hip")).read()
+    src = open(os.path.join(CSRC, "gelu.hpp")).read()
     m = re.search(r"constexpr float " + decl + r" = \{([^}]*)\}", src)
-    assert m, "GELU constants not found in gemm.hip"
+    assert m, "GELU constants not found in gelu.hpp"
     return np.array([float(v.strip().rstrip("f")) for v in m.group(1).split(",")], dtype=np.float32)
 
 
