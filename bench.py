@@ -17,7 +17,9 @@ Besides the headline:
     each stage's duration; aux_loss: moe_aux_loss (per-expert importance and
     the two load-balance losses) on the step's routing, timed the same way;
   - graph_ms_per_step: moe_forward captured once in a HIP graph and replayed
-    (no host launch cost per kernel);
+    (no host launch cost per kernel); graph4_ms_per_step: four calls per
+    captured graph (each replay boundary costs a fixed ~8 us of device idle
+    time, which four calls share);
   - cold: each step timed alone by events after writing a 512 MiB buffer
     (twice the last-level cache), median / p10 / p90;
   - measured_peaks: the chip's own ceilings in the same run, a 1 GiB device
@@ -117,8 +119,11 @@ def main() -> int:
                     help="time only the warm steps (no graph replay, no cold-cache steps): counter runs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
+    ap.add_argument("--graph-ab", action="store_true",
+                    help="only interleave 3 rounds of 20 eager moe_forward steps and 20 graph replays "
+                         "(for a kernel trace; --summarize --kind gaps condenses it)")
     ap.add_argument("--summarize", default=None, help="rocprofv3 results.db to condense (no GPU)")
-    ap.add_argument("--kind", choices=["stats", "traffic", "pmc"], default="stats")
+    ap.add_argument("--kind", choices=["stats", "traffic", "pmc", "gaps"], default="stats")
     ap.add_argument("--pmc-dbs", nargs="*", default=[], help="with --kind pmc: results.db files of counter passes")
     ap.add_argument("--fetch-db", default=None, help="with --kind traffic: the FETCH_SIZE results.db")
     ap.add_argument("--write-db", default=None, help="with --kind traffic: the WRITE_SIZE results.db")
@@ -156,6 +161,8 @@ def main() -> int:
     log(f"[bench] {spec.name}: inputs ready in {time.perf_counter() - t_gen:.1f}s")
 
     stream = torch.cuda.current_stream()
+    if args.graph_ab:
+        return graph_ab(dev, torch)
     if args.calib_copy_mib > 0:
         # a plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read
         # for it calibrates the counters (the only 1-byte-element copy here)
@@ -214,7 +221,7 @@ def main() -> int:
                 for j, n in enumerate(names)}
 
     # ---- moe_forward replayed from a HIP graph
-    graph_ms = None
+    graph_ms = graph4_ms = None
     try:
         if args.skip_extras:
             raise RuntimeError("skipped (--skip-extras)")
@@ -236,6 +243,22 @@ def main() -> int:
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / K
         del graph
+        # four layer calls per graph: the replay boundary's fixed cost is paid
+        # once per four steps
+        graph4 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph4):
+            for _ in range(4):
+                forward()
+        for _ in range(2):
+            graph4.replay()
+        torch.cuda.synchronize()
+        reps4 = max(1, K // 4)
+        t0 = time.perf_counter()
+        for _ in range(reps4):
+            graph4.replay()
+        torch.cuda.synchronize()
+        graph4_ms = (time.perf_counter() - t0) * 1e3 / (4 * reps4)
+        del graph4
     except RuntimeError as e:  # capture unavailable: report the eager figures only
         log(f"[bench] graph capture skipped: {e}")
 
@@ -414,12 +437,73 @@ def main() -> int:
         "stages": stages,
         "staged_ms_per_step": staged_ms,
         "graph_ms_per_step": graph_ms,
+        "graph4_ms_per_step": graph4_ms,
         "cold": cold_ms,
         "measured_peaks": peaks,
         "backward": backward,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def graph_ab(dev, torch):
+    """Three rounds of 20 eager moe_forward steps then 20 replays of one
+    captured call, timed on the host; run under a kernel trace, the trace
+    shows where the time goes (bench.py --summarize <db> --kind gaps)."""
+    fwd = lambda: dev.run_forward(inspect=False)
+    for _ in range(30):
+        fwd()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd()
+    for rnd in range(3):
+        for mode in ("eager", "graph"):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(20):
+                g.replay() if mode == "graph" else fwd()
+            torch.cuda.synchronize()
+            print(f"round {rnd} {mode}: {(time.perf_counter() - t0) * 1e3 / 20:.4f} ms/step", flush=True)
+    return 0
+
+
+def _gaps(db):
+    """Kernel durations and device gaps of the last 3 x (20 eager + 20 graph)
+    steps of a --graph-ab trace."""
+    import statistics
+    c = sqlite3.connect(db)
+    rows = list(c.execute("select name, start, end from kernels order by start"))
+    steps, cur = [], []
+    for n, a, b in rows:
+        k = _short(n)
+        if k in ("gate_fused_kernel", "gate_partial_kernel", "gate_logits_kernel", "cosine_gate_kernel") and cur:
+            steps.append(cur)
+            cur = []
+        cur.append((k, a, b))
+    steps.append(cur)
+    steps = [st for st in steps if any("ffn" in k or "grouped_gemm" in k for k, _, _ in st)][-120:]
+    out = []
+    for i in range(6):
+        blk = steps[i * 20:(i + 1) * 20]
+        mode = "eager" if i % 2 == 0 else "graph"
+        per = {}
+        for st in blk:
+            for k, a, b in st:
+                per.setdefault(k, []).append((b - a) / 1e3)
+        inner = statistics.mean(sum(max(0, st[j + 1][1] - st[j][2]) for j in range(len(st) - 1)) / 1e3 for st in blk)
+        between = statistics.mean((blk[j + 1][0][1] - blk[j][-1][2]) / 1e3 for j in range(len(blk) - 1))
+        span = (blk[-1][-1][2] - blk[0][0][1]) / 1e3 / len(blk)
+        kd = ", ".join(f"{k} {statistics.mean(v):.1f}" for k, v in per.items())
+        out.append(f"round {i // 2} {mode}: per-step span {span:.1f} us; gaps inside a step {inner:.1f} us; "
+                   f"gap before the next step {between:.1f} us; kernels (us): {kd}")
+    return out
 
 
 def measured_peaks(api, torch, stream):
@@ -537,6 +621,16 @@ def _pmc_all(db):
 
 def summarize(args):
     lines = [f"command: {args.command}"] if args.command else []
+    if args.kind == "gaps":
+        lines.append("source: rocprofv3 --kernel-trace of bench.py --graph-ab (kernels table)")
+        lines.append(f"workload: {args.workload}")
+        lines.extend(_gaps(args.summarize))
+        text = "\n".join(lines) + "\n"
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        print(text)
+        return 0
     if args.kind == "pmc":
         # per-dispatch averages of each counter over the expert FFN's launches
         # (the later half of them: warm steps), from one or more passes
