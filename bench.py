@@ -122,8 +122,11 @@ def main() -> int:
     ap.add_argument("--graph-ab", action="store_true",
                     help="only interleave 3 rounds of 20 eager moe_forward steps and 20 graph replays "
                          "(for a kernel trace; --summarize --kind gaps condenses it)")
+    ap.add_argument("--dispatch-scaling", action="store_true",
+                    help="only time moe_dispatch on caller routing at T = 16k .. 256k tokens (N = 64, k = 2) "
+                         "and moe_forward's dispatch at the same T (noisy gate, N = 8)")
     ap.add_argument("--summarize", default=None, help="rocprofv3 results.db to condense (no GPU)")
-    ap.add_argument("--kind", choices=["stats", "traffic", "pmc", "gaps"], default="stats")
+    ap.add_argument("--kind", choices=["stats", "traffic", "pmc", "gaps", "dispatch"], default="stats")
     ap.add_argument("--pmc-dbs", nargs="*", default=[], help="with --kind pmc: results.db files of counter passes")
     ap.add_argument("--fetch-db", default=None, help="with --kind traffic: the FETCH_SIZE results.db")
     ap.add_argument("--write-db", default=None, help="with --kind traffic: the WRITE_SIZE results.db")
@@ -133,6 +136,9 @@ def main() -> int:
 
     if args.summarize or args.kind == "traffic" and args.fetch_db or args.kind == "pmc" and args.pmc_dbs:
         return summarize(args)
+
+    if args.dispatch_scaling:
+        return dispatch_scaling()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no "
@@ -446,6 +452,76 @@ def main() -> int:
     return 0
 
 
+def dispatch_scaling():
+    """moe_dispatch (count, scan where the count table is large, rows and
+    permute kernels) on a seeded caller routing of T tokens over 64 experts
+    (k = 2, Zipf-skewed choices), T from 16k to 256k: mean of 20 calls by
+    events. Under a kernel trace the per-kernel times show that every
+    kernel's time grows linearly with T (one JSON line per T)."""
+    import torch
+
+    from mixture_experts_sparse_gate_amd import _lib, api, workloads
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    rng = np.random.default_rng(0)
+    for T in (16384, 32768, 65536, 131072, 262144):
+        spec = workloads.MoESpec("dispatch_scaling", T=T, d=256, h=256, N=64, k=2, capacity_factor=1.25,
+                                 gate="softmax", renorm=False, dtype="bf16")
+        p = 1.0 / np.arange(1, spec.N + 1) ** 0.8
+        p /= p.sum()
+        first = rng.choice(spec.N, size=T, p=p)
+        second = (first + 1 + rng.choice(spec.N - 1, size=T)) % spec.N
+        idx = torch.from_numpy(np.stack([first, second], 1).astype(np.int32)).cuda()
+        desc = api.desc_from_spec(spec)
+        R = api.rows_bound(desc)
+        dv = dict(dtype=torch.int32, device="cuda")
+        x = torch.zeros(T, spec.d, dtype=torch.bfloat16, device="cuda")
+        count, off = torch.empty(spec.N, **dv), torch.empty(spec.N + 1, **dv)
+        row_of, tor = torch.empty(T * spec.k, **dv), torch.empty(R, **dv)
+        x_perm = torch.empty(R, spec.d, dtype=torch.bfloat16, device="cuda")
+        ws = api.workspace(desc, _lib.MOE_WS_DISPATCH)
+        call = lambda: api.dispatch(desc, x, idx, count, off, row_of, tor, x_perm, ws=ws)
+        for _ in range(3):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(20):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"T": T, "N": spec.N, "k": spec.k, "moe_dispatch_us": a.elapsed_time(b) / 20 * 1e3}),
+              flush=True)
+    return 0
+
+
+def _dispatch_kernels(db):
+    """Mean duration per dispatch kernel for each T of a --dispatch-scaling
+    trace (the 23 calls per T follow each other in T order)."""
+    import statistics
+    c = sqlite3.connect(db)
+    rows = [(_short(n), (b - a) / 1e3) for n, a, b in c.execute("select name, start, end from kernels order by start")]
+    names = ("count_kernel", "scan_kernel", "rows_kernel", "permute_kernel")
+    calls = []
+    cur = {}
+    for k, dur in rows:
+        if k not in names:
+            continue
+        if k == "count_kernel" and cur:
+            calls.append(cur)
+            cur = {}
+        cur[k] = dur
+    calls.append(cur)
+    out = []
+    Ts = (16384, 32768, 65536, 131072, 262144)
+    for i, T in enumerate(Ts):
+        blk = calls[i * 23 + 3:(i + 1) * 23]
+        kd = ", ".join(f"{k} {statistics.mean(c[k] for c in blk if k in c):.1f}" for k in names
+                       if any(k in c for c in blk))
+        out.append(f"T={T}: mean over {len(blk)} calls (us): {kd}")
+    return out
+
+
 def graph_ab(dev, torch):
     """Three rounds of 20 eager moe_forward steps then 20 replays of one
     captured call, timed on the host; run under a kernel trace, the trace
@@ -621,10 +697,14 @@ def _pmc_all(db):
 
 def summarize(args):
     lines = [f"command: {args.command}"] if args.command else []
-    if args.kind == "gaps":
-        lines.append("source: rocprofv3 --kernel-trace of bench.py --graph-ab (kernels table)")
-        lines.append(f"workload: {args.workload}")
-        lines.extend(_gaps(args.summarize))
+    if args.kind in ("gaps", "dispatch"):
+        if args.kind == "gaps":
+            lines.append("source: rocprofv3 --kernel-trace of bench.py --graph-ab (kernels table)")
+            lines.append(f"workload: {args.workload}")
+            lines.extend(_gaps(args.summarize))
+        else:
+            lines.append("source: rocprofv3 --kernel-trace of bench.py --dispatch-scaling (kernels table)")
+            lines.extend(_dispatch_kernels(args.summarize))
         text = "\n".join(lines) + "\n"
         if args.out:
             with open(args.out, "w") as f:
@@ -691,6 +771,22 @@ def summarize(args):
             lines.append(f"{tag}_scale_factor: {fac:.4f}")
             lines.append(f"{tag}_ffn_kib_per_step_raw: {kib:.1f}")
         lines.append(f"workload: {args.workload}")
+        # a second calibration point for FETCH_SIZE: the gate kernel reads x
+        # (T d s bytes) and the small gate matrices once per call
+        try:
+            from mixture_experts_sparse_gate_amd import workloads as _w
+            sp = _w.get(args.workload)
+            gate = [v for d_, n, g, v in _pmc_per_kernel(args.fetch_db, "FETCH_SIZE") if "gate_fused_kernel" in n]
+            if gate:
+                steady = gate[len(gate) // 2:]
+                fac = known_kib / out["fetch"]["calib_kib"] if out["fetch"]["calib_kib"] and known_kib else float("nan")
+                got = sum(steady) / len(steady) * fac * 1024
+                x_bytes = sp.T * sp.d * (2 if sp.dtype == "bf16" else 4)
+                lines.append(f"gate_fetch_bytes_per_call: {got:.0f}")
+                lines.append(f"gate_x_bytes_per_call: {x_bytes}")
+                lines.append(f"gate_fetch_over_x: {got / x_bytes:.4f}")
+        except Exception as e:  # the check is informative only
+            lines.append(f"gate_fetch_check: unavailable ({e})")
         lines.append(f"ffn_hbm_bytes_per_step: {res['fetch'] + res['write']:.0f}")
         lines.append(f"ffn_hbm_read_bytes_per_step: {res['fetch']:.0f}")
         lines.append(f"ffn_hbm_write_bytes_per_step: {res['write']:.0f}")
