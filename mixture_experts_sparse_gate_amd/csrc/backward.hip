@@ -36,17 +36,28 @@
 namespace moe {
 namespace {
 
-constexpr int kTile = 128;     // output tile rows and columns
-constexpr int kBK = 32;        // K per step
-constexpr int kThreads = 256;  // 2 x 2 waves of 64 x 64
+constexpr int kBK = 32;  // K per step
 constexpr int kStages = 4;
-constexpr int kOpBytes = 8192;  // one operand's tile of one stage, either layout
-constexpr int kLoads = kOpBytes / 16 / kThreads;  // 16-byte loads per thread per operand and stage
 constexpr int kNumXcd = 8;
+constexpr int64_t kBwdBigTileMin = 256;  // CUs of the chip
+
+// Output tiles of TS x TS (128 or 256): two waves along M and TS / 64 along
+// N, each wave TS / 2 rows x 64 columns (FM x FN fragments of 32 x 32).
+// 256 x 256 tiles (8 waves, one block per CU) read half the operand bytes
+// per flop of 128 x 128 ones; they are taken where they give every CU a tile.
+template <int TS> struct Tile {
+  static constexpr int THREADS = TS == 256 ? 512 : 256;
+  static constexpr int WN = TS / 64;
+  static constexpr int WTM = TS / 2;
+  static constexpr int FM = WTM / 32, FN = 2;
+  static constexpr int OP_BYTES = TS * kBK * 2;            // one operand's tile of one stage
+  static constexpr int LOADS = OP_BYTES / 16 / THREADS;    // 16-byte loads per thread per operand
+  static_assert(TS == 128 || TS == 256, "tile size");
+};
 
 // 16-byte chunk swizzles (gfx950 LDS: 64 banks of 4 bytes): rows of 4 chunks
-// (K-contiguous tiles, 64-byte rows) and rows of 16 chunks (K-strided tiles,
-// 256-byte rows), each making its fragment reads conflict-free
+// (K-contiguous tiles, 64-byte rows) and rows of 16 or 32 chunks (K-strided
+// tiles, 256- or 512-byte rows), each making its fragment reads conflict-free
 __device__ inline int swz_rows4(int r) { return (r >> 2) & 3; }
 __device__ inline int swz_rows16(int k) { return (2 * (k & 3)) ^ (8 * (k & 1)); }
 
@@ -60,11 +71,12 @@ __device__ inline void wait_loads_and_lds() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-template <BwdLayout L> struct Operand;
+template <BwdLayout L, int TS> struct Operand;
 
-// Tile of 128 rows (of M or N) x 32 K, K contiguous: row x at byte
-// x * 64, chunk c of it at position c ^ swz_rows4(x).
-template <> struct Operand<BwdLayout::kKContig> {
+// Tile of TS rows (of M or N) x 32 K, K contiguous: row x at byte x * 64,
+// chunk c of it at position c ^ swz_rows4(x).
+template <int TS> struct Operand<BwdLayout::kKContig, TS> {
+  static constexpr int READS = 1;  // LDS reads per fragment
   // slot i of this thread: row and global chunk
   __device__ static void slot(int s, int& row, int& chunk) {
     row = s >> 2;
@@ -79,24 +91,26 @@ template <> struct Operand<BwdLayout::kKContig> {
   }
 };
 
-// Tile of 32 K x 128 columns (of M or N), K strided: K row k at byte
-// k * 256, chunk c of it at position c ^ swz_rows16(k). Fragments by
+// Tile of 32 K x TS columns (of M or N), K strided: K row k at byte
+// k * 2 TS, chunk c of it at position c ^ swz_rows16(k). Fragments by
 // transposing reads: in each 16-lane group q, lane r reads the 4 values of
 // K row 8 (q / 2) + r / 4 (+ 4 for the second read, + 16 ss) at columns
 // 32 f + 16 (q % 2) + 4 (r % 4) .. + 3, and the hardware hands each lane 8
 // consecutive K values of one column.
-template <> struct Operand<BwdLayout::kKStrided> {
+template <int TS> struct Operand<BwdLayout::kKStrided, TS> {
+  static constexpr int READS = 2;
+  static constexpr int ROW = 2 * TS;  // bytes per K row
   __device__ static void slot(int s, int& row, int& chunk) {
-    row = s >> 4;
-    chunk = (s & 15) ^ swz_rows16(row);
+    row = s / (TS / 8);
+    chunk = (s % (TS / 8)) ^ swz_rows16(row);
   }
   __device__ static u32x4 frag(const char* st, int base, int f, int ss, int lane) {
     const int q = lane >> 4, r = lane & 15;
     const int chunk = (base + 32 * f) / 8 + 2 * (q & 1) + ((r & 3) >> 1);
     const int krow = 8 * (q >> 1) + (r >> 2);
-    const char* p = st + krow * 256 + ((chunk ^ swz_rows16(r >> 2)) * 16) + 8 * (r & 1);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss) * 256));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss + 4) * 256));
+    const char* p = st + krow * ROW + ((chunk ^ swz_rows16(r >> 2)) * 16) + 8 * (r & 1);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss) * ROW));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss + 4) * ROW));
     const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
     return u32x4{a[0], a[1], b[0], b[1]};
   }
@@ -105,6 +119,7 @@ template <> struct Operand<BwdLayout::kKStrided> {
 // Ragged-M schedule: the block's (group, first row, end row, column tile)
 // from seg, over row tiles of all groups (column tiles outermost), XCD by
 // XCD in contiguous stretches. Returns false for blocks past the last tile.
+template <int TS>
 __device__ bool schedule_ragged_m(const BwdGemmParams& p, int* sched) {
   __shared__ int s_sched[4];
   const int lane = lane_id();
@@ -119,7 +134,7 @@ __device__ bool schedule_ragged_m(const BwdGemmParams& p, int* sched) {
         lo[i] = min(max(p.seg[g], 0), p.M);
         hi[i] = min(max(p.seg[g + 1], lo[i]), p.M);
       }
-      nt[i] = (hi[i] - lo[i] + kTile - 1) / kTile;
+      nt[i] = (hi[i] - lo[i] + TS - 1) / TS;
       sum += nt[i];
     }
     int inc = sum;
@@ -129,7 +144,7 @@ __device__ bool schedule_ragged_m(const BwdGemmParams& p, int* sched) {
       if (lane >= m) inc += o;
     }
     const int rows_total = __shfl(inc, kWave - 1, kWave);
-    const int NT = (p.N + kTile - 1) / kTile;
+    const int NT = (p.N + TS - 1) / TS;
     const int tiles = rows_total * NT;
     const int per = (tiles + kNumXcd - 1) / kNumXcd;
     const int b = blockIdx.x;
@@ -142,50 +157,54 @@ __device__ bool schedule_ragged_m(const BwdGemmParams& p, int* sched) {
     for (int i = 0; i < GPL; ++i) {
       if (live && q >= start && q < start + nt[i]) {
         s_sched[0] = lane * GPL + i;
-        s_sched[1] = lo[i] + (q - start) * kTile;
+        s_sched[1] = lo[i] + (q - start) * TS;
         s_sched[2] = hi[i];
-        s_sched[3] = col * kTile;
+        s_sched[3] = col * TS;
       }
       start += nt[i];
     }
   }
   __syncthreads();
   for (int i = 0; i < 4; ++i) sched[i] = __builtin_amdgcn_readfirstlane(s_sched[i]);
-  if (sched[0] >= 0) sched[2] = min(sched[2], sched[1] + kTile);
+  if (sched[0] >= 0) sched[2] = min(sched[2], sched[1] + TS);
   return sched[0] >= 0;
 }
 
-template <BwdLayout LA, BwdLayout LB, BwdEpi EPI, typename O, bool RAGGED_K>
-__global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
+template <int TS, BwdLayout LA, BwdLayout LB, BwdEpi EPI, typename O, bool RAGGED_K>
+__global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmParams p) {
+  using T = Tile<TS>;
+  constexpr int THREADS = T::THREADS, FM = T::FM, FN = T::FN, LOADS = T::LOADS, OPB = T::OP_BYTES;
+  using OA = Operand<LA, TS>;
+  using OB = Operand<LB, TS>;
   // one LDS object per stage (A tile, then B tile), so that the compiler
   // can tell the stage being filled from the one being read
-  __shared__ __attribute__((aligned(1024))) char st0[2 * kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char st1[2 * kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char st2[2 * kOpBytes];
-  __shared__ __attribute__((aligned(1024))) char st3[2 * kOpBytes];
-  __shared__ float s_dot[2][kTile];
+  __shared__ __attribute__((aligned(1024))) char st0[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char st2[2 * OPB];
+  __shared__ __attribute__((aligned(1024))) char st3[2 * OPB];
+  __shared__ float s_dot[T::WN][TS];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / T::WN, wn = wave % T::WN;
 
   // ---- the tile: group g, output rows [m0, m1) (ragged M: rows of the
   // concatenated groups; ragged K: rows of the group's own output), columns
   // from n0, contraction rows [k_lo, k_hi)
   int g, m0, m1, n0, k_lo, k_hi;
   if constexpr (RAGGED_K) {
-    const int MT = (p.M + kTile - 1) / kTile, NT = (p.N + kTile - 1) / kTile;
+    const int MT = (p.M + TS - 1) / TS, NT = (p.N + TS - 1) / TS;
     const int tiles = p.groups * MT * NT, per = (tiles + kNumXcd - 1) / kNumXcd;
     const int b = blockIdx.x, tile = (b % kNumXcd) * per + b / kNumXcd;
     if (b / kNumXcd >= per || tile >= tiles) return;
     g = tile / (MT * NT);
     const int rem = tile % (MT * NT);
-    m0 = (rem % MT) * kTile;  // row tiles fastest: consecutive blocks share the B panel
-    n0 = (rem / MT) * kTile;
-    m1 = min(m0 + kTile, p.M);
+    m0 = (rem % MT) * TS;  // row tiles fastest: consecutive blocks share the B panel
+    n0 = (rem / MT) * TS;
+    m1 = min(m0 + TS, p.M);
     k_lo = min(max(p.seg[g], 0), p.a_rows);
     k_hi = min(max(p.seg[g + 1], k_lo), p.a_rows);
   } else {
     int sc[4];
-    if (!schedule_ragged_m(p, sc)) return;
+    if (!schedule_ragged_m<TS>(p, sc)) return;
     g = sc[0], m0 = sc[1], m1 = sc[2], n0 = sc[3];
     k_lo = 0;
     k_hi = p.K;
@@ -197,13 +216,13 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, (uint32_t)p.a_bytes);
   const char* Bg = static_cast<const char*>(p.B) + (int64_t)g * p.strideB * 2;
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bg, (uint32_t)p.b_bytes);
-  int a_base[kLoads], a_kc[kLoads], b_base[kLoads], b_kc[kLoads];
-  bool a_ok[kLoads], b_ok[kLoads];
+  int a_base[LOADS], a_kc[LOADS], b_base[LOADS], b_kc[LOADS];
+  bool a_ok[LOADS], b_ok[LOADS];
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int s = i * kThreads + tid;
+  for (int i = 0; i < LOADS; ++i) {
+    const int s = i * THREADS + tid;
     int row, chunk;
-    Operand<LA>::slot(s, row, chunk);
+    OA::slot(s, row, chunk);
     if constexpr (LA == BwdLayout::kKContig) {
       // row m0 + row of A (gathered: A row gather[m] / gather_div)
       const int m = m0 + row;
@@ -217,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
       a_base[i] = (int)(((int64_t)(k_lo + row) * p.lda + m0 + chunk * 8) * 2);
       a_kc[i] = row;  // K offset of the row
     }
-    Operand<LB>::slot(s, row, chunk);
+    OB::slot(s, row, chunk);
     if constexpr (LB == BwdLayout::kKContig) {
       const int n = n0 + row;
       b_ok[i] = n < p.N;
@@ -234,45 +253,66 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
   auto issue = [&](char* st, int kt) {
     const int k0 = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < LOADS; ++i) {
       const bool ok = a_ok[i] && k0 + a_kc[i] < K;
       const int off = LA == BwdLayout::kKContig ? a_base[i] + k0 * 2 : a_base[i] + (int)((int64_t)k0 * p.lda * 2);
-      lds_dma16(ra, (lds_void*)(st + (i * kThreads + wave * kWave) * 16), ok ? off : (int)kOutOfRange);
+      lds_dma16(ra, (lds_void*)(st + (i * THREADS + wave * kWave) * 16), ok ? off : (int)kOutOfRange);
     }
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
+    for (int i = 0; i < LOADS; ++i) {
       const bool ok = b_ok[i] && k0 + b_kc[i] < K;
       const int off = LB == BwdLayout::kKContig ? b_base[i] + k0 * 2 : b_base[i] + (int)((int64_t)k0 * p.ldb * 2);
-      lds_dma16(rb, (lds_void*)(st + kOpBytes + (i * kThreads + wave * kWave) * 16), ok ? off : (int)kOutOfRange);
+      lds_dma16(rb, (lds_void*)(st + OPB + (i * THREADS + wave * kWave) * 16), ok ? off : (int)kOutOfRange);
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[FN][FM];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // a step's two 16-deep substeps; the fragment reads of substep 1 are
+  // issued before the MFMAs of substep 0
   auto compute = [&](const char* st) {
-    u32x4 fa[2][2], fb[2][2];  // [substep][fragment]: B (columns n), A (rows m)
+    u32x4 fa[2][FM], fb[2][FN];  // [substep][fragment]: A (rows m), B (columns n)
+    auto read = [&](int ss) {
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
+      for (int f = 0; f < FN; ++f) fb[ss][f] = OB::frag(st + OPB, wn * 64, f, ss, lane);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        fb[ss][f] = Operand<LB>::frag(st + kOpBytes, wn * 64, f, ss, lane);
-        fa[ss][f] = Operand<LA>::frag(st, wm * 64, f, ss, lane);
-      }
+      for (int f = 0; f < FM; ++f) fa[ss][f] = OA::frag(st, wm * T::WTM, f, ss, lane);
+    };
+    read(0);
 #pragma unroll
-    for (int ss = 0; ss < 2; ++ss)
+    for (int ss = 0; ss < 2; ++ss) {
+      if (ss == 0) read(1);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FN; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fb[ss][i]),
                                                                __builtin_bit_cast(bf16x8, fa[ss][j]), acc[i][j], 0,
                                                                0, 0);
+    }
+    if constexpr (TS == 256) {
+      // instruction order for the step: the first substep's LDS reads, then
+      // each MFMA followed by one of the next substep's LDS reads and, after
+      // every second MFMA, one of the step's global->LDS loads
+      constexpr int DSR = FM * OA::READS + FN * OB::READS;  // LDS reads per substep
+      constexpr int MF = FM * FN;
+      constexpr int VM = 2 * LOADS;
+      __builtin_amdgcn_sched_group_barrier(0x100, DSR, 0);
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+        for (int m = 0; m < MF; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (ss == 0 && m < DSR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if ((ss * MF + m) % 2 == 1 && (ss * MF + m) / 2 < VM) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+        }
+    }
   };
 
   // ---- four stages, one barrier per step, loads three steps ahead
@@ -281,8 +321,8 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
   issue(st1, 1);
   issue(st2, 2);
   auto step = [&](char* cur, char* nxt, int kt) {
-    wait_loads_and_lds<4 * kLoads>();  // this step's loads have landed; the previous stage is read
-    __syncthreads();
+    wait_loads_and_lds<4 * LOADS>();  // this step's loads have landed; the previous stage is read
+    __builtin_amdgcn_s_barrier();
     issue(nxt, kt + 3);
     compute(cur);
   };
@@ -298,20 +338,22 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
   if (kt + 2 < nk) step(st2, st1, kt + 2);
   wait_loads_and_lds<0>();
 
-  // ---- epilogue: the lane holds D[n][m] for rows m = m0 + 64 wm + 32 j +
+  // ---- epilogue: the lane holds D[n][m] for rows m = m0 + WTM wm + 32 j +
   // lane % 32 and columns n = n0 + 64 wn + 32 i + 8 q + 4 (lane / 32) + 0..3
-  const int mrow = m0 + wm * 64 + (lane & 31);
+  const int mrow = m0 + wm * T::WTM + (lane & 31);
   const int ncol = n0 + wn * 64 + 4 * (lane >> 5);
   const int64_t cbase = RAGGED_K ? (int64_t)g * p.strideC : 0;
-  float dot[2] = {0.f, 0.f};
+  float dot[FM];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < FM; ++j) dot[j] = 0.f;
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
     const int m = mrow + 32 * j;
     const bool row_ok = m < m1;
     float w = 0.f;
     if constexpr (EPI == BwdEpi::kGeluGrad) w = row_ok ? p.row_w[p.tor[m]] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FN; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = ncol + 32 * i + 8 * q;
@@ -352,19 +394,24 @@ __global__ __launch_bounds__(kThreads) void bwd_gemm_kernel(BwdGemmParams p) {
       }
   }
   if constexpr (EPI == BwdEpi::kGeluGrad) {
-    // the row's dot over the tile's 128 columns, in a fixed order: the lane
-    // pair (lane, lane + 32), then wave column 0 before wave column 1
+    // the row's dot over each 128 columns of the tile, in a fixed order: the
+    // lane pair (lane, lane + 32), then the first 64 columns' wave before the
+    // second's
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dot[j] += __shfl_xor(dot[j], 32, kWave);
+    for (int j = 0; j < FM; ++j) dot[j] += __shfl_xor(dot[j], 32, kWave);
     if (lane < 32)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) s_dot[wn][wm * 64 + 32 * j + lane] = dot[j];
+      for (int j = 0; j < FM; ++j) s_dot[wn][wm * T::WTM + 32 * j + lane] = dot[j];
     __syncthreads();
-    const int NTc = (p.N + kTile - 1) / kTile;
-    if (tid < kTile && m0 + tid < m1)
-      p.pd[(int64_t)(m0 + tid) * NTc + n0 / kTile] = s_dot[0][tid] + s_dot[1][tid];
+    const int NTc = (p.N + 127) / 128;
+    for (int e = tid; e < TS * (TS / 128); e += THREADS) {
+      const int r = e % TS, c = e / TS;
+      if (m0 + r < m1 && n0 + 128 * c < p.N)
+        p.pd[(int64_t)(m0 + r) * NTc + n0 / 128 + c] = s_dot[2 * c][r] + s_dot[2 * c + 1][r];
+    }
   }
 }
+
 
 // dY rows: for each kept choice (t, j), row row_of[t k + j] = bf16(w_tj dy_t);
 // one wave per token, dy_t read once
@@ -604,16 +651,29 @@ __global__ __launch_bounds__(256) void colsum_kernel(const S* src, const int32_t
   out[(int64_t)e * cols + c] = s;
 }
 
+// upper bound on the tiles of a launch with TS x TS tiles
+template <int TS>
+int64_t bwd_tiles(const BwdGemmParams& p, bool ragged_k) {
+  const int64_t NT = (p.N + TS - 1) / TS;
+  return ragged_k ? (int64_t)p.groups * ((p.M + TS - 1) / TS) * NT : ((int64_t)p.M / TS + p.groups) * NT;
+}
+
+template <int TS, BwdLayout LA, BwdLayout LB, BwdEpi EPI, typename O, bool RK>
+hipError_t launch_tiles(const BwdGemmParams& p, int64_t tiles, hipStream_t s) {
+  const int64_t blocks = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+  hipLaunchKernelGGL((bwd_gemm_kernel<TS, LA, LB, EPI, O, RK>), dim3((unsigned)blocks), dim3(Tile<TS>::THREADS), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
+// 256 x 256 tiles where they give at least one per CU, else 128 x 128
 template <BwdLayout LA, BwdLayout LB, BwdEpi EPI, typename O, bool RK>
 hipError_t launch_bwd(const BwdGemmParams& p, hipStream_t s) {
-  int64_t tiles;
-  const int64_t NT = (p.N + kTile - 1) / kTile;
-  if (RK) tiles = (int64_t)p.groups * ((p.M + kTile - 1) / kTile) * NT;
-  else tiles = ((int64_t)p.M / kTile + p.groups) * NT;
+  const int64_t big = bwd_tiles<256>(p, RK);
+  if (big >= kBwdBigTileMin) return launch_tiles<256, LA, LB, EPI, O, RK>(p, big, s);
+  const int64_t tiles = bwd_tiles<128>(p, RK);
   if (tiles <= 0) return hipSuccess;
-  const int64_t blocks = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
-  hipLaunchKernelGGL((bwd_gemm_kernel<LA, LB, EPI, O, RK>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
-  return hipGetLastError();
+  return launch_tiles<128, LA, LB, EPI, O, RK>(p, tiles, s);
 }
 
 }  // namespace
