@@ -40,6 +40,11 @@ CASES = {
     "ragged_tails": (workloads.MoESpec("ragged_tails", T=333, d=200, h=136, N=5, k=3, capacity_factor=0.8,
                                        gate="softmax", renorm=False, dtype="bf16", expert_bias=True),
                      (0.2, 0.0)),
+    # large enough for the 256 x 256 tiles, with d and h not multiples of
+    # the tile: partial row, column and contraction tiles on that path
+    "ragged_big_tiles": (workloads.MoESpec("ragged_big_tiles", T=4096, d=1000, h=1960, N=8, k=2,
+                                           capacity_factor=1.0, gate="noisy", renorm=True, dtype="bf16",
+                                           expert_bias=True, zipf_s=0.5), (0.01, 0.1)),
     "noisy_top2_bf16": (W["noisy_top2_bf16"], (0.0, 0.0)),
     "large_expert_top2_bf16": (W["large_expert_top2_bf16"], (0.0, 0.0)),
     "decode_top8_bf16": (W["decode_top8_bf16"], (0.0, 0.0)),
