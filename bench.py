@@ -113,6 +113,9 @@ def main() -> int:
     ap.add_argument("--workload", default="large_expert_top2_bf16")
     ap.add_argument("--weights", choices=["layer", "fp8"], default="layer",
                     help="expert weights in the layer's dtype, or block-FP8 (moe_forward_fp8; bf16 layers)")
+    ap.add_argument("--combine-in-ffn", action="store_true",
+                    help="moe_forward with the gate-weighted combine folded into the single-launch expert FFN "
+                         "(MOE_FLAG_COMBINE_IN_FFN; applies where that launch runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--skip-extras", action="store_true",
@@ -156,8 +159,12 @@ def main() -> int:
     torch.cuda.set_device(0)
     t_gen = time.perf_counter()
     inp = make_inputs(spec, seed)
-    dev = api.DeviceLayer(inp)
+    dev = api.DeviceLayer(inp, flags=_lib.MOE_FLAG_COMBINE_IN_FFN if args.combine_in_ffn else 0)
     fp8 = args.weights == "fp8"
+    # the flag takes effect where the single-launch FFN runs (its arrival
+    # counts then enlarge the workspace)
+    folded = (args.combine_in_ffn and not fp8 and
+              api.workspace_size(dev.desc) > api.workspace_size(api.desc_from_spec(spec)))
     if fp8:
         if spec.dtype != "bf16":
             print("--weights fp8 needs a bf16 workload", file=sys.stderr)
@@ -437,7 +444,8 @@ def main() -> int:
         "config": {"workload": spec.name, "T": T, "d": d, "h": h, "N": N, "k": k, "gate": spec.gate,
                    "capacity_factor": spec.capacity_factor, "renorm": spec.renorm,
                    "capacity": int(dev.C), "kept_rows": A, "experts_touched": U,
-                   "weights": "fp8_e4m3_block128" if fp8 else spec.dtype},
+                   "weights": "fp8_e4m3_block128" if fp8 else spec.dtype,
+                   "combine": "in_ffn_launch" if folded else "separate"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "stages": stages,

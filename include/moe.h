@@ -96,8 +96,23 @@ typedef struct moe_desc {
   int32_t dtype;          /* moe_dtype_t of the X-dtype arrays */
   int32_t proj_dim;       /* cosine gate: p (columns of proj); else 0 */
   float inv_temperature;  /* cosine gate: 1/tau; else ignored */
-  int32_t reserved;       /* must be 0 */
+  int32_t flags;          /* MOE_FLAG_* bits; 0 for the default path */
 } moe_desc_t;
+
+/* moe_forward (and moe_forward_noalloc): fold the gate-weighted combine into
+ * the single-launch expert FFN. Each GEMM2 tile stores its rows of y_perm
+ * agent-coherently and counts them per (token, 256-column tile); the tile
+ * that brings a token's last kept row writes that token's y on those
+ * columns, summing the kept rows in j order with the sequence moe_combine
+ * uses, so y is bit-identical to the default path. (The fusion is the
+ * operator fusion and memory reuse of "MoE架构：突破单卡算力瓶颈的密钥" §3.3.)
+ * It applies where the single-launch FFN runs (bf16, at least 64 rows per
+ * expert on average, h a multiple of 128, enough tiles, the whole chip) and
+ * k <= 8; elsewhere the flag changes nothing. The workspace then also holds
+ * T * ceil(d / 256) int32 arrival counts. On the measured layers it is
+ * slower than the separate combine, so it is off by default. Other entry
+ * points ignore it. */
+#define MOE_FLAG_COMBINE_IN_FFN 1
 
 /* Which entry point a workspace is sized for. */
 typedef enum moe_ws_kind {

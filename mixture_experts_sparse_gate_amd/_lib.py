@@ -14,6 +14,7 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = r
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_NOISY, MOE_GATE_COSINE = 0, 1, 2
 MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_FORWARD, MOE_WS_FFN, MOE_WS_AUX, MOE_WS_BACKWARD = 0, 1, 2, 3, 4, 5
+MOE_FLAG_COMBINE_IN_FFN = 1
 
 
 class MoeDesc(ctypes.Structure):
@@ -29,7 +30,7 @@ class MoeDesc(ctypes.Structure):
         ("dtype", c_int32),
         ("proj_dim", c_int32),
         ("inv_temperature", c_float),
-        ("reserved", c_int32),
+        ("flags", c_int32),
     ]
 
 

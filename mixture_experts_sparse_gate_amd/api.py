@@ -23,12 +23,12 @@ _DTYPES = {"f32": _lib.MOE_F32, "bf16": _lib.MOE_BF16}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
-def desc_from_spec(spec: MoESpec) -> MoeDesc:
+def desc_from_spec(spec: MoESpec, flags: int = 0) -> MoeDesc:
     return MoeDesc(T=spec.T, d=spec.d, h=spec.h, N=spec.N, k=spec.k,
                    capacity_factor=float(spec.capacity_factor), gate=_GATES[spec.gate],
                    renorm=int(bool(spec.renorm)), dtype=_DTYPES[spec.dtype],
                    proj_dim=int(spec.proj_dim), inv_temperature=float(spec.inv_temperature),
-                   reserved=0)
+                   flags=int(flags))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -235,10 +235,10 @@ class DeviceLayer:
     """Device copies of one layer's inputs (from a MoEInputs) plus the
     output buffers of every stage, ready to pass to the entry points."""
 
-    def __init__(self, inp, device="cuda"):
+    def __init__(self, inp, device="cuda", flags: int = 0):
         spec = inp.spec
         self.spec = spec
-        self.desc = desc_from_spec(spec)
+        self.desc = desc_from_spec(spec, flags)
         dt = TORCH_DTYPE[spec.dtype]
 
         def up(a, dtype=dt):

@@ -53,7 +53,8 @@ int ntiles_of(const moe_desc_t* d) {
 
 moe_status_t check_desc(const moe_desc_t* d) {
   if (!d) return fail(MOE_ERR_INVALID, "desc is NULL");
-  if (d->reserved != 0) return fail(MOE_ERR_INVALID, "desc->reserved must be 0");
+  if (d->flags & ~MOE_FLAG_COMBINE_IN_FFN)
+    return fail(MOE_ERR_INVALID, "desc->flags: unknown bits 0x%x", (unsigned)(d->flags & ~MOE_FLAG_COMBINE_IN_FFN));
   if (d->dtype != MOE_F32 && d->dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID, "dtype %d is not MOE_F32 or MOE_BF16", d->dtype);
   if (d->gate < MOE_GATE_SOFTMAX || d->gate > MOE_GATE_COSINE)
@@ -147,11 +148,13 @@ DispatchWs dispatch_ws(const moe_desc_t* d) {
 }
 
 struct ForwardWs {
-  size_t route, dispatch, ffn_counters, topk_idx, topk_w, count, off, row_of, token_of_row, H,
+  size_t route, dispatch, ffn_counters, arrive, topk_idx, topk_w, count, off, row_of, token_of_row, H,
       y_perm, bytes;
   int n_counters;
+  int arrive_per_token;  // > 0: the single-launch FFN also does the combine
 };
 int ffn_counters_of(const moe_desc_t* d);
+bool combine_in_ffn(const moe_desc_t* d);
 ForwardWs forward_ws(const moe_desc_t* d) {
   ForwardWs w{};
   const size_t Tk = (size_t)d->T * d->k, R = (size_t)rows_bound_of(d), s = elem_bytes(d);
@@ -165,6 +168,8 @@ ForwardWs forward_ws(const moe_desc_t* d) {
   w.dispatch = take(dispatch_ws(d).bytes);
   w.n_counters = ffn_counters_of(d);
   w.ffn_counters = take((size_t)w.n_counters * 4);
+  w.arrive_per_token = combine_in_ffn(d) ? moe::fused_combine_col_tiles(d->d) : 0;
+  w.arrive = take((size_t)d->T * w.arrive_per_token * 4);
   w.topk_idx = take(Tk * 4);
   w.topk_w = take(Tk * 4);
   w.count = take((size_t)d->N * 4);
@@ -288,13 +293,15 @@ moe_status_t do_route(const moe_desc_t* d, const void* x, const void* w_gate, co
 }
 
 // zero, zero_n: ints for the dispatch to clear on the way (the fused FFN's
-// counters), or null
+// counters), or null; zero_tok, zero_tok_n: ints per token to clear (the
+// folded combine's arrival counts), or null
 // hist32: the gate's per-32-token choice counts, or null (counted here)
 // caller_routing: idx comes from the caller (moe_dispatch), not the gate
 moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx, int32_t* count,
                          int32_t* off, int32_t* row_of, int32_t* token_of_row, void* x_perm,
                          void* ws, hipStream_t s, int32_t* zero = nullptr, int zero_n = 0,
-                         const int32_t* hist32 = nullptr, bool caller_routing = false) {
+                         const int32_t* hist32 = nullptr, bool caller_routing = false,
+                         int32_t* zero_tok = nullptr, int zero_tok_n = 0) {
   const DispatchWs dw = dispatch_ws(d);
   moe::DispatchParams p{};
   p.x = x;
@@ -316,6 +323,8 @@ moe_status_t do_dispatch(const moe_desc_t* d, const void* x, const int32_t* idx,
   p.elem_bytes = elem_bytes(d);
   p.zero = zero;
   p.zero_n = zero_n;
+  p.zero_tok = zero_tok;
+  p.zero_tok_n = zero_tok_n;
   p.hist32 = hist32;
   return hip_status(moe::launch_dispatch(p, s), "dispatch");
 }
@@ -369,6 +378,13 @@ int ffn_counters_of(const moe_desc_t* d) {
   return moe::fused_ffn_fits(g1, g2, d->dtype == MOE_BF16, avg_rows) ? moe::fused_ffn_counters(g1) : 0;
 }
 
+// moe_forward folds the combine into the single-launch FFN where the caller
+// asks for it (MOE_FLAG_COMBINE_IN_FFN), that launch applies, and k is
+// within its per-token batches
+bool combine_in_ffn(const moe_desc_t* d) {
+  return (d->flags & MOE_FLAG_COMBINE_IN_FFN) && ffn_counters_of(d) > 0 && d->k <= moe::kFusedCombineMaxK;
+}
+
 // The single-launch FFN deals its work to one queue per XCD of the full
 // chip (256 CUs in 8 XCDs), each queue drained by the blocks whose hardware
 // XCC_ID names it. A device that is a partition of the chip has fewer XCDs,
@@ -397,17 +413,23 @@ bool whole_chip_device() {
 // Events the expert FFN's launches record (moe_time_ffn_launches), or null.
 moe::LaunchEvents g_ffn_events;
 
+// comb: the combine to fold into the single-launch form (or null); *combined
+// (if given) tells whether it was folded in (else the caller combines).
 moe_status_t do_ffn(const moe_desc_t* d, const void* A1, const int32_t* token_of_row,
                     const int32_t* off, const void* W1, const void* b1, const void* W2,
-                    const void* b2, void* H, void* y_perm, int32_t* counters, bool cleared, hipStream_t s) {
+                    const void* b2, void* H, void* y_perm, int32_t* counters, bool cleared, hipStream_t s,
+                    const moe::FusedCombine* comb = nullptr, bool* combined = nullptr) {
   const bool bf = d->dtype == MOE_BF16;
   const int avg_rows = (int)((d->T * d->k) / d->N);
   const int max_rows = (int)capacity_of(d);
   moe::GemmParams g1, g2;
   ffn_gemms(d, A1, token_of_row, off, W1, b1, W2, b2, H, y_perm, &g1, &g2);
   const moe::LaunchEvents ev = g_ffn_events;
-  if (counters && moe::fused_ffn_fits(g1, g2, bf, avg_rows) && whole_chip_device())
-    return hip_status(moe::launch_fused_ffn(g1, g2, counters, !cleared, s, ev), "expert FFN");
+  if (combined) *combined = false;
+  if (counters && moe::fused_ffn_fits(g1, g2, bf, avg_rows) && whole_chip_device()) {
+    if (combined) *combined = comb != nullptr;
+    return hip_status(moe::launch_fused_ffn(g1, g2, counters, !cleared, s, ev, comb), "expert FFN");
+  }
   TRY(hip_status(moe::launch_grouped_gemm(g1, moe::GemmKind::kFfn1Gelu, bf, avg_rows, max_rows, s, {ev.start, nullptr}),
                  "expert GEMM1"));
   return hip_status(moe::launch_grouped_gemm(g2, moe::GemmKind::kFfn2, bf, avg_rows, max_rows, s, {nullptr, ev.stop}),
@@ -525,12 +547,21 @@ moe_status_t forward_impl(const moe_desc_t* desc, const moe_layer_tensors_t* t, 
   // routing and row maps only: GEMM1 gathers its rows from x itself
   // (the dispatch also clears the fused FFN's counters)
   int32_t* counters = fw.n_counters ? at<int32_t>(ws, fw.ffn_counters) : nullptr;
+  // the combine folded into the single-launch FFN (bf16 weights, on request):
+  // its per-(token, column tile) arrival counts are cleared by the dispatch
+  const bool fold = !w8 && fw.arrive_per_token > 0;
+  int32_t* arrive = fold ? at<int32_t>(ws, fw.arrive) : nullptr;
   TRY(do_dispatch(desc, t->x, idx, count, off, row_of, tor, nullptr, at<char>(ws, fw.dispatch), s, counters,
-                  fw.n_counters, hist));
-  if (w8)
+                  fw.n_counters, hist, false, arrive, fold ? fw.arrive_per_token : 0));
+  bool combined = false;
+  if (w8) {
     TRY(do_ffn_w8(desc, t->x, tor, off, w8->W1q, w8->S1, t->b1, w8->W2q, w8->S2, t->b2, H, y_perm, s));
-  else
-    TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s));
+  } else {
+    const moe::FusedCombine comb{row_of, tor, w, t->y, arrive, (int)desc->T, desc->k};
+    TRY(do_ffn(desc, t->x, tor, off, t->W1, t->b1, t->W2, t->b2, H, y_perm, counters, true, s,
+               fold ? &comb : nullptr, &combined));
+  }
+  if (combined) return MOE_OK;
   return do_combine(desc, y_perm, row_of, w, t->y, s);
 }
 

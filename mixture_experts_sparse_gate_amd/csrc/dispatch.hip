@@ -210,6 +210,8 @@ __global__ __launch_bounds__(kBlock) void rows_kernel(DispatchParams p, int ntil
   // this tile's choices, as per-wave bitmasks per expert
   const int t = tile * kDispatchTile + threadIdx.x;
   const bool live = t < p.T;
+  if (live && p.zero_tok)
+    for (int i = 0; i < p.zero_tok_n; ++i) p.zero_tok[(int64_t)t * p.zero_tok_n + i] = 0;
   if (live) {
     for (int j = 0; j < k; ++j) {
       const int e = p.topk_idx[t * k + j];

@@ -60,6 +60,11 @@ template <> struct Mfma<float> {
   }
 };
 
+// cache-policy operand of the buffer builtins: sc1, agent scope (the access
+// is coherent across the XCDs' L2s, the form the compiler gives agent-scope
+// atomic loads and stores)
+constexpr int kCpolSc1 = 16;
+
 // 16 bytes per lane from the buffer at byte offset voff straight into LDS:
 // lane l writes dst + 16 l (dst is wave-uniform). Out-of-range reads write zeros.
 __device__ inline void lds_load16(__amdgpu_buffer_rsrc_t r, lds_void* dst, int voff) {
@@ -196,11 +201,13 @@ template <> struct Pack<float> {
 // All threads of the block call it with the same arguments; the LDS
 // objects are the block's (MOE_GEMM_LDS). at_k_end() runs between the K
 // loop and the epilogue. bscale: the block scales of W8 weights (GemmW8),
-// else unused.
+// else unused. coherent_out: the outputs are stored agent-coherently (sc1),
+// for blocks on other XCDs to read once the stores have completed.
 template <class C, class AtKEnd>
 __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* st0, char* st1, char* st2,
                                           char* st3, char* sa0, char* sa1, int g, int row_lo, int row_hi,
-                                          int n0, bool tail_tile, const float* bscale, AtKEnd&& at_k_end) {
+                                          int n0, bool tail_tile, const float* bscale, AtKEnd&& at_k_end,
+                                          bool coherent_out = false) {
   using E = typename C::Elem;
   using O = typename C::Out;
   constexpr int CE = C::CE, KC = C::KC, BK = C::BK, BM = C::BM, BN = C::BN, ES = C::ES, S = C::S;
@@ -564,8 +571,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         const int rr = t * RPI + lane / CPR, ch = lane % CPR;
         const u32x4 val = *(lds_u32x4*)(reg + rr * CPR * 16 + ((ch ^ swz_c<OB>(rr)) * 16));
         const int col = ccol0 + ch * (16 / OB);
-        if (frow + rr < row_hi && col < Ncols)
-          *reinterpret_cast<u32x4*>(Cp + (int64_t)(frow + rr) * p.ldc + col) = val;
+        if (frow + rr < row_hi && col < Ncols) {
+          if (coherent_out) {
+            // the slice's 32 rows as one buffer range
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cp + (int64_t)frow * p.ldc, (uint32_t)(32 * p.ldc * OB));
+            __builtin_amdgcn_raw_buffer_store_b128(val, rc, (rr * (int)p.ldc + col) * OB, 0, kCpolSc1);
+          } else {
+            *reinterpret_cast<u32x4*>(Cp + (int64_t)(frow + rr) * p.ldc + col) = val;
+          }
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -715,7 +729,63 @@ struct FusedFfn {
   // [kNumXcds] queues, the status word (bit 0: a wait for H expired), then
   // ready[row tiles]: zero at launch
   int32_t* counters;
+  FusedCombine comb;  // the folded combine (fused_ffn_kernel<C, true>)
 };
+
+// The combine of the tokens a GEMM2 tile completed (fin[0, nfin)), on the
+// tile's columns [n0, n0 + 256): y[t, c] = the sum over kept j, in j order,
+// of topk_w[t, j] * y_perm[row_of[t, j], c] in fp32 (one fma per term, the
+// sequence combine_kernel uses), rounded once to bf16. Each wave takes every
+// NW-th token, KB rows per token and 16 / KB tokens per batch with all their
+// loads in flight; a lane covers 4 columns. y_perm rows may have been stored
+// by blocks on other XCDs: they are read agent-coherently (sc1).
+template <int KB, int NW>
+__device__ void combine_finished(const int32_t* row_of, const float* topk_w, bf16* y, int k, const bf16* yp,
+                                 int ldc, int Ncols, int n0, const int* fin, int nfin, int wave, int lane) {
+  constexpr int U = 16 / KB;  // tokens per batch
+  const int col = n0 + lane * 4;
+  const bool live = col < Ncols;
+  for (int f0 = wave; f0 < nfin; f0 += NW * U) {
+    int rows[U][KB];
+    float w[U][KB];
+    u32x2 v[U][KB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = f0 + u * NW;
+      const int t = f < nfin ? fin[f] : 0;
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        const bool has = f < nfin && j < k;
+        rows[u][j] = has ? row_of[(int64_t)t * k + j] : -1;
+        w[u][j] = has ? topk_w[(int64_t)t * k + j] : 0.f;
+        v[u][j] = u32x2{0u, 0u};
+        if (rows[u][j] >= 0 && live) {
+          const uint64_t q = __hip_atomic_load(
+              reinterpret_cast<const uint64_t*>(yp + (int64_t)rows[u][j] * ldc + col), __ATOMIC_RELAXED,
+              __HIP_MEMORY_SCOPE_AGENT);
+          v[u][j] = u32x2{(uint32_t)q, (uint32_t)(q >> 32)};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int f = f0 + u * NW;
+      if (f >= nfin) break;  // wave-uniform
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KB; ++j) {
+        if (rows[u][j] < 0) continue;  // wave-uniform
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t wd = v[u][j][i >> 1];
+          const float yv = __uint_as_float((i & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+          acc[i] = __builtin_fmaf(w[u][j], yv, acc[i]);
+        }
+      }
+      if (live) Store<bf16>::four(y + (int64_t)fin[f] * Ncols + col, acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+}
 
 constexpr uint32_t kHwRegXccId = (3u << 11) | 20u;  // s_getreg: XCC_ID[3:0]
 constexpr int kFusedMaxGroups = 256;
@@ -724,7 +794,9 @@ constexpr int kFusedReady = kNumXcds + 1;   // index of ready[0]
 // polls of a GEMM2 tile's wait (s_sleep 4 each, about 0.1 s in all)
 constexpr int kFusedMaxPolls = 1 << 20;
 
-template <class C>
+// FOLD: GEMM2 tiles also do the gate-weighted combine (f.comb); see
+// FusedCombine.
+template <class C, bool FOLD>
 __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
   constexpr int BM = C::BM, BN = C::BN, TBM = C::TBM;
   static_assert(C::HAS_TAIL, "tail row tiles follow the full ones");
@@ -734,6 +806,8 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
   __shared__ int g_lo[kFusedMaxGroups], g_hi[kFusedMaxGroups], g_ef[kFusedMaxGroups], g_et[kFusedMaxGroups];
   __shared__ int tot[2];
   __shared__ int sched[9];
+  __shared__ int fin[FOLD ? BM : 1];  // tokens a GEMM2 tile completed (FOLD)
+  __shared__ int nfin;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int xcc = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kNumXcds - 1));
   if (wave == 0) {
@@ -848,7 +922,23 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
     }
     __syncthreads();
     const int kind = __builtin_amdgcn_readfirstlane(sched[1]);
-    if (kind < 0) break;
+    if (kind < 0) {
+      if constexpr (FOLD) {
+        // leaving: zero rows of y for the tokens whose every choice was
+        // dropped (no tile completes them), every NW-th token of the grid
+        constexpr int NW = C::THREADS / kWave;
+        const int d = fp->g2.Ncols, T = fp->comb.T, k = fp->comb.k;
+        const int32_t* row_of = fp->comb.row_of;
+        bf16* y = static_cast<bf16*>(fp->comb.y);
+        for (int t = blockIdx.x * NW + wave; t < T; t += gridDim.x * NW) {
+          bool any = false;
+          for (int j = 0; j < k; ++j) any |= row_of[(int64_t)t * k + j] >= 0;
+          if (any) continue;  // wave-uniform
+          for (int q = lane; q < d / 8; q += kWave) store16(y + (int64_t)t * d + q * 8, u32x4{0u, 0u, 0u, 0u});
+        }
+      }
+      break;
+    }
     const int g = __builtin_amdgcn_readfirstlane(sched[2]);
     const int row_lo = __builtin_amdgcn_readfirstlane(sched[3]);
     const int row_hi = __builtin_amdgcn_readfirstlane(sched[4]);
@@ -877,9 +967,17 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
       const __attribute__((address_space(4))) GemmParams* pp = &fp->g2;
       const int cols = min(BN, pp->Ncols - n0), cpr = cols / 8, rows = row_hi - row_lo;
       bf16* out = static_cast<bf16*>(pp->C);
-      for (int i = tid; i < rows * cpr; i += C::THREADS)
-        store16(out + (int64_t)(row_lo + i / cpr) * pp->ldc + n0 + (i % cpr) * 8,
-                u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u});
+      for (int i = tid; i < rows * cpr; i += C::THREADS) {
+        bf16* q = out + (int64_t)(row_lo + i / cpr) * pp->ldc + n0 + (i % cpr) * 8;
+        if constexpr (FOLD) {
+          // read by the folded combine, possibly on another XCD
+          uint64_t* q8 = reinterpret_cast<uint64_t*>(q);
+          __hip_atomic_store(q8, 0x7FC07FC07FC07FC0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(q8 + 1, 0x7FC07FC07FC07FC0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          store16(q, u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u});
+        }
+      }
       if (tid == 0) next = __hip_atomic_fetch_add(fp->counters + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     } else {
       // one copy of the tile code for both GEMMs
@@ -889,12 +987,46 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
                      if (tid == 0)
                        next = __hip_atomic_fetch_add(fp->counters + xcc, 1, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-                   });
+                   }, FOLD && kind == 2);
     }
     if (kind == 1) {
       wait_vmcnt<0>();  // this thread's H stores are in the L2
       __syncthreads();  // ... and every thread's
       if (tid == 0) __hip_atomic_fetch_add(ready + rid, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (FOLD) {
+      if (kind == 2) {
+        // every thread's agent-coherent y_perm stores of the tile have
+        // completed; then one arrival per row for its (token, column tile):
+        // the arrival that makes a token's count reach its number of kept
+        // choices completes that token's combine on these columns
+        const int32_t* row_of = fp->comb.row_of;
+        const int32_t* tor = fp->comb.token_of_row;
+        int32_t* arrive = fp->comb.arrive;
+        const int k = fp->comb.k;
+        wait_vmcnt<0>();
+        if (tid == 0) nfin = 0;
+        __syncthreads();
+        const int NT2 = (fp->g2.Ncols + BN - 1) / BN, ct = n0 / BN;
+        for (int i = tid; i < row_hi - row_lo; i += C::THREADS) {
+          const int t = tor[row_lo + i] / k;
+          int kept = 0;
+          for (int j = 0; j < k; ++j) kept += row_of[(int64_t)t * k + j] >= 0;
+          const int before =
+              __hip_atomic_fetch_add(arrive + (int64_t)t * NT2 + ct, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (before + 1 == kept) fin[atomicAdd(&nfin, 1)] = t;
+        }
+        __syncthreads();
+        const int n = nfin;
+        constexpr int NW = C::THREADS / kWave;
+        const bf16* yp = static_cast<const bf16*>(fp->g2.C);
+        const float* tw = fp->comb.topk_w;
+        bf16* y = static_cast<bf16*>(fp->comb.y);
+        const int ldc = (int)fp->g2.ldc, Nc = fp->g2.Ncols;
+        if (k <= 2) combine_finished<2, NW>(row_of, tw, y, k, yp, ldc, Nc, n0, fin, n, wave, lane);
+        else if (k <= 4) combine_finished<4, NW>(row_of, tw, y, k, yp, ldc, Nc, n0, fin, n, wave, lane);
+        else combine_finished<8, NW>(row_of, tw, y, k, yp, ldc, Nc, n0, fin, n, wave, lane);
+      }
     }
     if (tid == 0) sched[0] = next;
   }
@@ -983,19 +1115,25 @@ bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16_, int 
          g1.M > 0 && whole_lines;
 }
 
+int fused_combine_col_tiles(int d) { return (d + FusedCfg::BN - 1) / FusedCfg::BN; }
+
 hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
-                            hipStream_t s, LaunchEvents ev) {
+                            hipStream_t s, LaunchEvents ev, const FusedCombine* comb) {
   if (clear) {
     const int n = fused_ffn_counters(g1);
     hipLaunchKernelGGL(fill_kernel, dim3((n + 255) / 256), dim3(256), 0, s, counters, n);
   }
-  FusedFfn f{g1, g2, counters};
+  if (comb && comb->k > kFusedCombineMaxK) return hipErrorInvalidValue;
+  FusedFfn f{g1, g2, counters, comb ? *comb : FusedCombine{}};
   // one block per CU (a multiple of the XCD count)
-  if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, ev.start,
-                          ev.stop, 0, f);
-  else
-    hipLaunchKernelGGL(fused_ffn_kernel<FusedCfg>, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, f);
+  auto launch = [&](auto kernel) {
+    if (ev.start || ev.stop)
+      hipExtLaunchKernelGGL(kernel, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, ev.start, ev.stop, 0, f);
+    else
+      hipLaunchKernelGGL(kernel, dim3(kNumCUs), dim3(FusedCfg::THREADS), 0, s, f);
+  };
+  if (comb) launch(fused_ffn_kernel<FusedCfg, true>);
+  else launch(fused_ffn_kernel<FusedCfg, false>);
   return hipGetLastError();
 }
 

@@ -60,6 +60,8 @@ struct DispatchParams {
   int32_t* token_of_row;    // [R]
   void* x_perm;             // [R, d] or null (skip the copy)
   int32_t* zero;            // zero_n ints to clear on the way (or null)
+  int32_t* zero_tok;        // zero_tok_n ints per token to clear on the way (or null)
+  int zero_tok_n;
   // the gate's per-32-token choice counts (GateParams::hist), or null: then
   // the dispatch counts them itself
   const int32_t* hist32;
@@ -126,8 +128,24 @@ hipError_t launch_grouped_gemm(const GemmParams& p, GemmKind kind, bool bf16, in
 // if clear, else by the caller earlier on the stream.
 bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16, int avg_rows);
 int fused_ffn_counters(const GemmParams& g1);
+// The gate-weighted combine folded into the single-launch FFN: each GEMM2
+// tile stores its y_perm rows agent-coherently and counts them per (token,
+// column tile); the tile that brings a token's last kept row sums that
+// token's kept rows of the column tile in j order, exactly as
+// launch_combine does, into y. Blocks leaving the launch write zero rows
+// for tokens with every choice dropped. k <= kFusedCombineMaxK.
+struct FusedCombine {
+  const int32_t* row_of;        // [T*k]
+  const int32_t* token_of_row;  // [R]
+  const float* topk_w;          // [T, k]
+  void* y;                      // [T, d] bf16
+  int32_t* arrive;              // [T * fused_combine_col_tiles(d)], zero at launch
+  int T, k;
+};
+constexpr int kFusedCombineMaxK = 8;
+int fused_combine_col_tiles(int d);
 hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
-                            hipStream_t s, LaunchEvents ev = {});
+                            hipStream_t s, LaunchEvents ev = {}, const FusedCombine* comb = nullptr);
 // *out = the status word of the fused launch that last used `counters`
 // (bit 0: a GEMM2 tile's wait for its rows of H expired and its outputs were
 // set to NaN); counters null: *out = 0

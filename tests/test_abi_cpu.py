@@ -49,7 +49,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_struct_layout_matches_header(lib):
-    # T(8) d h N k(16) cf(8) gate renorm dtype proj_dim(16) inv_temp reserved(8) = 56 bytes
+    # T(8) d h N k(16) cf(8) gate renorm dtype proj_dim(16) inv_temp flags(8) = 56 bytes
     assert ctypes.sizeof(_lib.MoeDesc) == 56
     assert ctypes.sizeof(_lib.MoeLayerTensors) == 19 * 8
 
@@ -93,6 +93,28 @@ def test_workspace_sizes(lib):
         assert n.value % 256 == 0 and n.value >= ((T + 255) // 256) * d.N * 4
 
 
+def _forward_ws(lib, spec, flags):
+    d = desc_from_spec(spec, flags)
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(d), _lib.MOE_WS_FORWARD, ctypes.byref(n)) == _lib.MOE_OK
+    return n.value
+
+
+def test_combine_in_ffn_flag_sizes_the_arrival_counts(lib):
+    # where the single-launch FFN applies, the folded combine adds
+    # T * ceil(d / 256) int32 arrival counts (256-byte aligned) to the
+    # forward workspace; where it does not (decode: < 64 rows per expert;
+    # the fp32 layer; h not a multiple of 128) the flag changes nothing
+    for name in ("noisy_top2_bf16", "large_expert_top2_bf16", "cosine_zipf_top4_bf16"):
+        spec = workloads.get(name)
+        extra = spec.T * ((spec.d + 255) // 256) * 4
+        extra = (extra + 255) // 256 * 256
+        assert _forward_ws(lib, spec, _lib.MOE_FLAG_COMBINE_IN_FFN) == _forward_ws(lib, spec, 0) + extra, name
+    for spec in (workloads.get("decode_top8_bf16"), workloads.get("tiny_top1_f32"),
+                 workloads.get("noisy_top2_bf16").with_(h=2056)):
+        assert _forward_ws(lib, spec, _lib.MOE_FLAG_COMBINE_IN_FFN) == _forward_ws(lib, spec, 0), spec.name
+
+
 def _bad(spec, **kw):
     d = desc_from_spec(spec)
     for k_, v in kw.items():
@@ -103,7 +125,7 @@ def _bad(spec, **kw):
 @pytest.mark.parametrize("field,value", [
     ("N", 0), ("N", 257), ("k", 0), ("k", 9), ("T", 0), ("capacity_factor", 0.0),
     ("capacity_factor", float("nan")), ("capacity_factor", float("inf")), ("d", 12), ("h", 1020),
-    ("gate", 3), ("dtype", 2), ("renorm", 2), ("reserved", 1),
+    ("gate", 3), ("dtype", 2), ("renorm", 2), ("flags", 2), ("flags", -1),
 ])
 def test_invalid_desc_is_rejected(lib, field, value):
     d = _bad(workloads.get("decode_top8_bf16").with_(N=8), **{field: value})

@@ -28,14 +28,18 @@ CASES = {
     # full size: the expert FFN is the single persistent launch, whose work
     # counters the captured dispatch clears on every replay
     "noisy_top2_bf16_full": W["noisy_top2_bf16"],
+    # the same with the combine folded into that launch: its arrival counts
+    # are cleared by the captured dispatch too
+    "noisy_top2_bf16_full_combine_in_ffn": W["noisy_top2_bf16"],
 }
+FLAGS = {"noisy_top2_bf16_full_combine_in_ffn": _lib.MOE_FLAG_COMBINE_IN_FFN}
 OUTPUTS = ("y", "topk_idx", "topk_w", "row_of", "expert_off")
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_graph_replays_match_eager(name):
     spec = CASES[name]
-    dev = api.DeviceLayer(make_inputs(spec, 11))
+    dev = api.DeviceLayer(make_inputs(spec, 11), flags=FLAGS.get(name, 0))
     say(f"[case] graph {spec.name} T={spec.T} d={spec.d} h={spec.h} N={spec.N} k={spec.k}")
     dev.run_forward(inspect=True)
     torch.cuda.synchronize()

@@ -230,6 +230,21 @@ def test_fused_ffn_forward_equals_stages(name):
         torch.cuda.synchronize()
         assert_ffn_status_clear(dev)
         assert torch.equal(dev.y, y_st)
+    # the combine folded into the same launch (MOE_FLAG_COMBINE_IN_FFN): every
+    # row of y is written by the launch itself (NaN before the call), bit for
+    # bit the separate combine's, fully dropped tokens included
+    fold = api.desc_from_spec(spec, _lib.MOE_FLAG_COMBINE_IN_FFN)
+    fold_ws = api.workspace(fold, _lib.MOE_WS_FORWARD)
+    assert fold_ws.numel() > dev.ws.numel(), "the flag adds the arrival counts"
+    for rep in range(3):
+        dev.y.fill_(float("nan"))
+        say(f"[case] forward with the combine in the FFN launch {spec.name} call {rep}")
+        api.forward(fold, dev.layer_tensors(inspect=True), fold_ws)
+        torch.cuda.synchronize()
+        st = api.ffn_status(fold, fold_ws)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert torch.equal(dev.y, y_st), f"folded combine, call {rep}"
 
 
 EDGE = {
