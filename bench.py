@@ -672,14 +672,32 @@ def _short(name: str) -> str:
     m = re.search(r"CfgI(\w+?)EEEEEvNS_10GemmParamsE", name)
     if m:
         return "grouped_gemm_kernel<" + m.group(1) + ">"
-    m = re.search(r"fused_ffn_kernelINS0_3CfgI(\w+?)EEEEEvNS0_8FusedFfnE", name)
+    m = re.search(r"fused_ffn_kernelINS0_3CfgI(\w+?)EEELb([01])EEEvNS0_8FusedFfnE", name)
     if m:
-        return "fused_ffn_kernel<" + m.group(1) + ">"
+        return "fused_ffn_kernel<" + m.group(1) + (", combine in launch>" if m.group(2) == "1" else ">")
+    m = re.search(r"fused_ffn_kernel<.*?Cfg<([^>]*)>, (true|false)>", name)
+    if m:
+        return "fused_ffn_kernel<" + m.group(1) + (", combine in launch>" if m.group(2) == "true" else ">")
+    # backward GEMMs: tile, operand layouts, epilogue, output type, ragged K
+    lay, epi = {"0": "Kc", "1": "Ks"}, {"0": "plain", "1": "U+H", "2": "dU"}
+    m = re.search(r"bwd_gemm_kernelILi(\d+)ELNS_9BwdLayoutE(\d)ELS\d+_(\d)ELNS_6BwdEpiE(\d)E(\w+?)Lb(\d)E", name)
+    if m:
+        ts, a_, b_, e_, o_, rk = m.groups()
+        o_ = "bf16" if "DF16b" in o_ else "f32"
+        return f"bwd_gemm_kernel<{ts} A:{lay[a_]} B:{lay[b_]} {epi[e_]} {o_}{' raggedK' if rk == '1' else ''}>"
+    m = re.search(r"bwd_gemm_kernel<(\d+), \(moe::BwdLayout\)(\d), \(moe::BwdLayout\)(\d), "
+                  r"\(moe::BwdEpi\)(\d), (\w+), (true|false)>", name)
+    if m:
+        ts, a_, b_, e_, o_, rk = m.groups()
+        o_ = "bf16" if "bf16" in o_ or "bfloat" in o_ else "f32"
+        return f"bwd_gemm_kernel<{ts} A:{lay[a_]} B:{lay[b_]} {epi[e_]} {o_}{' raggedK' if rk == 'true' else ''}>"
     for key in ("gate_logits_kernel", "gate_select_kernel", "cosine_select_kernel", "count_kernel",
                 "scan_kernel", "slots_kernel", "permute_kernel", "combine_kernel", "fill_kernel",
                 "gate_fused_kernel", "gate_partial_kernel", "gate_finish_kernel", "rows_kernel",
                 "copy_kernel", "mfma_kernel", "ffn_status_kernel", "cosine_gate_kernel", "aux_partial_kernel",
-                "aux_final_kernel", "quantize_fp8_kernel"):
+                "aux_final_kernel", "quantize_fp8_kernel", "bwd_token_kernel", "scale_rows_kernel",
+                "gate_grad_partial_kernel", "gate_grad_final_kernel", "importance_grad_kernel",
+                "column_sum_partial_kernel", "colsum_kernel", "probe"):
         if key in name:
             return key
     return name[:70]
