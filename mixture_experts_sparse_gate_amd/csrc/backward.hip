@@ -666,11 +666,15 @@ hipError_t launch_tiles(const BwdGemmParams& p, int64_t tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256 x 256 tiles where they give at least one per CU, else 128 x 128
+// 256 x 256 tiles where they give at least one per CU and the groups hold
+// at least 128 rows on average (fewer rows leave big tiles mostly empty, and
+// such layers are bound by their weight and gradient bytes, which two
+// blocks per CU of 128 x 128 tiles stream better), else 128 x 128
 template <BwdLayout LA, BwdLayout LB, BwdEpi EPI, typename O, bool RK>
 hipError_t launch_bwd(const BwdGemmParams& p, hipStream_t s) {
   const int64_t big = bwd_tiles<256>(p, RK);
-  if (big >= kBwdBigTileMin) return launch_tiles<256, LA, LB, EPI, O, RK>(p, big, s);
+  const int64_t avg_rows = p.groups > 0 ? (int64_t)(RK ? p.a_rows : p.M) / p.groups : 0;
+  if (big >= kBwdBigTileMin && avg_rows >= 128) return launch_tiles<256, LA, LB, EPI, O, RK>(p, big, s);
   const int64_t tiles = bwd_tiles<128>(p, RK);
   if (tiles <= 0) return hipSuccess;
   return launch_tiles<128, LA, LB, EPI, O, RK>(p, tiles, s);
