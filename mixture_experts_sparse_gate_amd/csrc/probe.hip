@@ -4,9 +4,9 @@
 //   copy_kernel  a plain device copy with 16-byte loads and stores (the
 //                STREAM "copy" pattern): HBM bandwidth for mixed read/write
 //                traffic once the buffers exceed the 256 MB last-level cache
-//   mfma_kernel  bf16 32x32x16 MFMAs on register operands only, four
-//                independent accumulators per wave: the matrix cores' rate
-//                with no memory traffic at all
+//   mfma_kernel  bf16 32x32x16 MFMAs on register operands only (four sets
+//                of hashed values), four independent accumulators per wave:
+//                the matrix cores' rate with no memory traffic at all
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,15 +36,35 @@ __global__ __launch_bounds__(kCopyBlock) void copy_kernel(const u32x4* __restric
 
 constexpr int kMfmaWaves = 8;  // per block: two waves per SIMD
 
+// a bf16 pair of finite values from 32 hashed bits: random signs and
+// mantissas, exponents within 2^-7 .. 2^0 (so that the sums stay finite)
+__device__ inline uint32_t bf16_pair(uint32_t r) {
+  const uint32_t lo = (r & 0x8000u) | ((0x78u + ((r >> 8) & 7u)) << 7) | (r & 0x7Fu);
+  const uint32_t hi = ((r >> 16) & 0x8000u) | ((0x78u + ((r >> 24) & 7u)) << 7) | ((r >> 16) & 0x7Fu);
+  return lo | (hi << 16);
+}
+
 __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(int iters, float* sink) {
   const int lane = lane_id();
-  // operands that the compiler cannot fold: built from the lane index
-  u32x4 a, b;
+  // four operand sets of hashed bf16 values, one per accumulator, so that
+  // consecutive MFMAs see different data (as a GEMM's do: the matrix cores'
+  // power, and so the clock under the board's power cap, depends on it);
+  // built from the lane and wave indices, which the compiler cannot fold
+  const uint32_t seed = (uint32_t)(lane + 64 * (threadIdx.x / kWave) + 512 * blockIdx.x) * 2654435761u;
+  u32x4 a[4], b[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a[i] = 0x3F803F80u ^ (uint32_t)(lane * (i + 1));
-    b[i] = 0x3F003F00u ^ (uint32_t)(lane + i);
-  }
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h = seed ^ (uint32_t)(0x9E3779B9u * (uint32_t)(8 * c + i + 1));
+      h ^= h >> 15;
+      h *= 0x2C1B3C6Du;
+      h ^= h >> 12;
+      a[c][i] = bf16_pair(h);
+      h *= 0x297A2D39u;
+      h ^= h >> 15;
+      b[c][i] = bf16_pair(h);
+    }
   f32x16 acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
@@ -53,8 +73,8 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void mfma_kernel(int iters, flo
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                       acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[c]),
+                                                       __builtin_bit_cast(bf16x8, b[c]), acc[c], 0, 0, 0);
   }
   float s = 0.f;
 #pragma unroll
