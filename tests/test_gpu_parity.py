@@ -166,6 +166,11 @@ FUSED = {
     "skew16_few_tiles": workloads.MoESpec("skew16_few_tiles", T=3000, d=1024, h=2048, N=16, k=2,
                                           capacity_factor=2.0, gate="softmax", renorm=True, dtype="bf16",
                                           zipf_s=1.5),
+    # skewed demand with contractions long enough for the ping-pong K loop
+    # (96 K-steps in both GEMMs): empty and small groups, tail tiles
+    "zipf16_pingpong": workloads.MoESpec("zipf16_pingpong", T=4096, d=3072, h=3072, N=16, k=2,
+                                         capacity_factor=2.0, gate="softmax", renorm=True, dtype="bf16",
+                                         zipf_s=1.5),
     # eight choices per token (the folded combine's widest batch), with drops
     "k8_drops": workloads.MoESpec("k8_drops", T=2048, d=1024, h=1024, N=16, k=8, capacity_factor=0.9,
                                   gate="softmax", renorm=True, dtype="bf16", zipf_s=0.7),
