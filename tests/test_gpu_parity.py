@@ -171,6 +171,11 @@ FUSED = {
     "zipf16_pingpong": workloads.MoESpec("zipf16_pingpong", T=4096, d=3072, h=3072, N=16, k=2,
                                          capacity_factor=2.0, gate="softmax", renorm=True, dtype="bf16",
                                          zipf_s=1.5),
+    # the ping-pong loop with remainder steps: GEMM1 runs 98 K-steps (3112 =
+    # 97 x 32 + 8, a partial last step), GEMM2 100; partial column tiles
+    "pingpong_ragged_k": workloads.MoESpec("pingpong_ragged_k", T=2048, d=3112, h=3200, N=8, k=2,
+                                           capacity_factor=1.25, gate="noisy", renorm=True, dtype="bf16",
+                                           expert_bias=True),
     # eight choices per token (the folded combine's widest batch), with drops
     "k8_drops": workloads.MoESpec("k8_drops", T=2048, d=1024, h=1024, N=16, k=8, capacity_factor=0.9,
                                   gate="softmax", renorm=True, dtype="bf16", zipf_s=0.7),
