@@ -71,6 +71,8 @@ __device__ inline void wait_loads_and_lds() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+
 template <BwdLayout L, int TS> struct Operand;
 
 // Tile of TS rows (of M or N) x 32 K, K contiguous: row x at byte x * 64,
@@ -340,6 +342,50 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
 
   // ---- epilogue: the lane holds D[n][m] for rows m = m0 + WTM wm + 32 j +
   // lane % 32 and columns n = n0 + 64 wn + 32 i + 8 q + 4 (lane / 32) + 0..3
+  if constexpr (EPI == BwdEpi::kPlain && std::is_same_v<O, float>) {
+    // fp32 outputs (dx rows, weight gradients): each 32-row slice of the
+    // wave's tile goes through a per-wave LDS region (32 rows of 256 bytes,
+    // 16-byte chunk c of row r at c ^ (r % 16)) and back as 16-byte pieces
+    // of rows, 16 lanes per row, so that every store instruction writes
+    // whole 256-byte row segments (stored from the MFMA layout, one
+    // instruction would cover 32 rows with 32 bytes each)
+    __syncthreads();  // every wave is done reading the stage buffers
+    constexpr int REG = 32 * 64 * 4;
+    constexpr int PER = 2 * OPB / REG;  // wave regions per stage buffer
+    static_assert(PER >= 1 && (THREADS / kWave) <= 4 * PER, "epilogue regions fit the stage buffers");
+    const int bsel = wave / PER;
+    char* const reg = (bsel == 0 ? st0 : bsel == 1 ? st1 : bsel == 2 ? st2 : st3) + (wave % PER) * REG;
+    const int lrow = lane & 31;
+    const int cbase_col = n0 + wn * 64;
+    float* const Cf = static_cast<float*>(p.C) + (RAGGED_K ? (int64_t)g * p.strideC : 0);
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int frow = m0 + wm * T::WTM + 32 * j;
+      if (frow >= m1) break;  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = 8 * i + 2 * q + (lane >> 5);  // the lane's 16-byte chunk of its row
+          *(lds_f32x4*)(reg + lrow * 256 + ((ch ^ (lrow & 15)) * 16)) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rr = 4 * t + (lane >> 4), ch = lane & 15;
+        const f32x4 v = *(lds_f32x4*)(reg + rr * 256 + ((ch ^ (rr & 15)) * 16));
+        const int col = cbase_col + 4 * ch;
+        if (frow + rr < m1 && col < p.N) *reinterpret_cast<f32x4*>(Cf + (int64_t)(frow + rr) * p.ldc + col) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    return;
+  }
   const int mrow = m0 + wm * T::WTM + (lane & 31);
   const int ncol = n0 + wn * 64 + 4 * (lane >> 5);
   const int64_t cbase = RAGGED_K ? (int64_t)g * p.strideC : 0;
