@@ -72,6 +72,7 @@ __device__ inline void wait_loads_and_lds() {
 }
 
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2w;
 
 template <BwdLayout L, int TS> struct Operand;
 
@@ -383,6 +384,137 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    return;
+  }
+  if constexpr (EPI == BwdEpi::kDualGelu) {
+    // U = acc + b1 and H = GELU(U), both bf16: each 32-row slice of the
+    // wave's tile goes through two per-wave LDS regions (32 rows of 128
+    // bytes, 16-byte chunk c of row r at c ^ (r % 8)) and back as 16-byte
+    // pieces of rows, 8 lanes per row, so that the stores write whole
+    // 128-byte row segments
+    __syncthreads();  // every wave is done reading the stage buffers
+    constexpr int REG = 2 * 32 * 128;
+    constexpr int PER = 2 * OPB / REG;
+    static_assert(PER >= 1 && (THREADS / kWave) <= 4 * PER, "epilogue regions fit the stage buffers");
+    const int bsel = wave / PER;
+    char* const ru = (bsel == 0 ? st0 : bsel == 1 ? st1 : bsel == 2 ? st2 : st3) + (wave % PER) * REG;
+    char* const rh = ru + 32 * 128;
+    const int lrow = lane & 31;
+    const int cb = n0 + wn * 64;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int frow = m0 + wm * T::WTM + 32 * j;
+      if (frow >= m1) break;  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = cb + 32 * i + 8 * q + 4 * (lane >> 5);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+          if (p.bias && n < p.N) {
+            const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.bias) + (int64_t)g * p.N + n);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] += chunk_elem<bf16>(u32x4{bb[0], bb[1], 0u, 0u}, r);
+          }
+          const int off = lrow * 128 + (((4 * i + q) ^ (lrow & 7)) * 16) + 8 * (lane >> 5);
+          *(lds_u32x2w*)(ru + off) = u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
+          *(lds_u32x2w*)(rh + off) =
+              u32x2{f32_to_bf16_bits(gelu_erf_bf16(v[0])) | (f32_to_bf16_bits(gelu_erf_bf16(v[1])) << 16),
+                    f32_to_bf16_bits(gelu_erf_bf16(v[2])) | (f32_to_bf16_bits(gelu_erf_bf16(v[3])) << 16)};
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int rr = 8 * t + (lane >> 3), ch = lane & 7;
+        const int off = rr * 128 + ((ch ^ (rr & 7)) * 16);
+        const u32x4 uv = *(lds_u32x4*)(ru + off);
+        const u32x4 hv = *(lds_u32x4*)(rh + off);
+        const int col = cb + 8 * ch;
+        if (frow + rr < m1 && col < p.N) {
+          const int64_t at = (int64_t)(frow + rr) * p.ldc + col;
+          *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.C) + at) = uv;
+          *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.C2) + at) = hv;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    return;
+  }
+  if constexpr (EPI == BwdEpi::kGeluGrad) {
+    // G = dy W2^T (fp32 in acc): each 32-row slice of the wave's tile goes
+    // through a per-wave LDS region (as the fp32 outputs above) into row
+    // order; then 16 lanes per row take 4 columns each: U and H are read and
+    // dU = bf16(w G GELU'(U)) written as whole 128-byte row segments, and
+    // the row's dot G . H over the wave's 64 columns is the lane's 4 terms
+    // (fma in column order) summed over the 16 lanes by xor-shuffles in a
+    // fixed order; the two waves of each 128 columns are then added, the
+    // lower columns' first
+    __syncthreads();  // every wave is done reading the stage buffers
+    constexpr int REG = 32 * 64 * 4;
+    constexpr int PER = 2 * OPB / REG;
+    static_assert(PER >= 1 && (THREADS / kWave) <= 4 * PER, "epilogue regions fit the stage buffers");
+    const int bsel = wave / PER;
+    char* const reg = (bsel == 0 ? st0 : bsel == 1 ? st1 : bsel == 2 ? st2 : st3) + (wave % PER) * REG;
+    const int lrow = lane & 31;
+    const int cb = n0 + wn * 64;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int frow = m0 + wm * T::WTM + 32 * j;
+      if (frow >= m1) break;  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ch = 8 * i + 2 * q + (lane >> 5);
+          *(lds_f32x4*)(reg + lrow * 256 + ((ch ^ (lrow & 15)) * 16)) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int rr = 4 * t + (lane >> 4), ch = lane & 15;
+        const f32x4 gv = *(lds_f32x4*)(reg + rr * 256 + ((ch ^ (rr & 15)) * 16));
+        const int m = frow + rr, col = cb + 4 * ch;
+        float dot = 0.f;
+        if (m < m1 && col < p.N) {
+          const float w = p.row_w[p.tor[m]];
+          const int64_t at = (int64_t)m * p.ldc + col;
+          const u32x2 uu = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.U) + at);
+          const u32x2 hh = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.H) + at);
+          float du[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float u = chunk_elem<bf16>(u32x4{uu[0], uu[1], 0u, 0u}, r);
+            const float h = chunk_elem<bf16>(u32x4{hh[0], hh[1], 0u, 0u}, r);
+            du[r] = w * gv[r] * gelu_grad(u);
+            dot = fmaf(gv[r], h, dot);
+          }
+          Store<bf16>::four(static_cast<bf16*>(p.C) + at, du[0], du[1], du[2], du[3]);
+        }
+#pragma unroll
+        for (int sh = 8; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh, kWave);
+        if (ch == 0) s_dot[wn][wm * T::WTM + 32 * j + rr] = dot;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();
+    const int NTc = (p.N + 127) / 128;
+    for (int e = tid; e < TS * (TS / 128); e += THREADS) {
+      const int r = e % TS, c = e / TS;
+      if (m0 + r < m1 && n0 + 128 * c < p.N)
+        p.pd[(int64_t)(m0 + r) * NTc + n0 / 128 + c] = s_dot[2 * c][r] + s_dot[2 * c + 1][r];
     }
     return;
   }
