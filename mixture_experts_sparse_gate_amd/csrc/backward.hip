@@ -37,7 +37,6 @@ namespace moe {
 namespace {
 
 constexpr int kBK = 32;  // K per step
-constexpr int kStages = 4;
 constexpr int kNumXcd = 8;
 constexpr int64_t kBwdBigTileMin = 256;  // CUs of the chip
 
@@ -85,13 +84,14 @@ template <int TS> struct Operand<BwdLayout::kKContig, TS> {
     row = s >> 2;
     chunk = (s & 3) ^ swz_rows4(row);
   }
-  // the lane's fragment (8 consecutive K of row base + 32 f + lane % 32, K
-  // half lane / 32 of substep ss)
-  __device__ static u32x4 frag(const char* st, int base, int f, int ss, int lane) {
+  // byte offset in the tile of the lane's fragment (8 consecutive K of row
+  // base + 32 f + lane % 32, K half lane / 32 of substep ss)
+  __device__ static int frag_off(int base, int f, int ss, int lane) {
     const int x = base + 32 * f + (lane & 31);
     const int c = 2 * ss + (lane >> 5);
-    return *(lds_u32x4*)(st + x * 64 + ((c ^ swz_rows4(x)) * 16));
+    return x * 64 + ((c ^ swz_rows4(x)) * 16);
   }
+  __device__ static u32x4 frag(const char* st, int off) { return *(lds_u32x4*)(st + off); }
 };
 
 // Tile of 32 K x TS columns (of M or N), K strided: K row k at byte
@@ -107,13 +107,15 @@ template <int TS> struct Operand<BwdLayout::kKStrided, TS> {
     row = s / (TS / 8);
     chunk = (s % (TS / 8)) ^ swz_rows16(row);
   }
-  __device__ static u32x4 frag(const char* st, int base, int f, int ss, int lane) {
+  __device__ static int frag_off(int base, int f, int ss, int lane) {
     const int q = lane >> 4, r = lane & 15;
     const int chunk = (base + 32 * f) / 8 + 2 * (q & 1) + ((r & 3) >> 1);
-    const int krow = 8 * (q >> 1) + (r >> 2);
-    const char* p = st + krow * ROW + ((chunk ^ swz_rows16(r >> 2)) * 16) + 8 * (r & 1);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss) * ROW));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + (16 * ss + 4) * ROW));
+    const int krow = 16 * ss + 8 * (q >> 1) + (r >> 2);
+    return krow * ROW + ((chunk ^ swz_rows16(r >> 2)) * 16) + 8 * (r & 1);
+  }
+  __device__ static u32x4 frag(const char* st, int off) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + off));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + off + 4 * ROW));
     const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
     return u32x4{a[0], a[1], b[0], b[1]};
   }
@@ -277,15 +279,30 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // the lane's fragment offsets within a stage ([substep][fragment]; B's
+  // include the A tile before it), computed once: each fragment read is then
+  // one offset from its stage object. (The compiler tells the stages apart
+  // only for LDS accesses whose address it traces to one object in a few
+  // steps; a read it cannot trace makes it wait for every direct-to-LDS
+  // load in flight, which empties the pipeline each step.)
+  int oa[2][FM], ob[2][FN];
+#pragma unroll
+  for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f) oa[ss][f] = OA::frag_off(wm * T::WTM, f, ss, lane);
+#pragma unroll
+    for (int f = 0; f < FN; ++f) ob[ss][f] = OPB + OB::frag_off(wn * 64, f, ss, lane);
+  }
+
   // a step's two 16-deep substeps; the fragment reads of substep 1 are
   // issued before the MFMAs of substep 0
   auto compute = [&](const char* st) {
     u32x4 fa[2][FM], fb[2][FN];  // [substep][fragment]: A (rows m), B (columns n)
     auto read = [&](int ss) {
 #pragma unroll
-      for (int f = 0; f < FN; ++f) fb[ss][f] = OB::frag(st + OPB, wn * 64, f, ss, lane);
+      for (int f = 0; f < FN; ++f) fb[ss][f] = OB::frag(st, ob[ss][f]);
 #pragma unroll
-      for (int f = 0; f < FM; ++f) fa[ss][f] = OA::frag(st, wm * T::WTM, f, ss, lane);
+      for (int f = 0; f < FM; ++f) fa[ss][f] = OA::frag(st, oa[ss][f]);
     };
     read(0);
 #pragma unroll
