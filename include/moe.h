@@ -288,7 +288,7 @@ MOE_API moe_status_t moe_quantize_fp8(const void* W, int32_t dtype, int32_t grou
                                       uint8_t* codes, float* scales, void* stream);
 
 /* moe_expert_ffn with block-FP8 expert weights (bf16 layers with d and h
- * multiples of 128, else MOE_ERR_UNSUPPORTED): W1q / S1 are
+ * multiples of 128 and at most 16384, else MOE_ERR_UNSUPPORTED): W1q / S1 are
  * moe_quantize_fp8 of W1 [N, d, h], W2q / S2 of W2 [N, h, d]. With W' the
  * dequantised weights (decoded code times its block's scale):
  *   H[r] = GELU(x_perm[r] W1'[e] + b1[e]), y_perm[r] = H[r] W2'[e] + b2[e],

@@ -458,6 +458,9 @@ moe_status_t check_fp8_layer(const moe_desc_t* d) {
     return fail(MOE_ERR_UNSUPPORTED, "fp8 expert weights need a bf16 layer");
   if (d->d % 128 || d->h % 128)
     return fail(MOE_ERR_UNSUPPORTED, "fp8 expert weights need d and h multiples of 128 (d=%d, h=%d)", d->d, d->h);
+  if (d->d > moe::kW8MaxK || d->h > moe::kW8MaxK)
+    return fail(MOE_ERR_UNSUPPORTED, "fp8 expert weights need d and h at most %d (d=%d, h=%d)", moe::kW8MaxK, d->d,
+                d->h);
   return MOE_OK;
 }
 

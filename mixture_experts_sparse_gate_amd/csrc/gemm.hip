@@ -98,6 +98,9 @@ constexpr int kNumXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 // twice the barriers) outweighs its gain there.
 constexpr int kPingPongMinSteps = 96;
 constexpr int kGroupN = 4;   // n-tiles per run of the tile order
+// Block-FP8 weights: registers of per-lane block scales a wave holds (64
+// scale blocks each), which bounds K at 128 * 64 * kW8ScaleRegs.
+constexpr int kW8ScaleRegs = kW8MaxK / (128 * 64);
 
 // W8_: the weights are block-FP8 codes in K-groups of 8 (GemmW8) instead of
 // E values; the activations stay E.
@@ -317,6 +320,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
     // W8: acc holds the current 128-deep block of K; acc8 the scaled total
     f32x16 acc8[C::W8 ? C::FN : 1][C::W8 ? FM : 1];
+    // W8: the wave's block scales (one per 128-deep block of K: its columns
+    // lie in one scale block; a wave wholly past Ncols, whose outputs are
+    // never stored, takes the last block's, so that the reads stay in the
+    // array), read before the K loop into lane b % 64 of register b / 64.
+    // A read inside the loop would complete behind the step's global->LDS
+    // loads, and its wait would drain the whole load pipeline.
+    float scl[C::W8 ? kW8ScaleRegs : 1];
     if constexpr (C::W8) {
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
@@ -324,6 +334,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         for (int j = 0; j < FM; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc8[i][j][r] = 0.f;
+      const int wn_u = __builtin_amdgcn_readfirstlane(wn);
+      const int cb = min((n0 + wn_u * C::WTN) / 128, Ncols / 128 - 1);
+      const int nkb = K / 128;
+#pragma unroll
+      for (int r = 0; r < kW8ScaleRegs; ++r) {
+        const int b = 64 * r + lane;
+        scl[r] = b < nkb ? bscale[((int64_t)g * nkb + b) * (Ncols / 128) + cb] : 0.f;
+      }
     }
 
     // ---- per-lane fragment offsets within a stage
@@ -440,12 +458,14 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         static_assert(S % SPB == 0, "scale blocks end on fixed stages");
         if constexpr ((cur + 1) % SPB == 0) {
           // the end of a 128-deep block of K: its sums, scaled once, join
-          // the total (one scale per wave: its columns lie in one block; a
-          // wave wholly past Ncols, whose outputs are never stored, takes
-          // the last block's, so that the read stays in the array)
-          const int wn_u = __builtin_amdgcn_readfirstlane(wn);
-          const int cb = min((n0 + wn_u * C::WTN) / 128, Ncols / 128 - 1);
-          const float sc = bscale[((int64_t)g * (K / 128) + kt / SPB) * (Ncols / 128) + cb];
+          // the total
+          const int b = __builtin_amdgcn_readfirstlane(kt / SPB);
+          float sc = 0.f;
+#pragma unroll
+          for (int r = 0; r < kW8ScaleRegs; ++r) {
+            const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scl[r]), b & 63));
+            if ((b >> 6) == r) sc = v;
+          }
 #pragma unroll
           for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -1262,6 +1282,7 @@ hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind,
   // needs a second accumulator set, which the 256 x 256 tile's registers
   // cannot hold.
   const bool gelu = kind == GemmKind::kFfn1Gelu;
+  if (p.K % 128 || p.K > kW8MaxK || p.Ncols % 128) return hipErrorInvalidValue;
   if (avg_rows < 64)
     return gelu ? launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, true, true>>(p, s, ev, w8.bscale)
                 : launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, false, true>>(p, s, ev, w8.bscale);

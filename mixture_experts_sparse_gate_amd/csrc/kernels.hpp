@@ -101,7 +101,8 @@ enum class GemmKind { kFfn1Gelu, kFfn2, kProjF32 };
 // Block-FP8 weights (launch_grouped_gemm_w8): B holds E4M3 codes in K-groups
 // of 8 (the byte of B[k][n] at (k/8 * Ncols + n) * 8 + k % 8, strideB bytes
 // per group) and bscale one fp32 scale per 128 x 128 block,
-// [groups, K/128, Ncols/128]; K a multiple of 128.
+// [groups, K/128, Ncols/128]; K a multiple of 128, at most kW8MaxK.
+constexpr int kW8MaxK = 16384;
 struct GemmW8 {
   const float* bscale;
 };
