@@ -225,10 +225,13 @@ def test_fp8_argument_checks(lib):
         a = list(args)
         a[i] = None
         assert ffn(ctypes.byref(dec), *a, None) == _lib.MOE_ERR_INVALID, i
-    # fp32 layers, and d or h not a multiple of 128, are not served
-    for spec in (workloads.get("tiny_top1_f32"), workloads.get("decode_top8_bf16").with_(h=2000)):
+    # fp32 layers, d or h not a multiple of 128, and d or h above 16384 (the
+    # scale blocks a wave holds in registers) are not served
+    for spec in (workloads.get("tiny_top1_f32"), workloads.get("decode_top8_bf16").with_(h=2000),
+                 workloads.get("decode_top8_bf16").with_(h=16384 + 128), workloads.get("decode_top8_bf16").with_(d=16512)):
         d = desc_from_spec(spec)
-        assert ffn(ctypes.byref(d), *args, None) == _lib.MOE_ERR_UNSUPPORTED
+        assert ffn(ctypes.byref(d), *args, None) == _lib.MOE_ERR_UNSUPPORTED, spec
+        assert b"fp8" in lib.moe_last_error()
         t = _lib.MoeLayerTensors(x=FAKE, w_gate=FAKE, y=FAKE)
         w8 = _lib.MoeFp8Weights(W1q=FAKE, S1=FAKE, W2q=FAKE, S2=FAKE)
         assert lib.moe_forward_fp8(ctypes.byref(d), ctypes.byref(t), ctypes.byref(w8), FAKE, 1 << 40, None) \
