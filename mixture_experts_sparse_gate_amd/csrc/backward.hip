@@ -188,6 +188,7 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
   __shared__ __attribute__((aligned(1024))) char st2[2 * OPB];
   __shared__ __attribute__((aligned(1024))) char st3[2 * OPB];
   __shared__ float s_dot[T::WN][TS];
+  __shared__ float s_w[EPI == BwdEpi::kGeluGrad ? TS : 1];  // the tile's row weights (kGeluGrad)
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int wm = wave / T::WN, wn = wave % T::WN;
 
@@ -340,6 +341,10 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
   issue(st0, 0);
   issue(st1, 1);
   issue(st2, 2);
+  // kGeluGrad: the weight of tile row tid, read while the first stages load
+  float w_pre = 0.f;
+  if constexpr (EPI == BwdEpi::kGeluGrad)
+    if (tid < TS && m0 + tid < m1) w_pre = p.row_w[p.tor[m0 + tid]];
   auto step = [&](char* cur, char* nxt, int kt) {
     wait_loads_and_lds<4 * LOADS>();  // this step's loads have landed; the previous stage is read
     __builtin_amdgcn_s_barrier();
@@ -473,15 +478,23 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
     // the row's dot G . H over the wave's 64 columns is the lane's 4 terms
     // (fma in column order) summed over the 16 lanes by xor-shuffles in a
     // fixed order; the two waves of each 128 columns are then added, the
-    // lower columns' first
-    __syncthreads();  // every wave is done reading the stage buffers
+    // lower columns' first. The rows' weights w were read before the K loop;
+    // a slice's U and H pieces are all requested before any is used (rows
+    // and columns past the tile read clamped, in-range positions whose
+    // results are dropped), so that the slice waits for one round trip.
+    if (tid < TS) s_w[tid] = w_pre;
+    __syncthreads();  // every wave is done reading the stage buffers; s_w written
     constexpr int REG = 32 * 64 * 4;
     constexpr int PER = 2 * OPB / REG;
     static_assert(PER >= 1 && (THREADS / kWave) <= 4 * PER, "epilogue regions fit the stage buffers");
     const int bsel = wave / PER;
     char* const reg = (bsel == 0 ? st0 : bsel == 1 ? st1 : bsel == 2 ? st2 : st3) + (wave % PER) * REG;
     const int lrow = lane & 31;
-    const int cb = n0 + wn * 64;
+    const int ch = lane & 15;
+    const int col = n0 + wn * 64 + 4 * ch;
+    const int colc = min(col, p.N - 4);
+    const bf16* const Ub = static_cast<const bf16*>(p.U);
+    const bf16* const Hb = static_cast<const bf16*>(p.H);
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int frow = m0 + wm * T::WTM + 32 * j;
@@ -490,33 +503,38 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
       for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int ch = 8 * i + 2 * q + (lane >> 5);
-          *(lds_f32x4*)(reg + lrow * 256 + ((ch ^ (lrow & 15)) * 16)) =
+          const int c = 8 * i + 2 * q + (lane >> 5);
+          *(lds_f32x4*)(reg + lrow * 256 + ((c ^ (lrow & 15)) * 16)) =
               f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
+      u32x2 uu[8], hh[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int mc = min(frow + 4 * t + (lane >> 4), m1 - 1);
+        const int64_t at = (int64_t)mc * p.ldc + colc;
+        uu[t] = *reinterpret_cast<const u32x2*>(Ub + at);
+        hh[t] = *reinterpret_cast<const u32x2*>(Hb + at);
+      }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const int rr = 4 * t + (lane >> 4), ch = lane & 15;
+        const int rr = 4 * t + (lane >> 4);
         const f32x4 gv = *(lds_f32x4*)(reg + rr * 256 + ((ch ^ (rr & 15)) * 16));
-        const int m = frow + rr, col = cb + 4 * ch;
+        const int m = frow + rr;
         float dot = 0.f;
         if (m < m1 && col < p.N) {
-          const float w = p.row_w[p.tor[m]];
-          const int64_t at = (int64_t)m * p.ldc + col;
-          const u32x2 uu = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.U) + at);
-          const u32x2 hh = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.H) + at);
+          const float w = s_w[m - m0];
           float du[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float u = chunk_elem<bf16>(u32x4{uu[0], uu[1], 0u, 0u}, r);
-            const float h = chunk_elem<bf16>(u32x4{hh[0], hh[1], 0u, 0u}, r);
+            const float u = chunk_elem<bf16>(u32x4{uu[t][0], uu[t][1], 0u, 0u}, r);
+            const float h = chunk_elem<bf16>(u32x4{hh[t][0], hh[t][1], 0u, 0u}, r);
             du[r] = w * gv[r] * gelu_grad(u);
             dot = fmaf(gv[r], h, dot);
           }
-          Store<bf16>::four(static_cast<bf16*>(p.C) + at, du[0], du[1], du[2], du[3]);
+          Store<bf16>::four(static_cast<bf16*>(p.C) + (int64_t)m * p.ldc + col, du[0], du[1], du[2], du[3]);
         }
 #pragma unroll
         for (int sh = 8; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh, kWave);
@@ -535,78 +553,8 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
     }
     return;
   }
-  const int mrow = m0 + wm * T::WTM + (lane & 31);
-  const int ncol = n0 + wn * 64 + 4 * (lane >> 5);
-  const int64_t cbase = RAGGED_K ? (int64_t)g * p.strideC : 0;
-  float dot[FM];
-#pragma unroll
-  for (int j = 0; j < FM; ++j) dot[j] = 0.f;
-#pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int m = mrow + 32 * j;
-    const bool row_ok = m < m1;
-    float w = 0.f;
-    if constexpr (EPI == BwdEpi::kGeluGrad) w = row_ok ? p.row_w[p.tor[m]] : 0.f;
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = ncol + 32 * i + 8 * q;
-        if (!row_ok || n >= p.N) continue;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-        const int64_t at = cbase + (int64_t)m * p.ldc + n;
-        if constexpr (EPI == BwdEpi::kPlain) {
-          if constexpr (std::is_same_v<O, float>)
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.C) + at) = f32x4{v[0], v[1], v[2], v[3]};
-          else
-            Store<bf16>::four(static_cast<bf16*>(p.C) + at, v[0], v[1], v[2], v[3]);
-        } else if constexpr (EPI == BwdEpi::kDualGelu) {
-          if (p.bias) {
-            const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.bias) +
-                                                             (int64_t)g * p.N + n);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] += chunk_elem<bf16>(u32x4{bb[0], bb[1], 0u, 0u}, r);
-          }
-          Store<bf16>::four(static_cast<bf16*>(p.C) + at, v[0], v[1], v[2], v[3]);
-          Store<bf16>::four(static_cast<bf16*>(p.C2) + at, gelu_erf_bf16(v[0]), gelu_erf_bf16(v[1]),
-                            gelu_erf_bf16(v[2]), gelu_erf_bf16(v[3]));
-        } else {
-          // G = dy W2^T: dU = bf16(w G GELU'(U)); the row's dot G . H
-          const u32x2 uu = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.U) + at);
-          const u32x2 hh = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.H) + at);
-          float du[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float u = chunk_elem<bf16>(u32x4{uu[0], uu[1], 0u, 0u}, r);
-            const float h = chunk_elem<bf16>(u32x4{hh[0], hh[1], 0u, 0u}, r);
-            du[r] = w * v[r] * gelu_grad(u);
-            dot[j] = fmaf(v[r], h, dot[j]);
-          }
-          Store<bf16>::four(static_cast<bf16*>(p.C) + at, du[0], du[1], du[2], du[3]);
-        }
-      }
-  }
-  if constexpr (EPI == BwdEpi::kGeluGrad) {
-    // the row's dot over each 128 columns of the tile, in a fixed order: the
-    // lane pair (lane, lane + 32), then the first 64 columns' wave before the
-    // second's
-#pragma unroll
-    for (int j = 0; j < FM; ++j) dot[j] += __shfl_xor(dot[j], 32, kWave);
-    if (lane < 32)
-#pragma unroll
-      for (int j = 0; j < FM; ++j) s_dot[wn][wm * T::WTM + 32 * j + lane] = dot[j];
-    __syncthreads();
-    const int NTc = (p.N + 127) / 128;
-    for (int e = tid; e < TS * (TS / 128); e += THREADS) {
-      const int r = e % TS, c = e / TS;
-      if (m0 + r < m1 && n0 + 128 * c < p.N)
-        p.pd[(int64_t)(m0 + r) * NTc + n0 / 128 + c] = s_dot[2 * c][r] + s_dot[2 * c + 1][r];
-    }
-  }
+  static_assert(EPI != BwdEpi::kPlain || std::is_same_v<O, float>, "plain outputs are fp32");
 }
-
 
 // dY rows: for each kept choice (t, j), row row_of[t k + j] = bf16(w_tj dy_t);
 // one wave per token, dy_t read once
