@@ -1,7 +1,8 @@
 """The two GELUs of the expert FFN kernel (gelu.hpp; the accurate one for
-fp32 results, the cheaper one for bf16 results): their constants are the ones
-fit_gelu.py derives, and each formula, evaluated step by step in fp32, stays
-within its stated error of the exact GELU (scipy's erfc in fp64)."""
+fp32 results, the cheaper one for bf16 results) and the GELU derivative of
+the backward kernel: their constants are the ones fit_gelu.py derives, and
+each formula, evaluated step by step in fp32, stays within its stated error
+of the exact function (scipy's erfc in fp64)."""
 import math
 import os
 import re
@@ -16,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mixture_experts_sparse_gate_amd", "csrc")
 
 
-def kernel_constants(decl=r"h\[8\]"):
+def kernel_constants(decl=r"kGeluR\[8\]"):
     src = open(os.path.join(CSRC, "gelu.hpp")).read()
     m = re.search(r"constexpr float " + decl + r" = \{([^}]*)\}", src)
     assert m, "GELU constants not found in gelu.hpp"
@@ -66,6 +67,29 @@ def gelu_bf16_kernel_fp32(u, g):
     for _ in range(5):
         q = (q * q).astype(f)
     return fma32(-np.abs(u), q, np.maximum(u, f(0)))
+
+
+def gelu_grad_kernel_fp32(u, h):
+    """The kernel's gelu_grad step by step in fp32: q = R(t) E = Phi(-|u|)
+    with gelu_erf's t, R and E = exp(-u^2 / 2), then u E / sqrt(2 pi) added
+    to 1 - q (u >= 0) or q (u < 0) by one fma."""
+    f = np.float32
+    u = u.astype(f)
+    a = np.abs(u)
+    t = (f(1) / fma32(a, f(0.24748737341529164), f(1))).astype(f)
+    r = np.full_like(u, h[7])
+    for i in range(6, -1, -1):
+        r = fma32(r, t, h[i])
+    arg = ((u * f(-0.72134752044448170)).astype(f) * u).astype(f)
+    e = np.exp2(arg.astype(np.float64)).astype(f)
+    q = (r * e).astype(f)
+    cdf = np.where(u >= 0, (f(1) - q).astype(f), q)
+    return fma32(u, (f(0.39894228040143268) * e).astype(f), cdf)
+
+
+def gelu_grad_exact(u):
+    u = u.astype(np.float64)
+    return 0.5 * scipy_special.erfc(-u / math.sqrt(2.0)) + u * np.exp(-0.5 * u * u) / math.sqrt(2.0 * math.pi)
 
 
 def bf16_bits(v):
@@ -130,3 +154,20 @@ def test_bf16_form_rounds_like_exact():
     ref = bf16_bits(gelu_exact(u)).astype(np.int64)
     assert np.mean(got != ref) < 1e-3
     assert np.abs(got - ref).max() <= 1
+
+
+def test_gelu_grad_error_against_exact_derivative():
+    c = kernel_constants()
+    u = np.linspace(-13.0, 13.0, 2_600_001).astype(np.float32)
+    got = gelu_grad_kernel_fp32(u, c).astype(np.float64)
+    ref = gelu_grad_exact(u)
+    assert np.abs(got - ref).max() < 4e-6
+    # the derivative by central differences of the exact GELU (a check of
+    # the closed form itself), and its limits: 1/2 at 0 (within R's error),
+    # 1 and 0 far out
+    x = np.linspace(-6.0, 6.0, 1201)
+    step = 1e-5
+    fd = (gelu_exact(x + step) - gelu_exact(x - step)) / (2 * step)
+    assert np.abs(fd - gelu_grad_exact(x)).max() < 1e-8
+    z = gelu_grad_kernel_fp32(np.array([0.0, 20.0, -20.0], dtype=np.float32), c)
+    assert abs(z[0] - 0.5) < 2e-6 and z[1] == np.float32(1.0) and z[2] == 0.0
