@@ -22,11 +22,13 @@
 //                      gradients) or ragged K (groups of contraction rows, the
 //                      weight gradients, one [M, N] output per group).
 //   scale_rows_kernel  dY rows: bf16(w * dy_t) into each kept row of t
-//   bwd_token_kernel   one block per token: gate-weight gradients (partial
-//                      dots in a fixed order), softmax and softplus backward,
-//                      dx = sum of the token's dx_perm rows + the gate's part
-//   gate_grad_kernels  dW_g = x^T dl, dW_n = x^T dz, d logit_bias: per
-//                      256-token partial sums, then added in chunk order
+//   bwd_token_kernel   one wave per token: gate-weight gradients (partial
+//                      dots in a fixed order), softmax and softplus backward
+//   bwd_dx_kernel      dx = sum of the token's dx_perm rows + the gate's
+//                      part, 4 elements per thread
+//   gate_grad_kernels  dW_g = x^T dl, dW_n = x^T dz (one pass over x),
+//                      d logit_bias: per 64-token partial sums, then added
+//                      in chunk order
 //   colsum_kernel      db1, db2: per expert column sums in row order
 // Every reduction runs in a fixed order; no floating-point atomics.
 #include "common.hpp"
@@ -606,133 +608,236 @@ __global__ __launch_bounds__(64) void importance_grad_kernel(const float* imp, f
   }
 }
 
-constexpr int kTokThreads = 256;
+constexpr int kGateTok = 64;  // tokens per partial sum of the gate's gradients
+constexpr int kTokWaves = 4;  // tokens per block of the token kernel, one wave each
 
-// a fixed-order block sum of one value per thread (tree over LDS)
-__device__ float block_sum(float v, float* red) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  for (int s = kTokThreads / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
-  }
-  const float out = red[0];
-  __syncthreads();
-  return out;
+// sum and maximum over the wave's 64 lanes, in a fixed (butterfly) order
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// the wave's LDS writes before this point are seen by its reads after it
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One block per token t: the gate weights' gradients g_tj, the logits'
-// gradient dl[t] (softmax backward), for the noisy gate dz[t] = dl eps
-// sigmoid(x W_n), and dx[t] = sum over kept j of dx_perm[row] (j order) +
-// dl W_g^T + dz W_n^T.
-__global__ __launch_bounds__(kTokThreads) void bwd_token_kernel(BwdTokenParams p) {
-  __shared__ float red[kTokThreads];
-  __shared__ float s_g[32], s_w[32];
-  __shared__ int s_e[32], s_row[32];
-  __shared__ float s_dl[kMaxExperts], s_dz[kMaxExperts];
-  const int t = blockIdx.x, tid = threadIdx.x;
+// One wave per token t: the gate weights' gradients g_tj (lane j), the
+// logits' gradient dl[t] (softmax backward) and, for the noisy gate,
+// dz[t] = dl eps sigmoid(x W_n). Reductions over the wave are butterflies.
+__global__ __launch_bounds__(kWave * kTokWaves) void bwd_token_kernel(BwdTokenParams p) {
+  __shared__ float s_dl[kTokWaves][kMaxExperts], s_dz[kTokWaves][kMaxExperts];
+  const int wave = threadIdx.x / kWave, lane = lane_id();
+  const int t = blockIdx.x * kTokWaves + wave;
+  if (t >= p.T) return;  // wave-uniform; the waves share no data
   const int k = p.k, N = p.N, d = p.d;
-  if (tid < k) {
-    const int64_t i = (int64_t)t * k + tid;
-    s_e[tid] = p.topk_idx[i];
-    s_w[tid] = p.topk_w[i];
-    const int r = p.row_of[i];
-    s_row[tid] = r;
-    float gsum = 0.f;
-    if (r >= 0)
-      for (int c = 0; c < p.ntc; ++c) gsum += p.pd[(int64_t)r * p.ntc + c];
-    s_g[tid] = gsum;
+  float* const dl = s_dl[wave];
+  float* const dz = s_dz[wave];
+  // lane j < k: choice j's expert, weight, row and gate-weight gradient
+  // (the row's partial dots G . H over its column tiles, split over the
+  // lanes and added by a butterfly)
+  int e = 0, r = -1;
+  float w = 0.f, g = 0.f;
+  if (lane < k) {
+    const int64_t i = (int64_t)t * k + lane;
+    e = p.topk_idx[i];
+    w = p.topk_w[i];
+    r = p.row_of[i];
   }
-  __syncthreads();
+  for (int j = 0; j < k; ++j) {
+    const int rj = __shfl(r, j, kWave);
+    if (rj < 0) continue;  // wave-uniform
+    float part = 0.f;
+    for (int c = lane; c < p.ntc; c += kWave) part += p.pd[(int64_t)rj * p.ntc + c];
+    part = wave_sum(part);
+    if (lane == j) g = part;
+  }
   if (p.b2) {
     // + dy_t . b2_e for each kept choice
     for (int j = 0; j < k; ++j) {
-      if (s_row[j] < 0) continue;  // block-uniform
+      const int rj = __shfl(r, j, kWave), ej = __shfl(e, j, kWave);
+      if (rj < 0) continue;  // wave-uniform
       float part = 0.f;
-      const bf16* b = p.b2 + (int64_t)s_e[j] * d;
-      for (int i = tid; i < d; i += kTokThreads) part += (float)p.dy[(int64_t)t * d + i] * (float)b[i];
-      const float s = block_sum(part, red);
-      if (tid == 0) s_g[j] += s;
-      __syncthreads();
+      for (int i = lane; i < d; i += kWave)
+        part += (float)p.dy[(int64_t)t * d + i] * (float)p.b2[(int64_t)ej * d + i];
+      part = wave_sum(part);
+      if (lane == j) g += part;
     }
   }
-  if (tid < k && p.dimp) s_g[tid] += p.dimp[s_e[tid]];
-  __syncthreads();
-  // softmax backward (thread n for expert n)
+  if (lane < k && p.dimp) g += p.dimp[e];
+  // softmax backward
   if (p.renorm) {
-    if (tid == 0) {
-      float s = 0.f;
-      for (int j = 0; j < k; ++j) s += s_w[j] * s_g[j];
-      red[0] = s;
-    }
-    for (int n = tid; n < N; n += kTokThreads) s_dl[n] = 0.f;
-    __syncthreads();
-    if (tid < k) s_dl[s_e[tid]] = s_w[tid] * (s_g[tid] - red[0]);
+    float sw = 0.f;  // sum over j of w_j g_j, j in order
+    for (int j = 0; j < k; ++j) sw += __shfl(w, j, kWave) * __shfl(g, j, kWave);
+    for (int n = lane; n < N; n += kWave) dl[n] = 0.f;
+    wave_lds_sync();
+    if (lane < k) dl[e] = w * (g - sw);
   } else {
-    // p = softmax of the logits (max, exps and their sum in expert order)
-    if (tid == 0) {
-      const float* l = p.logits + (int64_t)t * N;
-      float m = l[0];
-      for (int n = 1; n < N; ++n) m = fmaxf(m, l[n]);
-      float z = 0.f;
-      for (int n = 0; n < N; ++n) z += expf(l[n] - m);
-      red[0] = m;
-      red[1] = z;
+    // p = softmax of the logits; G scattered over the experts (in dz)
+    const float* l = p.logits + (int64_t)t * N;
+    float lv[kMaxExperts / kWave], m = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kMaxExperts / kWave; ++q) {
+      const int n = lane + kWave * q;
+      lv[q] = n < N ? l[n] : -INFINITY;
+      m = fmaxf(m, lv[q]);
     }
-    for (int n = tid; n < N; n += kTokThreads) s_dz[n] = 0.f;  // G, scattered
-    __syncthreads();
-    if (tid < k) s_dz[s_e[tid]] = s_g[tid];
-    __syncthreads();
-    const float m = red[0], z = red[1];
-    for (int n = tid; n < N; n += kTokThreads) s_dl[n] = expf(p.logits[(int64_t)t * N + n] - m) / z;
-    __syncthreads();
-    if (tid == 0) {
-      float s = 0.f;
-      for (int n = 0; n < N; ++n) s += s_dl[n] * s_dz[n];
-      red[2] = s;
+    m = wave_max(m);
+    float ex[kMaxExperts / kWave], zp = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxExperts / kWave; ++q) {
+      ex[q] = lane + kWave * q < N ? expf(lv[q] - m) : 0.f;
+      zp += ex[q];
     }
-    __syncthreads();
-    const float s = red[2];
-    for (int n = tid; n < N; n += kTokThreads) s_dl[n] = s_dl[n] * (s_dz[n] - s);
+    const float z = wave_sum(zp);
+    for (int n = lane; n < N; n += kWave) dz[n] = 0.f;
+    wave_lds_sync();
+    if (lane < k) dz[e] = g;
+    wave_lds_sync();
+    float sp = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxExperts / kWave; ++q) {
+      const int n = lane + kWave * q;
+      ex[q] = ex[q] / z;
+      if (n < N) sp += ex[q] * dz[n];
+    }
+    const float sg = wave_sum(sp);
+#pragma unroll
+    for (int q = 0; q < kMaxExperts / kWave; ++q) {
+      const int n = lane + kWave * q;
+      if (n < N) dl[n] = ex[q] * (dz[n] - sg);
+    }
   }
-  __syncthreads();
-  // noisy gate: dz = dl eps sigmoid(x W_n), x W_n by block sums per expert
+  wave_lds_sync();
+  // noisy gate: dz = dl eps sigmoid(x W_n), x W_n eight experts at a time;
+  // with N a multiple of 8 a lane's 8 weights are one 16-byte load, and the
+  // loads of 8 of its columns are issued before their FMAs
   if (p.w_noise) {
-    for (int n = 0; n < N; ++n) {
-      float part = 0.f;
-      for (int i = tid; i < d; i += kTokThreads)
-        part += (float)p.x[(int64_t)t * d + i] * (float)p.w_noise[(int64_t)i * N + n];
-      const float z = block_sum(part, red);
-      if (tid == 0) {
-        const float e = expf(-fabsf(z));
-        const float sig = z >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
-        s_dz[n] = s_dl[n] * p.noise[(int64_t)t * N + n] * sig;
+    const bool vec = N % 8 == 0;
+    for (int n0 = 0; n0 < N; n0 += 8) {
+      float acc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+      if (vec) {
+        for (int i0 = lane; i0 < d; i0 += 8 * kWave) {
+          float xv[8];
+          u32x4 wc[8];
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const int i = min(i0 + b * kWave, d - 1);
+            xv[b] = i0 + b * kWave < d ? (float)p.x[(int64_t)t * d + i] : 0.f;
+            wc[b] = *reinterpret_cast<const u32x4*>(p.w_noise + (int64_t)i * N + n0);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the FMAs
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc[u] = fmaf(xv[b], chunk_elem<bf16>(wc[b], u), acc[u]);
+        }
+      } else {
+        for (int i = lane; i < d; i += kWave) {
+          const float xv = (float)p.x[(int64_t)t * d + i];
+          const bf16* wr = p.w_noise + (int64_t)i * N + n0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (n0 + u < N) acc[u] = fmaf(xv, (float)wr[u], acc[u]);
+        }
+      }
+      float zsel = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float zu = wave_sum(acc[u]);
+        if (lane == u) zsel = zu;
+      }
+      const int n = n0 + lane;
+      if (lane < 8 && n < N) {
+        const float ez = expf(-fabsf(zsel));
+        const float sig = zsel >= 0.f ? 1.f / (1.f + ez) : ez / (1.f + ez);
+        dz[n] = dl[n] * p.noise[(int64_t)t * N + n] * sig;
       }
     }
-    __syncthreads();
+    wave_lds_sync();
   }
-  for (int n = tid; n < N; n += kTokThreads) {
-    p.dl[(int64_t)t * N + n] = s_dl[n];
-    if (p.w_noise) p.dz[(int64_t)t * N + n] = s_dz[n];
+  for (int n = lane; n < N; n += kWave) {
+    p.dl[(int64_t)t * N + n] = dl[n];
+    if (p.w_noise) p.dz[(int64_t)t * N + n] = dz[n];
   }
-  // dx
-  for (int i = tid; i < d; i += kTokThreads) {
-    float v = 0.f;
-    for (int j = 0; j < k; ++j)
-      if (s_row[j] >= 0) v += p.dx_perm[(int64_t)s_row[j] * d + i];
-    float gsum = 0.f;
-    for (int n = 0; n < N; ++n) gsum = fmaf(s_dl[n], (float)p.w_gate[(int64_t)i * N + n], gsum);
-    if (p.w_noise)
-      for (int n = 0; n < N; ++n) gsum = fmaf(s_dz[n], (float)p.w_noise[(int64_t)i * N + n], gsum);
-    v += gsum;
-    reinterpret_cast<uint16_t*>(p.dx)[(int64_t)t * d + i] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+constexpr int kDxThreads = 256;  // threads of the dx kernel, 4 elements each
+
+// dx[t][i..i+3] = sum over kept j of dx_perm[row_tj][i..] (j order) +
+// dl[t] W_g^T + dz[t] W_n^T (experts in order, the noise part after the
+// gate part): block (t, y) covers elements 1024 y .. + 1023 of token t,
+// with the token's rows, dl and dz in LDS. Dropped choices read row 0 and
+// add nothing.
+__global__ __launch_bounds__(kDxThreads) void bwd_dx_kernel(BwdTokenParams p) {
+  __shared__ float s_sv[2][kMaxExperts];
+  __shared__ int s_row[32];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int k = p.k, N = p.N, d = p.d;
+  for (int n = tid; n < N; n += kDxThreads) {
+    s_sv[0][n] = p.dl[(int64_t)t * N + n];
+    if (p.w_noise) s_sv[1][n] = p.dz[(int64_t)t * N + n];
   }
+  if (tid < k) s_row[tid] = p.row_of[(int64_t)t * k + tid];
+  __syncthreads();
+  const int i = (blockIdx.y * kDxThreads + tid) * 4;
+  if (i >= d) return;  // d is a multiple of 8: i < d covers i + 3
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    f32x4 a[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int rj = j0 + b < k ? s_row[j0 + b] : -1;
+      a[b] = *reinterpret_cast<const f32x4*>(p.dx_perm + (int64_t)max(rj, 0) * d + i);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the adds
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+      if (j0 + b < k && s_row[j0 + b] >= 0)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] += a[b][u];
+  }
+  float gs[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool vec = N % 8 == 0;  // gate rows of whole 16-byte chunks
+  for (int pass = 0; pass < (p.w_noise ? 2 : 1); ++pass) {
+    const bf16* W = pass ? p.w_noise : p.w_gate;
+    const float* sv = s_sv[pass];
+    if (vec) {
+      for (int n0 = 0; n0 < N; n0 += 8) {
+        u32x4 c[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) c[u] = *reinterpret_cast<const u32x4*>(W + (int64_t)(i + u) * N + n0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) gs[u] = fmaf(sv[n0 + q], chunk_elem<bf16>(c[u], q), gs[u]);
+      }
+    } else {
+      for (int n = 0; n < N; ++n) {
+        const float sn = sv[n];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) gs[u] = fmaf(sn, (float)W[(int64_t)(i + u) * N + n], gs[u]);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] += gs[u];
+  Store<bf16>::four(p.dx + (int64_t)t * d + i, v[0], v[1], v[2], v[3]);
 }
 
 // partial[c][n] = sum over the tokens of chunk c of src[t][n] (t ascending)
 __global__ __launch_bounds__(256) void column_sum_partial_kernel(const float* src, float* partial, int T, int N) {
   const int c = blockIdx.x;
-  const int t0 = c * 256, t1 = min(T, t0 + 256);
+  const int t0 = c * kGateTok, t1 = min(T, t0 + kGateTok);
   for (int n = threadIdx.x; n < N; n += 256) {
     float s = 0.f;
     for (int t = t0; t < t1; ++t) s += src[(int64_t)t * N + n];
@@ -740,44 +845,79 @@ __global__ __launch_bounds__(256) void column_sum_partial_kernel(const float* sr
   }
 }
 
-constexpr int kGateTok = 256;  // tokens per partial sum of the gate's weight gradients
-
-// partial[c][i][n] = sum over the tokens of chunk c of x[t, i] * src[t, n]
-// (t ascending); one thread per i, experts in groups of 8
-__global__ __launch_bounds__(256) void gate_grad_partial_kernel(const bf16* x, const float* src, float* partial,
-                                                                int T, int d, int N) {
-  __shared__ float s_src[kGateTok * 8];
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int c = blockIdx.y;
-  const int t0 = c * kGateTok, t1 = min(T, t0 + kGateTok);
-  for (int n0 = 0; n0 < N; n0 += 8) {
-    __syncthreads();
-    for (int q = threadIdx.x; q < (t1 - t0) * 8; q += 256) {
-      const int tt = q / 8, nn = n0 + q % 8;
-      s_src[q] = nn < N ? src[(int64_t)(t0 + tt) * N + nn] : 0.f;
-    }
-    __syncthreads();
-    if (i >= d) continue;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int t = t0; t < t1; ++t) {
-      const float xv = (float)x[(int64_t)t * d + i];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = fmaf(xv, s_src[(t - t0) * 8 + u], acc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (n0 + u < N) partial[((int64_t)c * d + i) * N + n0 + u] = acc[u];
+// partial[c][i][n] = sum over the tokens t of chunk c (ascending) of
+// x[t][i] src[t][n], where src is src0 for n < N and src1 (the noisy
+// gate's dz, or null) for N <= n < 2N. One wave per block: lane l holds
+// IL consecutive columns i (one 8- or 16-byte load of x per token) times
+// NL experts from blockIdx.z NL; the chunk's src values sit in LDS.
+template <int IL, int NL>
+__global__ __launch_bounds__(kWave) void gate_grad_partial_kernel(const bf16* x, const float* src0,
+                                                                  const float* src1, float* partial, int T, int d,
+                                                                  int N) {
+  __shared__ float s_src[kGateTok][NL];
+  const int Np = src1 ? 2 * N : N;
+  const int lane = threadIdx.x;
+  const int i0 = (blockIdx.x * kWave + lane) * IL;
+  const int c = blockIdx.y, nb = blockIdx.z * NL;
+  const int t0 = c * kGateTok, nt = min(T - t0, kGateTok);
+  for (int q = lane; q < kGateTok * NL; q += kWave) {
+    const int tt = q / NL, n = nb + q % NL;
+    float v = 0.f;
+    if (tt < nt && n < Np) v = n < N ? src0[(int64_t)(t0 + tt) * N + n] : src1[(int64_t)(t0 + tt) * N + n - N];
+    s_src[tt][q % NL] = v;
   }
+  __syncthreads();
+  const bool live = i0 < d;  // d and i0 multiples of IL: the lane's IL columns are in range
+  const bf16* xp = x + (int64_t)t0 * d + (live ? i0 : 0);
+  float acc[IL][NL];
+#pragma unroll
+  for (int u = 0; u < IL; ++u)
+#pragma unroll
+    for (int n = 0; n < NL; ++n) acc[u][n] = 0.f;
+  // batches of 16 tokens: the batch's loads are all issued before its FMAs
+  // (rows past the chunk read row t0, in range, and meet zero src values)
+  for (int tb = 0; tb < nt; tb += 16) {
+    u32x4 raw[16];
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int64_t at = (int64_t)(tb + b < nt ? tb + b : 0) * d;
+      if constexpr (IL == 8) {
+        raw[b] = *reinterpret_cast<const u32x4*>(xp + at);
+      } else {
+        const u32x2 r2 = *reinterpret_cast<const u32x2*>(xp + at);
+        raw[b] = u32x4{r2[0], r2[1], 0u, 0u};
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the FMAs
+#pragma unroll
+    for (int b = 0; b < 16; ++b)
+#pragma unroll
+      for (int u = 0; u < IL; ++u) {
+        const float xv = chunk_elem<bf16>(raw[b], u);
+#pragma unroll
+        for (int n = 0; n < NL; ++n) acc[u][n] = fmaf(xv, s_src[tb + b][n], acc[u][n]);
+      }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int u = 0; u < IL; ++u)
+#pragma unroll
+    for (int n = 0; n < NL; ++n)
+      if (nb + n < Np) partial[((int64_t)c * d + i0 + u) * Np + nb + n] = acc[u][n];
 }
 
-// out[i][n] = the chunks' partial sums added in chunk order
-__global__ __launch_bounds__(256) void gate_grad_final_kernel(const float* partial, float* out, int chunks,
-                                                              int64_t n_out) {
+// the chunks' partial sums added in chunk order: column n < N of
+// partial[.][i] into out0[i][n], n >= N into out1[i][n - N]
+__global__ __launch_bounds__(256) void gate_grad_final_kernel(const float* partial, float* out0, float* out1,
+                                                              int chunks, int d, int N, int Np) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t n_out = (int64_t)d * Np;
   if (q >= n_out) return;
   float s = 0.f;
   for (int c = 0; c < chunks; ++c) s += partial[(int64_t)c * n_out + q];
-  out[q] = s;
+  const int i = (int)(q / Np), n = (int)(q % Np);
+  if (n < N) out0[(int64_t)i * N + n] = s;
+  else out1[(int64_t)i * N + n - N] = s;
 }
 
 // out[e][c] = sum over rows [off[e], off[e+1]) of src[row][c], rows in
@@ -852,20 +992,28 @@ hipError_t launch_importance_grad(const float* imp, float* dimp, int N, float c0
 }
 
 hipError_t launch_bwd_token(const BwdTokenParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_token_kernel, dim3(p.T), dim3(kTokThreads), 0, s, p);
+  hipLaunchKernelGGL(bwd_token_kernel, dim3((p.T + kTokWaves - 1) / kTokWaves), dim3(kWave * kTokWaves), 0, s, p);
+  hipLaunchKernelGGL(bwd_dx_kernel, dim3(p.T, (p.d + 4 * kDxThreads - 1) / (4 * kDxThreads)), dim3(kDxThreads), 0,
+                     s, p);
   return hipGetLastError();
 }
 
 int gate_grad_chunks(int64_t T) { return (int)((T + kGateTok - 1) / kGateTok); }
 
-hipError_t launch_gate_grad(const bf16* x, const float* src, float* partial, float* out, int T, int d, int N,
-                            hipStream_t s) {
+hipError_t launch_gate_grad(const bf16* x, const float* src0, const float* src1, float* partial, float* out0,
+                            float* out1, int T, int d, int N, hipStream_t s) {
   const int chunks = gate_grad_chunks(T);
-  hipLaunchKernelGGL(gate_grad_partial_kernel, dim3((d + 255) / 256, chunks), dim3(256), 0, s, x, src, partial, T,
-                     d, N);
-  const int64_t n_out = (int64_t)d * N;
-  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, partial, out,
-                     chunks, n_out);
+  const int Np = src1 ? 2 * N : N;
+  if (Np <= 8)
+    hipLaunchKernelGGL((gate_grad_partial_kernel<8, 8>), dim3((d + 8 * kWave - 1) / (8 * kWave), chunks, 1),
+                       dim3(kWave), 0, s, x, src0, src1, partial, T, d, N);
+  else
+    hipLaunchKernelGGL((gate_grad_partial_kernel<4, 16>),
+                       dim3((d + 4 * kWave - 1) / (4 * kWave), chunks, (Np + 15) / 16), dim3(kWave), 0, s, x, src0,
+                       src1, partial, T, d, N);
+  const int64_t n_out = (int64_t)d * Np;
+  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, partial, out0,
+                     out1, chunks, d, N, Np);
   return hipGetLastError();
 }
 
@@ -879,8 +1027,8 @@ hipError_t launch_colsum_bf16(const bf16* src, const int32_t* off, float* out, i
 hipError_t launch_column_sum(const float* src, float* partial, float* out, int T, int N, hipStream_t s) {
   const int chunks = gate_grad_chunks(T);
   hipLaunchKernelGGL(column_sum_partial_kernel, dim3(chunks), dim3(256), 0, s, src, partial, T, N);
-  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((N + 255) / 256), dim3(256), 0, s, partial, out, chunks,
-                     (int64_t)N);
+  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((N + 255) / 256), dim3(256), 0, s, partial, out, out, chunks, 1,
+                     N, N);
   return hipGetLastError();
 }
 

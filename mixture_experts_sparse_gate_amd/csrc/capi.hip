@@ -210,7 +210,8 @@ BackwardWs backward_ws(const moe_desc_t* d) {
   w.imp = take((size_t)d->N * 4);
   w.dimp = take((size_t)d->N * 4);
   const size_t chunks = (size_t)moe::gate_grad_chunks(d->T);
-  const size_t gp = chunks * d->d * d->N * 4, bp = chunks * d->N * 4;
+  const size_t np = (size_t)d->N * (d->gate == MOE_GATE_NOISY ? 2 : 1);
+  const size_t gp = chunks * d->d * np * 4, bp = chunks * d->N * 4;
   w.gpart = take(gp > bp ? gp : bp);
   w.bytes = o;
   return w;
@@ -969,8 +970,9 @@ moe_status_t moe_backward(const moe_desc_t* desc, const moe_backward_tensors_t* 
   TRY(hip_status(moe::launch_bwd_token(tp, s), "backward: tokens"));
   // the gate's weights and logit bias
   float* part = at<float>(ws, bw.gpart);
-  TRY(hip_status(moe::launch_gate_grad(tp.x, dl, part, t->dw_gate, T, d, N, s), "backward: dw_gate"));
-  if (noisy) TRY(hip_status(moe::launch_gate_grad(tp.x, dz, part, t->dw_noise, T, d, N, s), "backward: dw_noise"));
+  TRY(hip_status(moe::launch_gate_grad(tp.x, dl, noisy ? dz : nullptr, part, t->dw_gate, noisy ? t->dw_noise : nullptr,
+                                       T, d, N, s),
+                 "backward: dw_gate, dw_noise"));
   if (t->dlogit_bias)
     TRY(hip_status(moe::launch_column_sum(dl, part, t->dlogit_bias, T, N, s), "backward: dlogit_bias"));
   // the expert biases

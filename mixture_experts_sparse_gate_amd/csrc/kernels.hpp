@@ -209,9 +209,11 @@ struct BwdTokenParams {
 };
 hipError_t launch_bwd_token(const BwdTokenParams& p, hipStream_t s);
 int gate_grad_chunks(int64_t T);
-// out [d, N] = x^T src (src [T, N] fp32), through partial [gate_grad_chunks(T), d, N]
-hipError_t launch_gate_grad(const bf16* x, const float* src, float* partial, float* out, int T, int d, int N,
-                            hipStream_t s);
+// out0 [d, N] = x^T src0 and (src1 non-null) out1 [d, N] = x^T src1, src
+// [T, N] fp32, through partial [gate_grad_chunks(T), d, N'] (N' = 2N with
+// src1, else N)
+hipError_t launch_gate_grad(const bf16* x, const float* src0, const float* src1, float* partial, float* out0,
+                            float* out1, int T, int d, int N, hipStream_t s);
 // out [N] = column sums of src [T, N], through partial [gate_grad_chunks(T), N]
 hipError_t launch_column_sum(const float* src, float* partial, float* out, int T, int N, hipStream_t s);
 // out [groups, cols] = per group the sums of its rows [off[g], off[g+1]) of src [rows, cols]
