@@ -427,16 +427,21 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     // everything but the previous step's weight loads (this step's pair was
     // started two steps back), an odd step for everything but the last two
     // steps' loads (its weights were started three steps back, by an even step).
+    // (The prologue's loads are issued in program order, scheduling barriers
+    // between them.)
     const int nk = (K + BK - 1) / BK;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     issue_a(a_stage(I0{}), 0);
+    __builtin_amdgcn_sched_barrier(0);
     issue_b(b_stage(I0{}), 0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (S > 2) {
       if constexpr (AP == 1) issue_a(a_stage(I1{}), BK);
       issue_b(b_stage(I1{}), BK);
     }
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (S > 3) {
       if constexpr (AP == 1) issue_a(a_stage(I2{}), 2 * BK);
       issue_b(b_stage(I2{}), 2 * BK);
@@ -524,8 +529,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       // Every wave passes the same barriers: two per step in either order.
       // Before the barrier that precedes group 0's mem(t), every wave waits
       // for its loads of step t (both groups have then issued mem(0..t-1)):
-      // all but the last B_INST loads (t even) or AI + 2 B_INST (t odd);
-      // before the other barrier only for its LDS reads.
+      // all but the last 2 B_INST loads (t even: mem issues a pair's loads
+      // ahead of the weight loads, a scheduling barrier keeping that order,
+      // so the last two weight stages were issued after step t's pair) or
+      // AI + 2 B_INST (t odd); before the other barrier only for its LDS reads.
       const int grp = wave >> 2;
       // The memory phase runs at raised wave priority, so that its reads and
       // loads issue ahead of the other wave's MFMAs (measured: +0.5 % on the
@@ -535,7 +542,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         constexpr int cur = decltype(st)::value;
         constexpr int nxt = (cur + S - 1) % S;
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (cur % 2 == 0) issue_a(a_stage(std::integral_constant<int, (cur + 2) % 4>{}), (kt + 2) * BK);
+        if constexpr (cur % 2 == 0) {
+          issue_a(a_stage(std::integral_constant<int, (cur + 2) % 4>{}), (kt + 2) * BK);
+          __builtin_amdgcn_sched_barrier(0);  // the pair's loads ahead of the weight loads
+        }
         issue_b(b_stage(std::integral_constant<int, nxt>{}), (kt + S - 1) * BK);
         load_frags(a_stage(st), b_stage(st), 0, 0, (cur & 1) ? 64 : 0);
         load_frags(a_stage(st), b_stage(st), 1, 1, (cur & 1) ? 64 : 0);
@@ -553,7 +563,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       };
       // waits before the barrier ahead of group 0's mem(t)
       auto sync_data = [&](auto t_c) {
-        if constexpr (decltype(t_c)::value % 2 == 0) wait_vmcnt_lds<C::B_INST>();
+        if constexpr (decltype(t_c)::value % 2 == 0) wait_vmcnt_lds<2 * C::B_INST>();
         else wait_vmcnt_lds<AI + 2 * C::B_INST>();
         __builtin_amdgcn_s_barrier();
       };
