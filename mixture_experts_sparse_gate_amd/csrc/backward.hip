@@ -848,8 +848,8 @@ __global__ __launch_bounds__(256) void column_sum_partial_kernel(const float* sr
 // partial[c][i][n] = sum over the tokens t of chunk c (ascending) of
 // x[t][i] src[t][n], where src is src0 for n < N and src1 (the noisy
 // gate's dz, or null) for N <= n < 2N. One wave per block: lane l holds
-// IL consecutive columns i (one 8- or 16-byte load of x per token) times
-// NL experts from blockIdx.z NL; the chunk's src values sit in LDS.
+// IL consecutive columns i (one 8-byte load of x per token) times NL
+// experts from blockIdx.z NL; the chunk's src values sit in LDS.
 template <int IL, int NL>
 __global__ __launch_bounds__(kWave) void gate_grad_partial_kernel(const bf16* x, const float* src0,
                                                                   const float* src1, float* partial, int T, int d,
@@ -907,17 +907,33 @@ __global__ __launch_bounds__(kWave) void gate_grad_partial_kernel(const bf16* x,
 }
 
 // the chunks' partial sums added in chunk order: column n < N of
-// partial[.][i] into out0[i][n], n >= N into out1[i][n - N]
-__global__ __launch_bounds__(256) void gate_grad_final_kernel(const float* partial, float* out0, float* out1,
-                                                              int chunks, int d, int N, int Np) {
-  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// partial[.][i] into out0[i][n], n >= N into out1[i][n - N]. A block takes
+// 64 outputs; wave w adds chunks w cs .. (w + 1) cs - 1 in order (cs =
+// ceil(chunks / 8)), and wave 0 adds the eight sums in wave order.
+constexpr int kFinalWaves = 8;
+__global__ __launch_bounds__(kWave * kFinalWaves) void gate_grad_final_kernel(const float* partial, float* out0,
+                                                                             float* out1, int chunks, int d, int N,
+                                                                             int Np) {
+  __shared__ float s_part[kFinalWaves][kWave];
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   const int64_t n_out = (int64_t)d * Np;
-  if (q >= n_out) return;
+  const int64_t q = (int64_t)blockIdx.x * kWave + lane;
+  const int cs = (chunks + kFinalWaves - 1) / kFinalWaves;
+  const int c0 = w * cs, c1 = min(chunks, c0 + cs);
   float s = 0.f;
-  for (int c = 0; c < chunks; ++c) s += partial[(int64_t)c * n_out + q];
+  if (q < n_out) {
+#pragma unroll 8
+    for (int c = c0; c < c1; ++c) s += partial[(int64_t)c * n_out + q];
+  }
+  s_part[w][lane] = s;
+  __syncthreads();
+  if (w != 0 || q >= n_out) return;
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < kFinalWaves; ++j) t += s_part[j][lane];
   const int i = (int)(q / Np), n = (int)(q % Np);
-  if (n < N) out0[(int64_t)i * N + n] = s;
-  else out1[(int64_t)i * N + n - N] = s;
+  if (n < N) out0[(int64_t)i * N + n] = t;
+  else out1[(int64_t)i * N + n - N] = t;
 }
 
 // out[e][c] = sum over rows [off[e], off[e+1]) of src[row][c], rows in
@@ -1005,15 +1021,15 @@ hipError_t launch_gate_grad(const bf16* x, const float* src0, const float* src1,
   const int chunks = gate_grad_chunks(T);
   const int Np = src1 ? 2 * N : N;
   if (Np <= 8)
-    hipLaunchKernelGGL((gate_grad_partial_kernel<8, 8>), dim3((d + 8 * kWave - 1) / (8 * kWave), chunks, 1),
+    hipLaunchKernelGGL((gate_grad_partial_kernel<4, 8>), dim3((d + 4 * kWave - 1) / (4 * kWave), chunks, 1),
                        dim3(kWave), 0, s, x, src0, src1, partial, T, d, N);
   else
     hipLaunchKernelGGL((gate_grad_partial_kernel<4, 16>),
                        dim3((d + 4 * kWave - 1) / (4 * kWave), chunks, (Np + 15) / 16), dim3(kWave), 0, s, x, src0,
                        src1, partial, T, d, N);
   const int64_t n_out = (int64_t)d * Np;
-  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, partial, out0,
-                     out1, chunks, d, N, Np);
+  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((unsigned)((n_out + kWave - 1) / kWave)),
+                     dim3(kWave * kFinalWaves), 0, s, partial, out0, out1, chunks, d, N, Np);
   return hipGetLastError();
 }
 
@@ -1027,8 +1043,8 @@ hipError_t launch_colsum_bf16(const bf16* src, const int32_t* off, float* out, i
 hipError_t launch_column_sum(const float* src, float* partial, float* out, int T, int N, hipStream_t s) {
   const int chunks = gate_grad_chunks(T);
   hipLaunchKernelGGL(column_sum_partial_kernel, dim3(chunks), dim3(256), 0, s, src, partial, T, N);
-  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((N + 255) / 256), dim3(256), 0, s, partial, out, out, chunks, 1,
-                     N, N);
+  hipLaunchKernelGGL(gate_grad_final_kernel, dim3((N + kWave - 1) / kWave), dim3(kWave * kFinalWaves), 0, s, partial,
+                     out, out, chunks, 1, N, N);
   return hipGetLastError();
 }
 
