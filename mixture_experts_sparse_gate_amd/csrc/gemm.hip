@@ -666,10 +666,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     constexpr int CPR = C::WTN * OB / 16;  // 16-byte chunks per slice row
     constexpr int RPI = kWave / CPR;       // slice rows per 64-lane read
     constexpr int REG = 32 * CPR * 16;     // bytes of one slice
+    // wave w's region: slot w / S of stage buffer w % S while the stage
+    // buffers hold every wave's; past that (8-wave 128 x 128 tiles), the
+    // activation pair buffers, two regions each
     constexpr int WPS = (C::THREADS / kWave + S - 1) / S;  // waves per stage buffer
-    static_assert(WPS * REG <= ST, "epilogue slices fit the stage buffers");
-    const int wsel = wave % S;
-    char* const reg = (wsel == 0 ? st0 : wsel == 1 ? st1 : wsel == 2 ? st2 : st3) + (wave / S) * REG;
+    constexpr int PST = ST / REG;                          // regions per stage buffer
+    constexpr int PSA = AP == 2 ? C::A_STAGE / REG : 0;    // regions per activation pair buffer
+    static_assert(WPS <= PST || (AP == 2 && PST >= 1 && PST * S + 2 * PSA >= C::THREADS / kWave),
+                  "epilogue slices fit the stage buffers");
+    char* reg;
+    if (WPS <= PST || wave < PST * S) {
+      const int wsel = wave % S;
+      reg = (wsel == 0 ? st0 : wsel == 1 ? st1 : wsel == 2 ? st2 : st3) + (wave / S) * REG;
+    } else {
+      const int w2 = wave - PST * S;
+      reg = (w2 / PSA == 0 ? sa0 : sa1) + (w2 % PSA) * REG;
+    }
     O* Cp = static_cast<O*>(p.C);
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
@@ -1212,6 +1224,14 @@ hipError_t launch_dtype(const GemmParams& p, int avg_rows, int max_rows, hipStre
   const int64_t tiles256 = (int64_t)(p.M / 256 + groups) * ((p.Ncols + 255) / 256);
   if (tiles256 >= kNumCUs / 2)
     return launch_cfg<Cfg<E, O, 256, 256, 2, 4, 4, 4, G>>(p, s, ev);
+  // bf16, at most one 128x128 tile per CU (e.g. the cosine gate's
+  // projection, a single group of T rows by 256 columns): eight waves of
+  // 32 x 64, two per SIMD, so that one wave's waits are covered by the
+  // other's MFMAs
+  if constexpr (sizeof(E) == 2) {
+    const int64_t tiles128 = (int64_t)(p.M / 128 + groups) * ((p.Ncols + 127) / 128);
+    if (tiles128 <= kNumCUs) return launch_cfg<Cfg<E, O, 128, 128, 4, 2, 4, 4, G>>(p, s, ev);
+  }
   return launch_cfg<Cfg<E, O, 128, 128, 2, 2, 4, 4, G>>(p, s, ev);
 }
 
