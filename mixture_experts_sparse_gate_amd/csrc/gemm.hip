@@ -220,10 +220,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
                                           bool coherent_out = false) {
   using E = typename C::Elem;
   using O = typename C::Out;
-  constexpr int CE = C::CE, KC = C::KC, BK = C::BK, BM = C::BM, BN = C::BN, ES = C::ES, S = C::S;
+  constexpr int CE = C::CE, KC = C::KC, BK = C::BK, ES = C::ES, S = C::S;
   constexpr int AP = C::AP, KCA = C::KCA;
   constexpr int ST = AP == 1 ? C::A_STAGE + C::B_STAGE : C::B_STAGE;  // bytes of st0..st3
-  (void)BM;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
@@ -675,12 +674,13 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     static_assert(WPS <= PST || (AP == 2 && PST >= 1 && PST * S + 2 * PSA >= C::THREADS / kWave),
                   "epilogue slices fit the stage buffers");
     char* reg;
-    if (WPS <= PST || wave < PST * S) {
-      const int wsel = wave % S;
+    const int wsel = wave % S;
+    if constexpr (WPS <= PST) {
       reg = (wsel == 0 ? st0 : wsel == 1 ? st1 : wsel == 2 ? st2 : st3) + (wave / S) * REG;
     } else {
       const int w2 = wave - PST * S;
-      reg = (w2 / PSA == 0 ? sa0 : sa1) + (w2 % PSA) * REG;
+      if (w2 < 0) reg = (wsel == 0 ? st0 : wsel == 1 ? st1 : wsel == 2 ? st2 : st3) + (wave / S) * REG;
+      else reg = (w2 / PSA == 0 ? sa0 : sa1) + (w2 % PSA) * REG;
     }
     O* Cp = static_cast<O*>(p.C);
 #pragma unroll
@@ -747,8 +747,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p, const float* bscale) {
-  using E = typename C::Elem;
-  using O = typename C::Out;
   constexpr int BM = C::BM, BN = C::BN;
   // one LDS object per stage, so that the compiler can tell a stage being
   // filled by the asynchronous loads from the one being read. AP == 1: stage
@@ -761,7 +759,6 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p, 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
-  const int wm = wave / C::WN, wn = wave % C::WN;
   // ---- tile schedule. A group's rows make full-height tiles of BM rows;
   // with tail tiles (HAS_TAIL), a remainder of at most BM/2 rows makes
   // tiles of TBM rows instead of one partial full-height tile. Phase 0 lists
