@@ -866,7 +866,15 @@ moe_status_t moe_backward(const moe_desc_t* desc, const moe_backward_tensors_t* 
   g.N = h;
   g.K = d;
   g.groups = N;
-  TRY(hip_status(moe::launch_bwd_gemm(g, moe::BwdGemmKind::kRecompute, s), "backward: U, H"));
+  {
+    // U and H on the forward's GEMM1 tiles (same K order and GELU, so H
+    // repeats the forward's bits), storing the pre-activation as well
+    moe::GemmParams g1, g2;
+    ffn_gemms(desc, t->x, t->token_of_row, t->expert_off, t->W1, t->b1, t->W2, t->b2, H, nullptr, &g1, &g2);
+    g1.C2 = U;
+    const int avg_rows = (int)((desc->T * desc->k) / desc->N);
+    TRY(hip_status(moe::launch_grouped_gemm_dual(g1, avg_rows, s), "backward: U, H"));
+  }
   moe::BwdGemmParams gg = g;
   gg.A = t->dy;
   gg.B = t->W2;

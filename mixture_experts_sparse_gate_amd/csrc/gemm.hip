@@ -104,11 +104,14 @@ constexpr int kW8ScaleRegs = kW8MaxK / (128 * 64);
 
 // W8_: the weights are block-FP8 codes in K-groups of 8 (GemmW8) instead of
 // E values; the activations stay E.
-template <typename E, typename O, int BM_, int BN_, int WM_, int WN_, int KC_, int S_, bool GELU_, bool W8_ = false>
+// DUAL_: GELU launches also store the pre-activation (GemmParams::C2).
+template <typename E, typename O, int BM_, int BN_, int WM_, int WN_, int KC_, int S_, bool GELU_, bool W8_ = false,
+          bool DUAL_ = false>
 struct Cfg {
   using Elem = E;
   using Out = O;
   static constexpr bool W8 = W8_;
+  static constexpr bool DUAL = DUAL_;
   static constexpr int ES = sizeof(E);
   static constexpr int CE = ElemTraits<E>::kPerChunk;   // elements per 16-byte chunk
   static constexpr int KC = KC_;                         // 16-byte chunks of K per activation row per stage
@@ -682,59 +685,122 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       if (w2 < 0) reg = (wsel == 0 ? st0 : wsel == 1 ? st1 : wsel == 2 ? st2 : st3) + (wave / S) * REG;
       else reg = (w2 / PSA == 0 ? sa0 : sa1) + (w2 % PSA) * REG;
     }
-    O* Cp = static_cast<O*>(p.C);
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int frow = row_lo + wm * WTM + j * 32;
-      if (frow >= row_hi) break;  // wave-uniform
-      // bias and GELU over the whole slice, each behind one uniform branch
-      if (has_bias) {
-#pragma unroll
-        for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][q], r);
-      }
-      if (gelu) {
-#pragma unroll
-        for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            acc[i][j][r] = std::is_same_v<O, bf16> ? gelu_erf_bf16(acc[i][j][r]) : gelu_erf(acc[i][j][r]);
-      }
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int cb = (i * 32 + 8 * q + 4 * lhalf) * OB;  // byte offset in the slice row
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-          Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int t = 0; t < 32 / RPI; ++t) {
-        const int rr = t * RPI + lane / CPR, ch = lane % CPR;
-        const u32x4 val = *(lds_u32x4*)(reg + rr * CPR * 16 + ((ch ^ swz_c<OB>(rr)) * 16));
-        const int col = ccol0 + ch * (16 / OB);
-        if (frow + rr < row_hi && col < Ncols) {
-          if (coherent_out) {
-            // the slice's 32 rows as one buffer range
-            const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cp + (int64_t)frow * p.ldc, (uint32_t)(32 * p.ldc * OB));
-            __builtin_amdgcn_raw_buffer_store_b128(val, rc, (rr * (int)p.ldc + col) * OB, 0, kCpolSc1);
-          } else {
-            *reinterpret_cast<u32x4*>(Cp + (int64_t)(frow + rr) * p.ldc + col) = val;
+    if constexpr (C::DUAL) {
+      // both the pre-activation (C2) and the activation (C), each slice
+      // through the same region
+      // slice j's values (acc[.][j]) through the wave's region into rows of Dp
+      auto store_slice = [&](O* Dp, int j, int frow) {
+  #pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cb = (i * 32 + 8 * q + 4 * lhalf) * OB;  // byte offset in the slice row
+            float v[4];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+            Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
           }
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  #pragma unroll
+        for (int t = 0; t < 32 / RPI; ++t) {
+          const int rr = t * RPI + lane / CPR, ch = lane % CPR;
+          const u32x4 val = *(lds_u32x4*)(reg + rr * CPR * 16 + ((ch ^ swz_c<OB>(rr)) * 16));
+          const int col = ccol0 + ch * (16 / OB);
+          if (frow + rr < row_hi && col < Ncols) {
+            if (coherent_out) {
+              // the slice's 32 rows as one buffer range
+              const __amdgpu_buffer_rsrc_t rc = make_rsrc(Dp + (int64_t)frow * p.ldc, (uint32_t)(32 * p.ldc * OB));
+              __builtin_amdgcn_raw_buffer_store_b128(val, rc, (rr * (int)p.ldc + col) * OB, 0, kCpolSc1);
+            } else {
+              *reinterpret_cast<u32x4*>(Dp + (int64_t)(frow + rr) * p.ldc + col) = val;
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      };
+  #pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int frow = row_lo + wm * WTM + j * 32;
+        if (frow >= row_hi) break;  // wave-uniform
+        // bias and GELU over the whole slice, each behind one uniform branch
+        if (has_bias) {
+  #pragma unroll
+          for (int i = 0; i < C::FN; ++i)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][q], r);
+        }
+        store_slice(static_cast<O*>(p.C2), j, frow);  // the pre-activation
+        if (gelu) {
+  #pragma unroll
+          for (int i = 0; i < C::FN; ++i)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[i][j][r] = std::is_same_v<O, bf16> ? gelu_erf_bf16(acc[i][j][r]) : gelu_erf(acc[i][j][r]);
+        }
+        store_slice(static_cast<O*>(p.C), j, frow);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      O* Cp = static_cast<O*>(p.C);
+  #pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int frow = row_lo + wm * WTM + j * 32;
+        if (frow >= row_hi) break;  // wave-uniform
+        // bias and GELU over the whole slice, each behind one uniform branch
+        if (has_bias) {
+  #pragma unroll
+          for (int i = 0; i < C::FN; ++i)
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+  #pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][q], r);
+        }
+        if (gelu) {
+  #pragma unroll
+          for (int i = 0; i < C::FN; ++i)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r)
+              acc[i][j][r] = std::is_same_v<O, bf16> ? gelu_erf_bf16(acc[i][j][r]) : gelu_erf(acc[i][j][r]);
+        }
+  #pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int cb = (i * 32 + 8 * q + 4 * lhalf) * OB;  // byte offset in the slice row
+            float v[4];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+            Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  #pragma unroll
+        for (int t = 0; t < 32 / RPI; ++t) {
+          const int rr = t * RPI + lane / CPR, ch = lane % CPR;
+          const u32x4 val = *(lds_u32x4*)(reg + rr * CPR * 16 + ((ch ^ swz_c<OB>(rr)) * 16));
+          const int col = ccol0 + ch * (16 / OB);
+          if (frow + rr < row_hi && col < Ncols) {
+            if (coherent_out) {
+              // the slice's 32 rows as one buffer range
+              const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cp + (int64_t)frow * p.ldc, (uint32_t)(32 * p.ldc * OB));
+              __builtin_amdgcn_raw_buffer_store_b128(val, rc, (rr * (int)p.ldc + col) * OB, 0, kCpolSc1);
+            } else {
+              *reinterpret_cast<u32x4*>(Cp + (int64_t)(frow + rr) * p.ldc + col) = val;
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
     }
   };
   if constexpr (C::HAS_TAIL) {
@@ -1298,6 +1364,17 @@ hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t*
     else launch(fused_ffn_kernel<FusedCfg, false, false>);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_dual(const GemmParams& p, int avg_rows, hipStream_t s) {
+  // the tile choice of launch_dtype<bf16, bf16, GELU>
+  if (avg_rows < 64) return launch_cfg<Cfg<bf16, bf16, 32, 256, 1, 4, 8, 4, true, false, true>>(p, s, {});
+  const int groups = p.seg ? p.groups : 0;
+  const int64_t tiles256 = (int64_t)(p.M / 256 + groups) * ((p.Ncols + 255) / 256);
+  if (tiles256 >= kNumCUs / 2) return launch_cfg<Cfg<bf16, bf16, 256, 256, 2, 4, 4, 4, true, false, true>>(p, s, {});
+  const int64_t tiles128 = (int64_t)(p.M / 128 + groups) * ((p.Ncols + 127) / 128);
+  if (tiles128 <= kNumCUs) return launch_cfg<Cfg<bf16, bf16, 128, 128, 4, 2, 4, 4, true, false, true>>(p, s, {});
+  return launch_cfg<Cfg<bf16, bf16, 128, 128, 2, 2, 4, 4, true, false, true>>(p, s, {});
 }
 
 hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, int avg_rows, hipStream_t s,

@@ -96,6 +96,7 @@ struct GemmParams {
   int64_t lda, ldc, strideB, strideBias;
   int M;                // rows when seg is null; else the row bound R
   int groups, K, Ncols;
+  void* C2;             // launch_grouped_gemm_dual: the pre-activation rows (as C), else unused
 };
 enum class GemmKind { kFfn1Gelu, kFfn2, kProjF32 };
 // Block-FP8 weights (launch_grouped_gemm_w8): B holds E4M3 codes in K-groups
@@ -116,6 +117,10 @@ struct LaunchEvents {
 // 32-row tiles that stream the weights below 64, else 256 x 256).
 hipError_t launch_grouped_gemm_w8(const GemmParams& p, GemmW8 w8, GemmKind kind, int avg_rows, hipStream_t s,
                                   LaunchEvents ev = {});
+// bf16 GEMM1 of the FFN storing both the pre-activation U = A B + bias (C2)
+// and H = GELU(U) (C), with the tiles, K order and GELU of the forward's
+// GEMM1 (the backward's recompute of U and H)
+hipError_t launch_grouped_gemm_dual(const GemmParams& p, int avg_rows, hipStream_t s);
 // E4M3 block quantisation (quant.hip): W [groups, K, Ncols] fp32 or bf16,
 // K and Ncols multiples of 128
 hipError_t launch_quantize_fp8(const void* W, bool bf16, int groups, int K, int Ncols, uint8_t* codes,
