@@ -411,67 +411,6 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
     }
     return;
   }
-  if constexpr (EPI == BwdEpi::kDualGelu) {
-    // U = acc + b1 and H = GELU(U), both bf16: each 32-row slice of the
-    // wave's tile goes through two per-wave LDS regions (32 rows of 128
-    // bytes, 16-byte chunk c of row r at c ^ (r % 8)) and back as 16-byte
-    // pieces of rows, 8 lanes per row, so that the stores write whole
-    // 128-byte row segments
-    __syncthreads();  // every wave is done reading the stage buffers
-    constexpr int REG = 2 * 32 * 128;
-    constexpr int PER = 2 * OPB / REG;
-    static_assert(PER >= 1 && (THREADS / kWave) <= 4 * PER, "epilogue regions fit the stage buffers");
-    const int bsel = wave / PER;
-    char* const ru = (bsel == 0 ? st0 : bsel == 1 ? st1 : bsel == 2 ? st2 : st3) + (wave % PER) * REG;
-    char* const rh = ru + 32 * 128;
-    const int lrow = lane & 31;
-    const int cb = n0 + wn * 64;
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int frow = m0 + wm * T::WTM + 32 * j;
-      if (frow >= m1) break;  // wave-uniform
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = cb + 32 * i + 8 * q + 4 * (lane >> 5);
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-          if (p.bias && n < p.N) {
-            const u32x2 bb = *reinterpret_cast<const u32x2*>(static_cast<const bf16*>(p.bias) + (int64_t)g * p.N + n);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] += chunk_elem<bf16>(u32x4{bb[0], bb[1], 0u, 0u}, r);
-          }
-          const int off = lrow * 128 + (((4 * i + q) ^ (lrow & 7)) * 16) + 8 * (lane >> 5);
-          *(lds_u32x2w*)(ru + off) = u32x2{f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                                           f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16)};
-          *(lds_u32x2w*)(rh + off) =
-              u32x2{f32_to_bf16_bits(gelu_erf_bf16(v[0])) | (f32_to_bf16_bits(gelu_erf_bf16(v[1])) << 16),
-                    f32_to_bf16_bits(gelu_erf_bf16(v[2])) | (f32_to_bf16_bits(gelu_erf_bf16(v[3])) << 16)};
-        }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int rr = 8 * t + (lane >> 3), ch = lane & 7;
-        const int off = rr * 128 + ((ch ^ (rr & 7)) * 16);
-        const u32x4 uv = *(lds_u32x4*)(ru + off);
-        const u32x4 hv = *(lds_u32x4*)(rh + off);
-        const int col = cb + 8 * ch;
-        if (frow + rr < m1 && col < p.N) {
-          const int64_t at = (int64_t)(frow + rr) * p.ldc + col;
-          *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.C) + at) = uv;
-          *reinterpret_cast<u32x4*>(static_cast<bf16*>(p.C2) + at) = hv;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    return;
-  }
   if constexpr (EPI == BwdEpi::kGeluGrad) {
     // G = dy W2^T (fp32 in acc): each 32-row slice of the wave's tile goes
     // through a per-wave LDS region (as the fp32 outputs above) into row
@@ -984,8 +923,6 @@ hipError_t launch_bwd(const BwdGemmParams& p, hipStream_t s) {
 hipError_t launch_bwd_gemm(const BwdGemmParams& p, BwdGemmKind kind, hipStream_t s) {
   using L = BwdLayout;
   switch (kind) {
-    case BwdGemmKind::kRecompute:  // U, H = GELU(U): gathered x rows, W1 [K][N]
-      return launch_bwd<L::kKContig, L::kKStrided, BwdEpi::kDualGelu, bf16, false>(p, s);
     case BwdGemmKind::kGeluGrad:  // dU: gathered dy rows, W2_e rows [N][K]
       return launch_bwd<L::kKContig, L::kKContig, BwdEpi::kGeluGrad, bf16, false>(p, s);
     case BwdGemmKind::kDataGrad:  // dx_perm = dU W1_e^T, fp32

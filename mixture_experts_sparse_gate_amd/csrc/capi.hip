@@ -847,25 +847,6 @@ moe_status_t moe_backward(const moe_desc_t* desc, const moe_backward_tensors_t* 
   TRY(hip_status(moe::launch_scale_rows(static_cast<const bf16*>(t->dy), t->row_of, t->topk_w, dY, T, d, k, s),
                  "backward: dY rows"));
   // U and H (recomputed), then dU and the partial dots G . H
-  moe::BwdGemmParams g{};
-  g.A = t->x;
-  g.gather = t->token_of_row;
-  g.gather_div = k;
-  g.lda = d;
-  g.a_bytes = (int64_t)T * d * 2;
-  g.B = t->W1;
-  g.ldb = h;
-  g.strideB = (int64_t)d * h;
-  g.b_bytes = (int64_t)d * h * 2;
-  g.C = U;
-  g.C2 = H;
-  g.ldc = h;
-  g.bias = t->b1;
-  g.seg = t->expert_off;
-  g.M = R;
-  g.N = h;
-  g.K = d;
-  g.groups = N;
   {
     // U and H on the forward's GEMM1 tiles (same K order and GELU, so H
     // repeats the forward's bits), storing the pre-activation as well
@@ -875,14 +856,24 @@ moe_status_t moe_backward(const moe_desc_t* desc, const moe_backward_tensors_t* 
     const int avg_rows = (int)((desc->T * desc->k) / desc->N);
     TRY(hip_status(moe::launch_grouped_gemm_dual(g1, avg_rows, s), "backward: U, H"));
   }
-  moe::BwdGemmParams gg = g;
+  // G = dy_perm W2_e^T (dy rows gathered as the x rows are; K = d)
+  moe::BwdGemmParams gg{};
   gg.A = t->dy;
+  gg.gather = t->token_of_row;
+  gg.gather_div = k;
+  gg.lda = d;
+  gg.a_bytes = (int64_t)T * d * 2;
   gg.B = t->W2;
   gg.ldb = d;
   gg.strideB = (int64_t)h * d;
+  gg.b_bytes = (int64_t)d * h * 2;
   gg.C = dU;
-  gg.C2 = nullptr;
-  gg.bias = nullptr;
+  gg.ldc = h;
+  gg.seg = t->expert_off;
+  gg.M = R;
+  gg.N = h;
+  gg.K = d;
+  gg.groups = N;
   gg.U = U;
   gg.H = H;
   gg.row_w = t->topk_w;

@@ -161,9 +161,8 @@ hipError_t launch_ffn_status(const int32_t* counters, int32_t* out, hipStream_t 
 typedef __bf16 bf16;
 constexpr int kMaxExperts = 256;
 enum class BwdLayout { kKContig, kKStrided };  // an operand's rows hold K (contiguous) or M / N (K strided)
-enum class BwdEpi { kPlain, kDualGelu, kGeluGrad };
+enum class BwdEpi { kPlain, kGeluGrad };
 enum class BwdGemmKind {
-  kRecompute,   // U = x_perm W1 + b1 and H = GELU(U): A gathered rows (K = d), B = W1 [d][h]; C = U, C2 = H
   kGeluGrad,    // G = dy_perm W2^T: A gathered dy rows, B = W2_e rows [h][d]; C = dU = bf16(w G GELU'(U)),
                 // pd = per-row dots G . H over each 128-column tile
   kDataGrad,    // dx_perm = dU W1_e^T: A = dU rows (K = h), B = W1_e rows [d][h]; C fp32
@@ -180,8 +179,6 @@ struct BwdGemmParams {
   int gather_div;
   int a_rows;            // kWeightGrad: rows of A and B (bound of seg)
   int M, N, K, groups;   // ragged M: M = row bound; kWeightGrad: each group's C is M x N
-  const void* bias;      // kRecompute: [groups, N] bf16 or null
-  void* C2;              // kRecompute: H
   const void* U;         // kGeluGrad: [rows, N] bf16
   const void* H;         // kGeluGrad: [rows, N] bf16
   const float* row_w;    // kGeluGrad: gate weight of choice t*k+j
