@@ -41,6 +41,9 @@ namespace {
 constexpr int kBK = 32;  // K per step
 constexpr int kNumXcd = 8;
 constexpr int64_t kBwdBigTileMin = 256;  // CUs of the chip
+// 256 x 256 tiles with at least this many K-steps run the ping-pong K loop
+// (its fixed cost per tile: one more MFMA interval, the second group's)
+constexpr int kBwdPingPongMinSteps = 32;
 
 // Output tiles of TS x TS (128 or 256): two waves along M and TS / 64 along
 // N, each wave TS / 2 rows x 64 columns (FM x FN fragments of 32 x 32).
@@ -338,31 +341,157 @@ __global__ __launch_bounds__(Tile<TS>::THREADS) void bwd_gemm_kernel(BwdGemmPara
     }
   };
 
-  // ---- four stages, one barrier per step, loads three steps ahead
+  // ---- four stages, loads three steps ahead. The prologue's loads go out
+  // in program order (scheduling barriers between them), so that counting
+  // the loads still in flight tells which steps have landed.
   const int nk = (K + kBK - 1) / kBK;
   issue(st0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   issue(st1, 1);
+  __builtin_amdgcn_sched_barrier(0);
   issue(st2, 2);
   // kGeluGrad: the weight of tile row tid, read while the first stages load
   float w_pre = 0.f;
   if constexpr (EPI == BwdEpi::kGeluGrad)
     if (tid < TS && m0 + tid < m1) w_pre = p.row_w[p.tor[m0 + tid]];
-  auto step = [&](char* cur, char* nxt, int kt) {
-    wait_loads_and_lds<4 * LOADS>();  // this step's loads have landed; the previous stage is read
-    __builtin_amdgcn_s_barrier();
-    issue(nxt, kt + 3);
-    compute(cur);
+  // one barrier per step: wait until this step's loads have landed and this
+  // wave's reads of the previous stage have returned, barrier, load into
+  // the stage just freed, compute
+  auto one_barrier_loop = [&]() {
+    auto step = [&](char* cur, char* nxt, int kt) {
+      wait_loads_and_lds<4 * LOADS>();
+      __builtin_amdgcn_s_barrier();
+      issue(nxt, kt + 3);
+      compute(cur);
+    };
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
+      step(st0, st3, kt);
+      step(st1, st0, kt + 1);
+      step(st2, st1, kt + 2);
+      step(st3, st2, kt + 3);
+    }
+    if (kt < nk) step(st0, st3, kt);
+    if (kt + 1 < nk) step(st1, st0, kt + 1);
+    if (kt + 2 < nk) step(st2, st1, kt + 2);
   };
-  int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    step(st0, st3, kt);
-    step(st1, st0, kt + 1);
-    step(st2, st1, kt + 2);
-    step(st3, st2, kt + 3);
+  if constexpr (TS == 256) {
+    if (nk >= kBwdPingPongMinSteps) {
+      // Ping-pong: waves 0-3 and 4-7 (one of each per SIMD) run the same
+      // steps half a step apart, two barriers per step, so that while one
+      // wave of a SIMD issues a step's MFMAs (its fragments already in
+      // registers) the other reads its next fragments and issues its loads.
+      // Group 0: [mem(t) | mma(t)] per step; group 1: [mma(t-1) | mem(t)],
+      // its first mma on zero fragments (adds nothing) and its last after
+      // the loop. mem(t) loads step t + 3 into the stage of step t - 1,
+      // which both groups have read before the barrier that precedes it.
+      // Before that barrier every wave waits for its loads of step t: all
+      // but the last two steps' (4 LOADS).
+      const int grp = wave >> 2;
+      u32x4 pa[2][FM], pb[2][FN];
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f) pa[ss][f] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int f = 0; f < FN; ++f) pb[ss][f] = u32x4{0u, 0u, 0u, 0u};
+      }
+      auto stage = [&](auto c) -> char* {
+        constexpr int i = decltype(c)::value % 4;
+        if constexpr (i == 0) return st0;
+        else if constexpr (i == 1) return st1;
+        else if constexpr (i == 2) return st2;
+        else return st3;
+      };
+      // the memory phase runs at raised wave priority, so that its reads and
+      // loads issue ahead of the other wave's MFMAs
+      auto mem = [&](auto c, int kt) {
+        constexpr int cur = decltype(c)::value;
+        const char* st = stage(c);
+        __builtin_amdgcn_s_setprio(1);
+        issue(stage(std::integral_constant<int, cur + 3>{}), kt + 3);
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+          for (int f = 0; f < FN; ++f) pb[ss][f] = OB::frag(st, ob[ss][f]);
+#pragma unroll
+          for (int f = 0; f < FM; ++f) pa[ss][f] = OA::frag(st, oa[ss][f]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto mma = [&]() {
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss)
+#pragma unroll
+          for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, pb[ss][i]),
+                                                                   __builtin_bit_cast(bf16x8, pa[ss][j]), acc[i][j],
+                                                                   0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto sync_data = [&]() {
+        wait_loads_and_lds<4 * LOADS>();
+        __builtin_amdgcn_s_barrier();
+      };
+      auto sync_lds = [&]() {
+        wait_loads_and_lds<63>();
+        __builtin_amdgcn_s_barrier();
+      };
+      using J0 = std::integral_constant<int, 0>;
+      using J1 = std::integral_constant<int, 1>;
+      using J2 = std::integral_constant<int, 2>;
+      using J3 = std::integral_constant<int, 3>;
+      // Each step opens with its data wait, so that the loop head (where the
+      // compiler merges its load tracking) is followed by an explicit wait:
+      // with the memory phase there instead, the merged tracking made the
+      // first step's fragment reads wait for every load in flight.
+      if (grp == 0) {
+        auto one = [&](auto c, int kt) {
+          sync_data();
+          mem(c, kt);
+          sync_lds();
+          mma();
+        };
+        int kt = 0;
+        for (; kt + 4 <= nk; kt += 4) {
+          one(J0{}, kt);
+          one(J1{}, kt + 1);
+          one(J2{}, kt + 2);
+          one(J3{}, kt + 3);
+        }
+        if (kt < nk) one(J0{}, kt);
+        if (kt + 1 < nk) one(J1{}, kt + 1);
+        if (kt + 2 < nk) one(J2{}, kt + 2);
+        sync_data();
+      } else {
+        auto one = [&](auto c, int kt) {
+          sync_data();
+          mma();  // step kt - 1 (zero fragments before step 0)
+          sync_lds();
+          mem(c, kt);
+        };
+        int kt = 0;
+        for (; kt + 4 <= nk; kt += 4) {
+          one(J0{}, kt);
+          one(J1{}, kt + 1);
+          one(J2{}, kt + 2);
+          one(J3{}, kt + 3);
+        }
+        if (kt < nk) one(J0{}, kt);
+        if (kt + 1 < nk) one(J1{}, kt + 1);
+        if (kt + 2 < nk) one(J2{}, kt + 2);
+        sync_data();
+        mma();  // step nk - 1
+      }
+    } else {
+      one_barrier_loop();
+    }
+  } else {
+    one_barrier_loop();
   }
-  if (kt < nk) step(st0, st3, kt);
-  if (kt + 1 < nk) step(st1, st0, kt + 1);
-  if (kt + 2 < nk) step(st2, st1, kt + 2);
   wait_loads_and_lds<0>();
 
   // ---- epilogue: the lane holds D[n][m] for rows m = m0 + WTM wm + 32 j +
