@@ -730,12 +730,17 @@ __global__ __launch_bounds__(kBlock) void gate_finish_kernel(const float* __rest
 // noisy): 32 tokens per block, the 8 waves splitting d. Each wave stages its
 // own gate rows (128 at a time) in its own LDS region and runs them through
 // the MFMA; the waves' sums add up in LDS in wave order, then the block
-// forms the logits and selects for its 32 tokens.
+// forms the logits and selects for its 32 tokens. NCG: 8-column groups of
+// the logit columns that hold gate columns (the rest of each staged row is
+// left as it is: it only feeds output columns that are never read).
 constexpr int kGfWaves = 8;
 constexpr int kGfRows = 128;
+// a wave whose slice of d has at most this many 128-row chunks (NCG <= 2)
+// issues all of its loads before its first MFMA
+constexpr int kGfMaxChunks = 4;
 static_assert(kGtTok * kGtCols % (kGfWaves * kWave) == 0, "logit entries per thread");
 
-template <bool NOISY>
+template <bool NOISY, int NCG>
 __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartialParams q, int krw,
                                                                        GateParams p) {
   __shared__ __attribute__((aligned(1024))) char wl[kGfWaves][kGfRows * kGtCols * 2];
@@ -771,8 +776,9 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
     pre_bias[j] = p.logit_bias && ok ? p.logit_bias[c] : 0.f;
   }
   const int kw0 = wave * krw, kw1 = min(kw0 + krw, q.d);
-  constexpr int U = kGfRows / 16;         // 16-K steps per chunk
-  constexpr int G = kGfRows * 4 / kWave;  // 16-byte gate granules per lane per chunk
+  constexpr int U = kGfRows / 16;           // 16-K steps per chunk
+  constexpr int G = kGfRows * NCG / kWave;  // 16-byte gate granules per lane per chunk
+  static_assert(NCG >= 1 && NCG <= kGtCols / 8 && G >= 1, "column groups");
   // one chunk's x fragments and gate rows; an offset past a descriptor's
   // range reads zeros (x past the wave's rows; gate granules of the other
   // matrix, past NC or past the wave's rows), so chunks past the end load
@@ -786,7 +792,7 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const int gi = i * kWave + lane;
-      const int kk = gi >> 2, col = 8 * (gi & 3);
+      const int kk = gi / NCG, col = 8 * (gi % NCG);
       const bool row_ok = kc + kk < kw1;
       const uint32_t row = (uint32_t)(kc + kk) * q.N;
       const uint32_t og = (row_ok && col < q.N) ? (row + col) * 2u : kOutOfRange;
@@ -807,15 +813,38 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
                                                     __builtin_bit_cast(bf16x8, xd[u]), acc, 0, 0, 0);
     }
   };
-  if (q.vec) {
+  // granule i of this lane: its place in the wave's staged rows (row of
+  // 64 bytes, 16-byte column group)
+  auto stage_gate = [&](const u32x4 (&wd)[G]) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int gi = i * kWave + lane;
+      store16(mine + ((gi / NCG) * 4 + gi % NCG) * 16, wd[i]);
+    }
+  };
+  const int nch = (kw1 - kw0 + kGfRows - 1) / kGfRows;  // the wave's chunks (<= 0: none)
+  if (NCG <= 2 && q.vec && nch <= kGfMaxChunks) {
+    // every chunk's x fragments and gate rows requested at once, then
+    // staged and multiplied chunk by chunk (one round trip per wave instead
+    // of one per chunk)
+    u32x4 xa[kGfMaxChunks][U], wa[kGfMaxChunks][G];
+#pragma unroll
+    for (int c = 0; c < kGfMaxChunks; ++c)
+      if (c < nch) load_chunk(kw0 + c * kGfRows, xa[c], wa[c]);
+#pragma unroll
+    for (int c = 0; c < kGfMaxChunks; ++c)
+      if (c < nch) {
+        stage_gate(wa[c]);
+        mfma_chunk(xa[c]);
+      }
+  } else if (q.vec) {
     // steps past the wave's rows meet zero rows and zero x: they add nothing
     u32x4 xv[U], wv[G];
     load_chunk(kw0, xv, wv);
     for (int kc = kw0; kc < kw1; kc += kGfRows) {
       u32x4 xn[U], wn[G];
       load_chunk(kc + kGfRows, xn, wn);  // in flight while this chunk computes
-#pragma unroll
-      for (int i = 0; i < G; ++i) store16(mine + (i * kWave + lane) * 16, wv[i]);
+      stage_gate(wv);
       mfma_chunk(xv);
 #pragma unroll
       for (int u = 0; u < U; ++u) xv[u] = xn[u];
@@ -830,8 +859,8 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
         const int k = kc + 16 * u;
         xv[u] = __builtin_amdgcn_raw_buffer_load_b128(xr, (k + 8 * lhalf < kw1) ? xoff + k * 2 : (int)kOutOfRange, 0, 0);
       }
-      for (int gi = lane; gi < kGfRows * 4; gi += kWave) {
-        const int kk = gi >> 2, col = 8 * (gi & 3);
+      for (int gi = lane; gi < kGfRows * NCG; gi += kWave) {
+        const int kk = gi / NCG, col = 8 * (gi % NCG);
         uint32_t h[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -840,7 +869,7 @@ __global__ __launch_bounds__(kGfWaves * kWave) void gate_fused_kernel(GatePartia
           const bf16* src = c < q.N ? q.wg + k * q.N + c : q.wn + k * q.N + (c - q.N);
           h[e] = (kc + kk < kw1 && c < q.NC) ? (uint32_t)__builtin_bit_cast(uint16_t, *src) : 0u;
         }
-        store16(mine + gi * 16,
+        store16(mine + (kk * 4 + gi % NCG) * 16,
                 u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)});
       }
       mfma_chunk(xv);
@@ -948,10 +977,21 @@ hipError_t launch_gate_bf16(const GateParams& p, bool noisy, hipStream_t s) {
     // one kernel: each wave takes a multiple of 16 of d
     const int krw = ((p.d + kGfWaves - 1) / kGfWaves + 15) / 16 * 16;
     const dim3 grid((p.T + kGtTok - 1) / kGtTok);
-    if (noisy)
-      hipLaunchKernelGGL((gate_fused_kernel<true>), grid, dim3(kGfWaves * kWave), 0, s, g, krw, p);
-    else
-      hipLaunchKernelGGL((gate_fused_kernel<false>), grid, dim3(kGfWaves * kWave), 0, s, g, krw, p);
+    const dim3 block(kGfWaves * kWave);
+    const int ncg = (g.NC + 7) / 8;
+    if (noisy) {
+      if (ncg <= 2)
+        hipLaunchKernelGGL((gate_fused_kernel<true, 2>), grid, block, 0, s, g, krw, p);
+      else
+        hipLaunchKernelGGL((gate_fused_kernel<true, 4>), grid, block, 0, s, g, krw, p);
+    } else {
+      if (ncg <= 1)
+        hipLaunchKernelGGL((gate_fused_kernel<false, 1>), grid, block, 0, s, g, krw, p);
+      else if (ncg <= 2)
+        hipLaunchKernelGGL((gate_fused_kernel<false, 2>), grid, block, 0, s, g, krw, p);
+      else
+        hipLaunchKernelGGL((gate_fused_kernel<false, 4>), grid, block, 0, s, g, krw, p);
+    }
     return hipGetLastError();
   }
   const GateSplit sp = gate_split(p.T, p.d, p.N, noisy);
