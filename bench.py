@@ -688,7 +688,8 @@ def _short(name: str) -> str:
         return "grouped_gemm_kernel<" + m.group(1) + ">"
     m = re.search(r"CfgI(\w+?)EEEEEvNS_10GemmParamsE", name)
     if m:
-        return "grouped_gemm_kernel<" + m.group(1) + ">"
+        # the Cfg's last flag: the dual (pre-activation and GELU) output
+        return "grouped_gemm_kernel<" + m.group(1) + (", U and H" if m.group(1).endswith("Lb1") else "") + ">"
     m = re.search(r"fused_ffn_kernelINS0_3CfgI(\w+?)EEELb([01])ELb([01])EEEvNS0_8FusedFfnE", name)
     if m:
         return ("fused_ffn_kernel<" + m.group(1) + (", combine in launch" if m.group(2) == "1" else "") +
@@ -698,7 +699,7 @@ def _short(name: str) -> str:
         return ("fused_ffn_kernel<" + m.group(1) + (", combine in launch" if m.group(2) == "true" else "") +
                 (", ping-pong" if m.group(3) == "true" else "") + ">")
     # backward GEMMs: tile, operand layouts, epilogue, output type, ragged K
-    lay, epi = {"0": "Kc", "1": "Ks"}, {"0": "plain", "1": "U+H", "2": "dU"}
+    lay, epi = {"0": "Kc", "1": "Ks"}, {"0": "plain", "1": "dU"}
     m = re.search(r"bwd_gemm_kernelILi(\d+)ELNS_9BwdLayoutE(\d)ELS\d+_(\d)ELNS_6BwdEpiE(\d)E(\w+?)Lb(\d)E", name)
     if m:
         ts, a_, b_, e_, o_, rk = m.groups()
