@@ -98,6 +98,11 @@ constexpr int kNumXcds = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 // twice the barriers) outweighs its gain there.
 constexpr int kPingPongMinSteps = 96;
 constexpr int kGroupN = 4;   // n-tiles per run of the tile order
+// Single launch with the ping-pong loop (long contractions): an XCD's
+// GEMM2 tail items come after this many of its GEMM1 full items (two rounds
+// of its 32 CUs, by which time its GEMM1 tail items, first in its queue,
+// have completed).
+constexpr int kTailsAfter = 64;
 // Block-FP8 weights: registers of per-lane block scales a wave holds (64
 // scale blocks each), which bounds K at 128 * 64 * kW8ScaleRegs.
 constexpr int kW8ScaleRegs = kW8MaxK / (128 * 64);
@@ -930,8 +935,9 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p, 
 // the L1 starts each launch empty. (An agent-scope acquire fence after the
 // wait instead, which invalidates the L1, cost 5 % of the FFN on the noisy
 // top-2 layer and 16 % on the cosine layer.) No block waits on a tile that
-// no running block holds: every GEMM1 tile of an XCD is dequeued before any of
-// its GEMM2 tiles, by a block that computes it without waiting. The wait is
+// no running block holds: a row tile's items are all in one XCD's queue, and
+// each of its GEMM1 tiles is dequeued before any of its GEMM2 tiles, by a
+// block that computes it without waiting. The wait is
 // bounded all the same; if it ever expires, the GEMM2 tile is not computed
 // from an incomplete H: its outputs are set to NaN and the launch's status
 // word records the expiry (moe_ffn_status reads it). A block's XCD is read
@@ -1097,7 +1103,26 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
       const int ta = (kNumXcds - 1 - xcc) * Tr / kNumXcds, tb = (kNumXcds - xcc) * Tr / kNumXcds;
       const int nfx = fb - fa, ntx = tb - ta;
       int t = sched[0], kind = 0, tail = 0, NT = 0, c = 0, base = 0;
-      if (t < nfx * NT1) {
+      if constexpr (PINGPONG) {
+        // Long contractions: the XCD's tail items first (GEMM1's, then,
+        // after kTailsAfter GEMM1 full items, GEMM2's), then the rest of its
+        // GEMM1 full items and its GEMM2 full items. GEMM2 full tiles fill
+        // whole rounds of the XCD's CUs; tail tiles taken after them would
+        // leave most CUs idle while they finish.
+        const int P = min(nfx * NT1, kTailsAfter);
+        if (t < ntx * NT1) {
+          kind = 1, tail = 1, NT = NT1, c = ntx, base = ta;
+        } else if ((t -= ntx * NT1) < P) {
+          kind = 1, NT = NT1, c = nfx, base = fa;
+        } else if ((t -= P) < ntx * NT2) {
+          kind = 2, tail = 1, NT = NT2, c = ntx, base = ta;
+        } else if ((t -= ntx * NT2) < nfx * NT1 - P) {
+          kind = 1, NT = NT1, c = nfx, base = fa, t += P;
+        } else if ((t -= nfx * NT1 - P) < nfx * NT2) {
+          kind = 2, NT = NT2, c = nfx, base = fa;
+        }
+      } else if (t < nfx * NT1) {
+        // GEMM1 full items, GEMM1 tail items, GEMM2 full, GEMM2 tail
         kind = 1, NT = NT1, c = nfx, base = fa;
       } else if ((t -= nfx * NT1) < ntx * NT1) {
         kind = 1, tail = 1, NT = NT1, c = ntx, base = ta;
