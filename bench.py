@@ -132,6 +132,10 @@ def main() -> int:
     ap.add_argument("--dispatch-scaling", action="store_true",
                     help="only time moe_dispatch on caller routing at T = 16k .. 256k tokens (N = 64, k = 2) "
                          "and moe_forward's dispatch at the same T (noisy gate, N = 8)")
+    ap.add_argument("--ffn-trace", action="store_true",
+                    help="only run --warmup then --steps moe_forward calls back to back on the trace build "
+                         "(libmoe_gfx950_trace.so) and summarise the single-launch FFN's per-item trace of "
+                         "the last call (per-XCD work and end times, tile times, shader clock)")
     ap.add_argument("--summarize", default=None, help="rocprofv3 results.db to condense (no GPU)")
     ap.add_argument("--kind", choices=["stats", "traffic", "pmc", "gaps", "dispatch"], default="stats")
     ap.add_argument("--pmc-dbs", nargs="*", default=[], help="with --kind pmc: results.db files of counter passes")
@@ -180,6 +184,8 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     if args.graph_ab:
         return graph_ab(dev, torch)
+    if args.ffn_trace:
+        return ffn_trace(args, dev, torch)
     if args.calib_copy_mib > 0:
         # a plain device copy of known size: what FETCH_SIZE / WRITE_SIZE read
         # for it calibrates the counters (the only 1-byte-element copy here)
@@ -532,6 +538,81 @@ def _dispatch_kernels(db):
                        if any(k in c for c in blk))
         out.append(f"T={T}: mean over {len(blk)} calls (us): {kd}")
     return out
+
+
+def ffn_trace(args, dev, torch):
+    """Per-item trace of the single-launch FFN on the trace build: the last of
+    --steps back-to-back moe_forward calls (after --warmup), summarised per XCD
+    and over time. Wall clock: a 100 MHz counter; clock = shader cycles over
+    wall time of each item."""
+    import numpy as np
+    from mixture_experts_sparse_gate_amd import _lib, api
+
+    lib = _lib.load(_lib.TRACE_LIB_PATH)
+    nbytes = int(lib.moe_ffn_trace_bytes())
+    if nbytes == 0:
+        print("the trace build records no trace", file=sys.stderr)
+        return 2
+    spec = dev.spec
+    tensors = dev.layer_tensors(inspect=True)
+    for _ in range(args.warmup + args.steps):
+        api.forward(dev.desc, tensors, dev.ws, lib_path=_lib.TRACE_LIB_PATH)
+    torch.cuda.synchronize()
+    buf = np.zeros(nbytes // 8, dtype=np.uint64)
+    api._check(lib.moe_ffn_trace_read(buf.ctypes.data), "moe_ffn_trace_read", _lib.TRACE_LIB_PATH)
+    rec = buf.reshape(-1, 8).astype(np.int64)
+    rec = rec[rec[:, 2] != 0]
+    if len(rec) == 0:
+        print("no single-launch FFN ran (the layer takes the two grouped-GEMM launches)", file=sys.stderr)
+        return 2
+    launch = rec[:, 5] >> 32
+    rec = rec[launch == launch.max()]
+    t0 = rec[:, 0].min()
+    start, wait_end, end = (rec[:, 0] - t0) / 100.0, (rec[:, 1] - t0) / 100.0, (rec[:, 2] - t0) / 100.0  # us
+    cyc = (rec[:, 4] - rec[:, 3]).astype(np.float64)
+    mhz = cyc / np.maximum(rec[:, 2] - rec[:, 0], 1) * 100.0
+    xcd, kind, tail = rec[:, 5] & 15, (rec[:, 5] >> 4) & 15, (rec[:, 5] >> 8) & 1
+    span = end.max()
+    busy = (end - wait_end).sum()
+    nk = {1: (spec.d + 31) // 32, 2: (spec.h + 31) // 32}
+    lines = [f"command: {args.command}" if args.command else
+             f"command: python3 <repo>/bench.py --workload {spec.name} --ffn-trace --warmup {args.warmup} --steps {args.steps}",
+             "source: moe_ffn_trace_read on libmoe_gfx950_trace.so (MOE_FFN_TRACE), records of the last of "
+             f"{args.warmup + args.steps} back-to-back moe_forward calls",
+             f"workload: {spec.name}",
+             f"items: {len(rec)}; span {span:.1f} us; tile time / (256 CUs x span): {busy / (256 * span):.3f}",
+             "per XCD: end of its last item (us); per kind: items x mean duration after the wait (us) @ mean clock (MHz)"]
+    names = {(1, 0): "GEMM1", (1, 1): "GEMM1 tail", (2, 0): "GEMM2", (2, 1): "GEMM2 tail"}
+    for x in range(8):
+        m = xcd == x
+        if not m.any():
+            continue
+        parts = []
+        for (k_, t_), nm in names.items():
+            q = m & (kind == k_) & (tail == t_)
+            if q.any():
+                parts.append(f"{nm} {q.sum()}x{(end[q] - wait_end[q]).mean():.1f}@{mhz[q].mean():.0f}")
+        lines.append(f"  XCD {x}: end {end[m].max():8.1f} | " + ", ".join(parts))
+    for k_ in (1, 2):
+        q = (kind == k_) & (tail == 0)
+        if q.any():
+            lines.append(f"GEMM{k_} full tiles: {cyc[q].mean():.0f} shader cycles per tile, "
+                         f"{cyc[q].mean() / nk[k_]:.0f} per 32-deep K-step ({nk[k_]} steps, epilogue included; "
+                         f"1024 cycles of MFMA work per step)")
+    lines.append("clock over the launch (items by midpoint):")
+    edges = np.linspace(0, span, 9)
+    mid = (start + end) / 2
+    for a, b in zip(edges[:-1], edges[1:]):
+        q = (mid >= a) & (mid < b) if b < span else (mid >= a)
+        if q.any():
+            lines.append(f"  {a:7.0f}-{b:7.0f} us: {q.sum():4d} items, {mhz[q].mean():.0f} MHz, "
+                         f"GEMM1 {(q & (kind == 1)).sum()}, GEMM2 {(q & (kind == 2)).sum()}")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
 
 
 def graph_ab(dev, torch):

@@ -417,6 +417,23 @@ MOE_API moe_status_t moe_backward(const moe_desc_t* desc, const moe_backward_ten
  * layers. Always returns MOE_OK. */
 MOE_API moe_status_t moe_time_ffn_launches(void* start_event, void* stop_event);
 
+/* Per-item trace of the single-launch expert FFN, a measurement aid of the
+ * trace build (libmoe_gfx950_trace.so, compiled with MOE_FFN_TRACE; the
+ * release and debug builds record nothing). Each block of that launch writes
+ * one record per work item it runs (its first 64 items), overwriting those
+ * of earlier launches: 8 uint64 per record, block b's item i at record
+ * b * 64 + i, for 256 blocks: [0] wall clock (100 MHz counter) when the item
+ * starts, [1] after a GEMM2 item's wait for its rows of H, [2] when it ends;
+ * [3], [4] the shader cycle counter at its start and end (cycles over wall
+ * time give the clock it ran at); [5] XCD | kind << 4 (1: GEMM1, 2: GEMM2)
+ * | tail tile << 8 | launch number << 32 (1, 2, ... per process); [6] the
+ * row tile; [7] the first output column. Unwritten records are zero.
+ * moe_ffn_trace_bytes: the size of the record array (0 in other builds).
+ * moe_ffn_trace_read: copies it to host memory of that size, synchronously
+ * (after the device's work so far); MOE_ERR_UNSUPPORTED in other builds. */
+MOE_API size_t moe_ffn_trace_bytes(void);
+MOE_API moe_status_t moe_ffn_trace_read(void* host);
+
 /* Measurement aids, to judge the layer's kernels against the chip's measured
  * ceilings as well as its published ones (run in the same process, timed by
  * the caller with events around the call).

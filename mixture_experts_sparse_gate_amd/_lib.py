@@ -9,6 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_gfx950.so")
 # the same library with the debug checks of caller routing (MOE_DEBUG_CHECKS)
 DEBUG_LIB_PATH = os.path.join(HERE, "libmoe_gfx950_debug.so")
+# the same library recording a per-item trace of the single-launch FFN (MOE_FFN_TRACE)
+TRACE_LIB_PATH = os.path.join(HERE, "libmoe_gfx950_trace.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
@@ -76,6 +78,8 @@ SIGNATURES = {
                                 c_size_t, c_void_p]),
     "moe_aux_loss": (c_int, [POINTER(MoeDesc), c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                              c_void_p]),
+    "moe_ffn_trace_bytes": (c_size_t, []),
+    "moe_ffn_trace_read": (c_int, [c_void_p]),
     "moe_status_string": (c_char_p, [c_int]),
     "moe_last_error": (c_char_p, []),
     "moe_version": (c_char_p, []),

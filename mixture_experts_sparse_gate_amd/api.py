@@ -152,15 +152,16 @@ def combine(desc, y_perm, row_of, topk_w, y, stream=None):
     _check(st, "moe_combine")
 
 
-def forward(desc, tensors: dict, ws: torch.Tensor, stream=None):
-    """tensors: the fields of moe_layer_tensors_t by name (missing = NULL)."""
+def forward(desc, tensors: dict, ws: torch.Tensor, stream=None, lib_path=_lib.LIB_PATH):
+    """tensors: the fields of moe_layer_tensors_t by name (missing = NULL).
+    lib_path=_lib.TRACE_LIB_PATH calls the trace build."""
     unknown = set(tensors) - {f for f, _ in MoeLayerTensors._fields_}
     if unknown:
         raise KeyError(f"unknown tensor names {sorted(unknown)}")
     lt = MoeLayerTensors(**{k: _ptr(v) for k, v in tensors.items() if v is not None})
-    st = _lib.load().moe_forward(ctypes.byref(desc), ctypes.byref(lt), _ptr(ws),
-                                 ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "moe_forward")
+    st = _lib.load(lib_path).moe_forward(ctypes.byref(desc), ctypes.byref(lt), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "moe_forward", lib_path)
 
 
 def backward(desc, tensors: dict, ws: torch.Tensor, aux_coef=None, stream=None):

@@ -3,10 +3,12 @@
     python -m mixture_experts_sparse_gate_amd.build [-j JOBS]
 
 Objects go to <repo>/_build/ and the libraries next to this file:
-libmoe_gfx950.so, and libmoe_gfx950_debug.so, the same library with the
+libmoe_gfx950.so; libmoe_gfx950_debug.so, the same library with the
 debug checks of caller-supplied routing (-DMOE_DEBUG_CHECKS: moe_dispatch
 copies topk_idx to the host and rejects indices outside [0, N) or repeated
-within a token). Every call recompiles, so a call always checks that the
+within a token); and libmoe_gfx950_trace.so, the same library whose
+single-launch FFN records a per-item trace (-DMOE_FFN_TRACE, read with
+moe_ffn_trace_read). Every call recompiles, so a call always checks that the
 current sources compile.
 """
 from __future__ import annotations
@@ -32,6 +34,10 @@ SOURCES = ["gate.hip", "dispatch.hip", "gemm.hip", "combine.hip", "aux.hip", "qu
 HOST_SOURCES = ["routing_check.cpp"]
 DEBUG_LIB_NAME = "libmoe_gfx950_debug.so"
 DEBUG_LIB_PATH = os.path.join(HERE, DEBUG_LIB_NAME)
+TRACE_LIB_NAME = "libmoe_gfx950_trace.so"
+TRACE_LIB_PATH = os.path.join(HERE, TRACE_LIB_NAME)
+# sources compiled again for the trace build (MOE_FFN_TRACE)
+TRACE_SOURCES = ["gemm.hip", "capi.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -52,14 +58,14 @@ HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-fvisibility=hidden"]
 
 
 def _compile(job) -> str:
-    src, debug = job if isinstance(job, tuple) else (job, False)
-    stem = os.path.splitext(src)[0] + ("_debug" if debug else "")
+    src, variant = job if isinstance(job, tuple) else (job, "")
+    stem = os.path.splitext(src)[0] + (f"_{variant}" if variant else "")
     obj = os.path.join(BUILD_DIR, stem + ".o")
+    defines = {"": [], "debug": ["-DMOE_DEBUG_CHECKS"], "trace": ["-DMOE_FFN_TRACE"]}[variant]
     if src.endswith(".cpp"):
         cmd = ["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     else:
-        cmd = [hipcc(), *HIP_FLAGS, *(["-DMOE_DEBUG_CHECKS"] if debug else []), "-c", os.path.join(CSRC, src),
-               "-o", obj]
+        cmd = [hipcc(), *HIP_FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
@@ -81,16 +87,22 @@ def _link(objs, path: str) -> None:
 
 def build(jobs: int = 0, verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs_list = SOURCES + HOST_SOURCES + [("capi.hip", True)]
+    jobs_list = SOURCES + HOST_SOURCES + [("capi.hip", "debug")] + [(src, "trace") for src in TRACE_SOURCES]
     jobs = jobs or min(len(jobs_list), max(1, os.cpu_count() or 1), 16)
     with ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, jobs_list))
-    release = objs[:len(SOURCES) + len(HOST_SOURCES)]
-    debug = [o for o in release if not o.endswith(os.sep + "capi.o")] + [objs[-1]]
+    nrel = len(SOURCES) + len(HOST_SOURCES)
+    release = objs[:nrel]
+    debug_capi, trace_objs = objs[nrel], objs[nrel + 1:]
+
+    def without(names):
+        return [o for o in release if os.path.basename(o) not in names]
+
+    _link(without({"capi.o"}) + [debug_capi], DEBUG_LIB_PATH)
+    _link(without({os.path.splitext(s)[0] + ".o" for s in TRACE_SOURCES}) + trace_objs, TRACE_LIB_PATH)
     _link(release, LIB_PATH)
-    _link(debug, DEBUG_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH} and {DEBUG_LIB_NAME}")
+        print(f"built {LIB_PATH}, {DEBUG_LIB_NAME} and {TRACE_LIB_NAME}")
     return LIB_PATH
 
 

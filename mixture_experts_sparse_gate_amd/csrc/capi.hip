@@ -1022,6 +1022,15 @@ moe_status_t moe_time_ffn_launches(void* start_event, void* stop_event) {
   return MOE_OK;
 }
 
+size_t moe_ffn_trace_bytes(void) { return moe::ffn_trace_bytes(); }
+
+moe_status_t moe_ffn_trace_read(void* host) {
+  if (!host) return fail(MOE_ERR_INVALID, "moe_ffn_trace_read: host is NULL");
+  if (moe::ffn_trace_bytes() == 0)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_ffn_trace_read: this build records no trace (MOE_FFN_TRACE)");
+  return hip_status(moe::ffn_trace_copy(host), "moe_ffn_trace_read");
+}
+
 const char* moe_status_string(moe_status_t st) {
   switch (st) {
     case MOE_OK: return "MOE_OK";

@@ -42,6 +42,10 @@
 namespace moe {
 namespace {
 
+#ifdef MOE_FFN_TRACE
+__device__ uint64_t g_ffn_trace[kFfnTraceBlocks * kFfnTraceItems * kFfnTraceWords];
+#endif
+
 template <typename E> struct Mfma;
 template <> struct Mfma<bf16> {
   // one 32x32x16 MFMA per pair of chunks
@@ -950,6 +954,9 @@ struct FusedFfn {
   // ready[row tiles]: zero at launch
   int32_t* counters;
   FusedCombine comb;  // the folded combine (fused_ffn_kernel<C, true>)
+#ifdef MOE_FFN_TRACE
+  uint32_t trace_launch;  // launch number written into the trace records
+#endif
 };
 
 // The combine of the tokens a GEMM2 tile completed (fin[0, nfin)), on the
@@ -1080,6 +1087,9 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
   // tile's epilogue runs (its result is stored to sched[0] after it)
   if (tid == 0)
     sched[0] = __hip_atomic_fetch_add(f.counters + xcc, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#ifdef MOE_FFN_TRACE
+  int tr_n = 0;
+#endif
   for (;;) {
     // Everything below reads the arguments through fp, re-read for each
     // tile: the empty asm hides that fp never changes, so that the compiler
@@ -1184,6 +1194,9 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
     const int n0 = __builtin_amdgcn_readfirstlane(sched[5]);
     const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[6]) != 0;
     const int rid = __builtin_amdgcn_readfirstlane(sched[7]);
+#ifdef MOE_FFN_TRACE
+    const uint64_t tr_t0 = __builtin_amdgcn_s_memrealtime(), tr_c0 = __builtin_readcyclecounter();
+#endif
     int expired = 0;
     if (kind == 2) {
       if (tid == 0) {
@@ -1199,6 +1212,9 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
       __syncthreads();
       expired = __builtin_amdgcn_readfirstlane(sched[8]);
     }
+#ifdef MOE_FFN_TRACE
+    const uint64_t tr_tw = __builtin_amdgcn_s_memrealtime();
+#endif
     int next = 0;
     if (expired) {
       // H of these rows may be incomplete: the tile's outputs become NaN
@@ -1267,6 +1283,20 @@ __global__ __launch_bounds__(C::THREADS) void fused_ffn_kernel(FusedFfn f) {
         else combine_finished<8, NW>(row_of, tw, y, k, yp, ldc, Nc, n0, fin, n, wave, lane);
       }
     }
+#ifdef MOE_FFN_TRACE
+    if (tid == 0 && tr_n < kFfnTraceItems && (int)blockIdx.x < kFfnTraceBlocks) {
+      uint64_t* r = g_ffn_trace + ((size_t)blockIdx.x * kFfnTraceItems + tr_n) * kFfnTraceWords;
+      r[0] = tr_t0;
+      r[1] = tr_tw;
+      r[2] = __builtin_amdgcn_s_memrealtime();
+      r[3] = tr_c0;
+      r[4] = __builtin_readcyclecounter();
+      r[5] = (uint64_t)xcc | ((uint64_t)kind << 4) | ((uint64_t)tail_tile << 8) | ((uint64_t)fp->trace_launch << 32);
+      r[6] = (uint64_t)rid;
+      r[7] = (uint64_t)n0;
+    }
+    ++tr_n;
+#endif
     if (tid == 0) sched[0] = next;
   }
 }
@@ -1364,6 +1394,14 @@ bool fused_ffn_fits(const GemmParams& g1, const GemmParams& g2, bool bf16_, int 
 
 int fused_combine_col_tiles(int d) { return (d + FusedCfg::BN - 1) / FusedCfg::BN; }
 
+#ifdef MOE_FFN_TRACE
+size_t ffn_trace_bytes() { return sizeof(g_ffn_trace); }
+hipError_t ffn_trace_copy(void* host) { return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_ffn_trace), sizeof(g_ffn_trace)); }
+#else
+size_t ffn_trace_bytes() { return 0; }
+hipError_t ffn_trace_copy(void*) { return hipErrorNotSupported; }
+#endif
+
 hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t* counters, bool clear,
                             hipStream_t s, LaunchEvents ev, const FusedCombine* comb) {
   if (clear) {
@@ -1372,6 +1410,10 @@ hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t*
   }
   if (comb && comb->k > kFusedCombineMaxK) return hipErrorInvalidValue;
   FusedFfn f{g1, g2, counters, comb ? *comb : FusedCombine{}};
+#ifdef MOE_FFN_TRACE
+  static uint32_t launches = 0;
+  f.trace_launch = ++launches;
+#endif
   // one block per CU (a multiple of the XCD count)
   auto launch = [&](auto kernel) {
     if (ev.start || ev.stop)

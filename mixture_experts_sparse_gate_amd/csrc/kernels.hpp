@@ -156,6 +156,15 @@ hipError_t launch_fused_ffn(const GemmParams& g1, const GemmParams& g2, int32_t*
 // (bit 0: a GEMM2 tile's wait for its rows of H expired and its outputs were
 // set to NaN); counters null: *out = 0
 hipError_t launch_ffn_status(const int32_t* counters, int32_t* out, hipStream_t s);
+// Per-item trace of the single-launch FFN (measurement build, MOE_FFN_TRACE):
+// block b's i-th item (i < kFfnTraceItems) writes record b * kFfnTraceItems + i
+// of kFfnTraceWords uint64: wall clock (100 MHz) at the item's start, after
+// its wait for H and at its end; shader cycle counter at its start and end;
+// XCD | kind << 4 | tail << 8 | launch number << 32; row tile; first column.
+// ffn_trace_bytes() is 0 and ffn_trace_copy() fails in other builds.
+constexpr int kFfnTraceItems = 64, kFfnTraceWords = 8, kFfnTraceBlocks = 256;
+size_t ffn_trace_bytes();
+hipError_t ffn_trace_copy(void* host);
 
 // ---- backward pass (backward.hip), bf16 layers
 typedef __bf16 bf16;

@@ -48,6 +48,18 @@ def test_every_declared_symbol_is_exported(lib):
     assert sorted(_lib.SIGNATURES) == declared_functions()
 
 
+def test_trace_calls_only_in_the_trace_build(lib):
+    # the release build records no FFN trace; the trace build holds 256 blocks
+    # x 64 records x 8 uint64 (host-side calls only: nothing reaches the GPU)
+    assert lib.moe_ffn_trace_bytes() == 0
+    buf = (ctypes.c_uint64 * 8)()
+    assert lib.moe_ffn_trace_read(ctypes.cast(buf, ctypes.c_void_p)) == _lib.MOE_ERR_UNSUPPORTED
+    assert lib.moe_ffn_trace_read(None) == _lib.MOE_ERR_INVALID
+    tr = _lib.load(_lib.TRACE_LIB_PATH)
+    assert tr.moe_ffn_trace_bytes() == 256 * 64 * 8 * 8
+    assert sorted(n for n in declared_functions() if not hasattr(tr, n)) == []
+
+
 def test_struct_layout_matches_header(lib):
     # T(8) d h N k(16) cf(8) gate renorm dtype proj_dim(16) inv_temp flags(8) = 56 bytes
     assert ctypes.sizeof(_lib.MoeDesc) == 56

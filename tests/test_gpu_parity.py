@@ -524,6 +524,43 @@ def test_ffn_launch_events(name):
     assert torch.equal(dev.y, y_ref)
 
 
+@pytest.mark.parametrize("name", ["noisy_top2_bf16", "zipf16_pingpong"])
+def test_ffn_trace_build(name):
+    """The trace build (libmoe_gfx950_trace.so) gives the release build's y
+    bit for bit and records every item of the single launch once: as many
+    GEMM1 and GEMM2 items as full and tail row tiles times column tiles, each
+    ending after it starts, on XCDs 0-7."""
+    spec = W[name] if name in W else FUSED[name]
+    inp = make_inputs(spec, workloads.WORKLOAD_SEED.get(name, 11))
+    dev = api.DeviceLayer(inp)
+    dev.run_forward(inspect=True)
+    torch.cuda.synchronize()
+    y_ref = dev.y.clone()
+    lib = _lib.load(_lib.TRACE_LIB_PATH)
+    nbytes = int(lib.moe_ffn_trace_bytes())
+    assert nbytes > 0 and int(_lib.load().moe_ffn_trace_bytes()) == 0
+    say(f"[case] FFN trace build {name}")
+    for _ in range(2):
+        dev.y.fill_(float("nan"))
+        api.forward(dev.desc, dev.layer_tensors(inspect=True), dev.ws, lib_path=_lib.TRACE_LIB_PATH)
+        torch.cuda.synchronize()
+        assert torch.equal(dev.y, y_ref)
+    buf = np.zeros(nbytes // 8, dtype=np.uint64)
+    assert lib.moe_ffn_trace_read(buf.ctypes.data) == _lib.MOE_OK
+    rec = buf.reshape(-1, 8).astype(np.int64)
+    rec = rec[rec[:, 2] != 0]
+    rec = rec[(rec[:, 5] >> 32) == (rec[:, 5] >> 32).max()]
+    kept = np.diff(host(dev.expert_off))
+    rem = kept % 256
+    small = (rem > 0) & (rem <= 128)
+    row_tiles = int((kept // 256 + ((rem > 0) & ~small)).sum() + np.where(small, (rem + 63) // 64, 0).sum())
+    nt1, nt2 = (spec.h + 255) // 256, (spec.d + 255) // 256
+    kind = (rec[:, 5] >> 4) & 15
+    assert (kind == 1).sum() == row_tiles * nt1 and (kind == 2).sum() == row_tiles * nt2
+    assert ((rec[:, 5] & 15) < 8).all() and (rec[:, 2] >= rec[:, 1]).all() and (rec[:, 1] >= rec[:, 0]).all()
+    assert (rec[:, 4] > rec[:, 3]).all()
+
+
 def _aux(dev, spec, importance=True, losses=True):
     imp = torch.full((spec.N,), -1.0, dtype=torch.float32, device="cuda") if importance else None
     los = torch.full((2,), -1.0, dtype=torch.float32, device="cuda") if losses else None
