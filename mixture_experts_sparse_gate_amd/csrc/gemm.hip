@@ -9,10 +9,13 @@
 // ("MoE稀疏计算加速技术解析与应用实践" §3.2).
 //
 // Design for gfx950:
-//  - The block computes a BM x BN tile of C. MFMA 32x32x16 is used in the
-//    transposed sense, D = B^T A^T: the weight tile is the MFMA's first
-//    operand and the activation rows its second, so each lane ends up with
-//    4 consecutive output columns of one row (8- or 16-byte stores).
+//  - The block computes a BM x BN tile of C. MFMA 16x16x32 (bf16 tiles with
+//    32-deep K-steps) or 32x32x16 (the others) is used in the transposed
+//    sense, D = B^T A^T: the weight tile is the MFMA's first operand and the
+//    activation rows its second, so each lane ends up with 4 consecutive
+//    output columns of one row (8- or 16-byte stores). Both shapes do the
+//    same flops per cycle; 16x16x32 spends less energy per flop, and the
+//    chip, held at its power cap by this loop, clocks higher with it.
 //  - Both tiles go global -> LDS with buffer_load_dwordx4 ... lds (no staging
 //    registers), as they lie in memory: activation rows K-contiguous, weight
 //    rows N-contiguous. The MFMA needs 8 consecutive K values of one weight
@@ -152,6 +155,11 @@ struct Cfg {
   // multiply a quarter (BM = 256) of a full tile's activation rows.
   static constexpr int TBM = 32 * WM;
   static constexpr bool HAS_TAIL = AP == 2 && TBM < BM;
+  // bf16 activations and weights with 32-deep K-steps: 16x16x32 MFMAs (the
+  // same flops per cycle as 32x32x16, at less energy per flop, so that the
+  // chip clocks higher under its power cap); otherwise 32x32x16 (32x32x2 for
+  // fp32)
+  static constexpr bool M16 = std::is_same_v<E, bf16> && !W8_ && KC_ == 4;
   static constexpr int A_INST_T = HAS_TAIL ? TBM * KCA / THREADS : A_INST;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(KC == 4 || KC == 8, "activation rows of 4 or 8 chunks");
@@ -162,6 +170,7 @@ struct Cfg {
   static_assert(S >= 2 && S <= 4 && LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS * (S - 2) < 64 && A_INST + 2 * B_INST < 64, "vmcnt range");
   static_assert(!HAS_TAIL || (TBM * KCA % THREADS == 0 && A_INST_T >= 1), "tail tiles: whole loads per thread");
+  static_assert(!M16 || (KCA == 8 && B_CPR >= 16), "16x16x32 fragments: paired 128-byte activation rows");
 };
 
 // Chunk swizzles, for gfx950's LDS as measured with bank-conflict counters:
@@ -189,6 +198,28 @@ template <int ES> __device__ inline int swz_b(int k) {
 // for 8-byte pieces (the minimum for 16 distinct bank pairs) and one per
 // 16 lanes for 16-byte pieces.
 template <int OB> __device__ inline int swz_c(int r) { return OB == 2 ? ((r >> 1) & 7) : (r & 15); }
+// 16x16x32 fragments (C::M16) read other rows together: lane l of an
+// activation read takes row l % 16 of a 16-row block, chunk l / 16, so a
+// pass of 16 lanes ({0-3, 12-15, 20-23, 24-27} and the like) reads rows
+// 0-3 and 12-15 of one chunk and rows 4-7 and 8-11 of the next; with
+// 2 ((r / 2) % 4) each row parity's eight reads land in eight distinct
+// chunk slots. A weight read takes K-rows 8q .. 8q + 3 (lane group q) of the
+// same 16 columns in all four groups, so rows 8 apart get the chunk slots
+// the plain swizzle leaves free (^ 8).
+template <class C> __device__ inline int swz_act(int r) {
+  if constexpr (C::M16) return 2 * ((r >> 1) & 3);
+  else return swz_a<C::KCA>(r);
+}
+template <class C> __device__ inline int swz_wt(int k) {
+  if constexpr (C::M16) return swz_b<2>(k) ^ (8 * ((k >> 3) & 1));
+  else return swz_b<C::ES>(k);
+}
+// acc (one 16x16 sub-block of outputs) += weight fragment wf x activation
+// fragment af
+__device__ inline void mfma16(f32x4& acc, const u32x4& wf, const u32x4& af) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf), __builtin_bit_cast(bf16x8, af), acc, 0,
+                                                0, 0);
+}
 
 // 4 floats as O into LDS: 8 bytes (bf16) or 16 bytes (fp32)
 template <typename O> struct Pack;
@@ -266,7 +297,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 #pragma unroll
   for (int i = 0; i < C::A_INST; ++i) {
     const int slot = i * C::THREADS + tid;
-    const int r = slot / KCA, c = (slot % KCA) ^ swz_a<KCA>(r);
+    const int r = slot / KCA, c = (slot % KCA) ^ swz_act<C>(r);
     if (p.gather) {
       // rows past the group read zeros: an offset past the descriptor's range
       const int grow = row_lo + r;
@@ -283,7 +314,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       // reads of one pass cover 256 contiguous bytes: no swizzle needed)
       b_off[i] = (slot / C::B_CPR) * Ncols * 8 + (slot % C::B_CPR) * 16;
     } else {
-      const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_b<ES>(k);
+      const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_wt<C>(k);
       b_off[i] = (k * Ncols + c * CE) * ES;
     }
   }
@@ -323,12 +354,25 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     };
 
     f32x16 acc[C::FN][FM];
+    if constexpr (!C::M16) {
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i)
+      for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-      for (int j = 0; j < FM; ++j)
+        for (int j = 0; j < FM; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    }
+    // M16: the K loop's accumulators, 16x16 sub-block Q = 2a + b of each
+    // 32x32 block (copied into acc[.][.][4Q .. 4Q+3] after the loop)
+    f32x4 acq[C::M16 ? C::FN : 1][C::M16 ? FM : 1][4];
+    if constexpr (C::M16) {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acq[i][j][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     // W8: acc holds the current 128-deep block of K; acc8 the scaled total
     f32x16 acc8[C::W8 ? C::FN : 1][C::W8 ? FM : 1];
     // W8: the wave's block scales (one per 128-deep block of K: its columns
@@ -364,7 +408,26 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     int fa_off[KC / 2];
 #pragma unroll
     for (int ss = 0; ss < KC / 2; ++ss)
-      fa_off[ss] = (wm * WTM + lrow) * KCA * 16 + (((2 * ss + lhalf) ^ swz_a<KCA>(lrow)) * 16);
+      fa_off[ss] = (wm * WTM + lrow) * KCA * 16 + (((2 * ss + lhalf) ^ swz_act<C>(lrow)) * 16);
+    // 16x16x32 (M16): the activation fragment of m-half b of 32-row block j
+    // is row wm*WTM + 32j + 16b + lane%16, chunk lane/16 (8 consecutive K),
+    // at fa16 + (32j + 16b) rows; the weight fragment of n-half a of 32-column
+    // block i is column wn*WTN + 32i + 16a + lane%16, K-rows 8(lane/16) + 0..7,
+    // two transposing reads of 4 K-rows each from fw16[i][a] (in each 16-lane
+    // group, lane 4q + r reads K-row q, columns 4r .. 4r+3 of the group's 16)
+    const int l16 = lane & 15, g16 = lane >> 4;
+    const int fa16 = (wm * WTM + l16) * KCA * 16 + ((g16 ^ swz_act<C>(l16)) * 16);
+    int fw16[C::M16 ? C::FN : 1][2];
+    if constexpr (C::M16) {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+          const int k = 8 * g16 + (l16 >> 2);
+          const int chunk = wn * C::WTN / 8 + 4 * i + 2 * a + ((l16 & 3) >> 1);
+          fw16[i][a] = k * C::B_CPR * 16 + ((chunk ^ swz_wt<C>(k)) * 16) + 8 * (l16 & 1);
+        }
+    }
     // weight fragment, bf16: 16-lane group q, lane r in it: rows 16s + 8(q/2) + 4p + r/4,
     // columns wn*WTN + 32i + 16(q%2) + 4(r%4) .. +3; the row's swizzle depends on r/4 only
     const int q16 = lane >> 4, r16 = lane & 15;
@@ -382,6 +445,22 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 
     u32x4 fa[2][C::FN], fb[2][FM];
     auto load_frags = [&](const char* sa, const char* sb, int ss, int buf, int hi) {
+      if constexpr (C::M16) {
+        // half ss of the K-step's fragments: m-half ss of every row block,
+        // n-half ss of every column block
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+          fb[buf][j] = *(lds_u32x4*)(sa + (fa16 ^ hi) + (j * 32 + 16 * ss) * KCA * 16);
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) {
+          const char* w = sb + fw16[i][ss];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)w);
+          const i16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(w + 4 * C::B_CPR * 16));
+          const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, up);
+          fa[buf][i] = u32x4{x[0], x[1], y[0], y[1]};
+        }
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < FM; ++j)
         fb[buf][j] = *(lds_u32x4*)(sa + (fa_off[ss] ^ hi) + j * 32 * KCA * 16);
@@ -415,7 +494,33 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
             fa[buf][i][e] = *(lds_u32*)(sb + fw32[e] + (8 * ss) * C::B_CPR * 16 + i * 128);
       }
     };
+    // M16: the K-step's 4 FN FM MFMAs once both halves are in registers;
+    // the first quarter needs only half 0
+    auto mma16 = [&]() {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) mfma16(acq[i][j][0], fa[0][i], fb[0][j]);
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) mfma16(acq[i][j][1], fa[0][i], fb[1][j]);
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) mfma16(acq[i][j][2], fa[1][i], fb[0][j]);
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) mfma16(acq[i][j][3], fa[1][i], fb[1][j]);
+    };
     auto compute = [&](const char* sa, const char* sb, int hi) {
+      if constexpr (C::M16) {
+        load_frags(sa, sb, 0, 0, hi);
+        load_frags(sa, sb, 1, 1, hi);
+        mma16();
+        return;
+      }
       load_frags(sa, sb, 0, 0, hi);
 #pragma unroll
       for (int ss = 0; ss < KC / 2; ++ss) {
@@ -493,7 +598,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
               }
         }
       }
-      if constexpr (ES == 2 && C::THREADS == 512) {
+      // (M16 takes the compiler's order: with these hints its fragments of
+      // both halves stayed live across the step and spilled)
+      if constexpr (ES == 2 && C::THREADS == 512 && !C::M16) {
         // (8-wave tiles) instruction order for the step: the first substep's LDS reads, then
         // each MFMA followed by one of the next substep's LDS reads and, after
         // every second MFMA, one of the step's global->LDS loads, so that the
@@ -564,12 +671,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         __builtin_amdgcn_sched_barrier(0);
       };
       auto mma = [&]() {
+        if constexpr (C::M16) {
+          mma16();
+        } else {
 #pragma unroll
-        for (int ss = 0; ss < 2; ++ss)
+          for (int ss = 0; ss < 2; ++ss)
 #pragma unroll
-          for (int i = 0; i < C::FN; ++i)
+            for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-            for (int j = 0; j < FM; ++j) Mfma<E>::step(acc[i][j], fa[ss][i], fb[ss][j]);
+              for (int j = 0; j < FM; ++j) Mfma<E>::step(acc[i][j], fa[ss][i], fb[ss][j]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       };
       // waits before the barrier ahead of group 0's mem(t)
@@ -638,6 +749,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = acc8[i][j];
     }
+    if constexpr (C::M16) {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = acq[i][j][q][r];
+    }
     wait_vmcnt<0>();
     at_k_end();
 
@@ -655,7 +776,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int off = (ccol0 + i * 32 + 8 * q + 4 * lhalf) * ES;
+          // M16: the lane's columns are 32i + 16q + 4(lane/16) .. +3 (q < 2)
+          if (C::M16 && q >= 2) continue;
+          const int off = (ccol0 + i * 32 + (C::M16 ? 16 * q + 4 * g16 : 8 * q + 4 * lhalf)) * ES;
           if constexpr (ES == 2) {
             const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
             bv[i][q] = u32x4{w[0], w[1], 0u, 0u};
@@ -703,11 +826,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         for (int i = 0; i < C::FN; ++i) {
   #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int cb = (i * 32 + 8 * q + 4 * lhalf) * OB;  // byte offset in the slice row
+            // slice row and byte offset in it of acc[i][j][4q .. 4q+3]: M32
+            // row lane%32, columns 32i + 8q + 4(lane/32); M16 (sub-block q =
+            // 2a + b) row 16b + lane%16, columns 32i + 16a + 4(lane/16)
+            const int srow = C::M16 ? 16 * (q & 1) + l16 : lrow;
+            const int cb = (i * 32 + (C::M16 ? 16 * (q >> 1) + 4 * g16 : 8 * q + 4 * lhalf)) * OB;
             float v[4];
   #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-            Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
+            Pack<O>::four_lds(reg + srow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(srow)) * 16) + cb % 16, v);
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -743,7 +870,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
   #pragma unroll
             for (int q = 0; q < 4; ++q)
   #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][q], r);
+              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][C::M16 ? q >> 1 : q], r);
         }
         store_slice(static_cast<O*>(p.C2), j, frow);  // the pre-activation
         if (gelu) {
@@ -768,7 +895,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
   #pragma unroll
             for (int q = 0; q < 4; ++q)
   #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][q], r);
+              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][C::M16 ? q >> 1 : q], r);
         }
         if (gelu) {
   #pragma unroll
@@ -781,11 +908,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         for (int i = 0; i < C::FN; ++i) {
   #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int cb = (i * 32 + 8 * q + 4 * lhalf) * OB;  // byte offset in the slice row
+            // slice row and byte offset in it of acc[i][j][4q .. 4q+3]: M32
+            // row lane%32, columns 32i + 8q + 4(lane/32); M16 (sub-block q =
+            // 2a + b) row 16b + lane%16, columns 32i + 16a + 4(lane/16)
+            const int srow = C::M16 ? 16 * (q & 1) + l16 : lrow;
+            const int cb = (i * 32 + (C::M16 ? 16 * (q >> 1) + 4 * g16 : 8 * q + 4 * lhalf)) * OB;
             float v[4];
   #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
-            Pack<O>::four_lds(reg + lrow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(lrow)) * 16) + cb % 16, v);
+            Pack<O>::four_lds(reg + srow * CPR * 16 + (((cb / 16) ^ swz_c<OB>(srow)) * 16) + cb % 16, v);
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
