@@ -155,11 +155,11 @@ struct Cfg {
   // multiply a quarter (BM = 256) of a full tile's activation rows.
   static constexpr int TBM = 32 * WM;
   static constexpr bool HAS_TAIL = AP == 2 && TBM < BM;
-  // bf16 activations and weights with 32-deep K-steps: 16x16x32 MFMAs (the
-  // same flops per cycle as 32x32x16, at less energy per flop, so that the
-  // chip clocks higher under its power cap); otherwise 32x32x16 (32x32x2 for
-  // fp32)
-  static constexpr bool M16 = std::is_same_v<E, bf16> && !W8_ && KC_ == 4;
+  // bf16 activations and weights with 32-deep K-steps: the ping-pong K loop
+  // takes 16x16x32 MFMAs (the same flops per cycle as 32x32x16, at less
+  // energy per flop, so that the chip clocks higher under its power cap);
+  // every other loop 32x32x16 (32x32x2 for fp32). Both give the same bits.
+  static constexpr bool M16_OK = std::is_same_v<E, bf16> && !W8_ && KC_ == 4;
   static constexpr int A_INST_T = HAS_TAIL ? TBM * KCA / THREADS : A_INST;
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold at least one 32x32 MFMA tile");
   static_assert(KC == 4 || KC == 8, "activation rows of 4 or 8 chunks");
@@ -170,7 +170,7 @@ struct Cfg {
   static_assert(S >= 2 && S <= 4 && LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(LOADS * (S - 2) < 64 && A_INST + 2 * B_INST < 64, "vmcnt range");
   static_assert(!HAS_TAIL || (TBM * KCA % THREADS == 0 && A_INST_T >= 1), "tail tiles: whole loads per thread");
-  static_assert(!M16 || (KCA == 8 && B_CPR >= 16), "16x16x32 fragments: paired 128-byte activation rows");
+  static_assert(!M16_OK || (KCA == 8 && B_CPR >= 16), "16x16x32 fragments: paired 128-byte activation rows");
 };
 
 // Chunk swizzles, for gfx950's LDS as measured with bank-conflict counters:
@@ -198,7 +198,7 @@ template <int ES> __device__ inline int swz_b(int k) {
 // for 8-byte pieces (the minimum for 16 distinct bank pairs) and one per
 // 16 lanes for 16-byte pieces.
 template <int OB> __device__ inline int swz_c(int r) { return OB == 2 ? ((r >> 1) & 7) : (r & 15); }
-// 16x16x32 fragments (C::M16) read other rows together: lane l of an
+// 16x16x32 fragments (M16) read other rows together: lane l of an
 // activation read takes row l % 16 of a 16-row block, chunk l / 16, so a
 // pass of 16 lanes ({0-3, 12-15, 20-23, 24-27} and the like) reads rows
 // 0-3 and 12-15 of one chunk and rows 4-7 and 8-11 of the next; with
@@ -206,13 +206,13 @@ template <int OB> __device__ inline int swz_c(int r) { return OB == 2 ? ((r >> 1
 // chunk slots. A weight read takes K-rows 8q .. 8q + 3 (lane group q) of the
 // same 16 columns in all four groups, so rows 8 apart get the chunk slots
 // the plain swizzle leaves free (^ 8).
-template <class C> __device__ inline int swz_act(int r) {
-  if constexpr (C::M16) return 2 * ((r >> 1) & 3);
-  else return swz_a<C::KCA>(r);
+template <int KCA, bool M16> __device__ inline int swz_act(int r) {
+  if constexpr (M16) return 2 * ((r >> 1) & 3);
+  else return swz_a<KCA>(r);
 }
-template <class C> __device__ inline int swz_wt(int k) {
-  if constexpr (C::M16) return swz_b<2>(k) ^ (8 * ((k >> 3) & 1));
-  else return swz_b<C::ES>(k);
+template <int ES, bool M16> __device__ inline int swz_wt(int k) {
+  if constexpr (M16) return swz_b<2>(k) ^ (8 * ((k >> 3) & 1));
+  else return swz_b<ES>(k);
 }
 // acc (one 16x16 sub-block of outputs) += weight fragment wf x activation
 // fragment af
@@ -265,6 +265,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
   using O = typename C::Out;
   constexpr int CE = C::CE, KC = C::KC, BK = C::BK, ES = C::ES, S = C::S;
   constexpr int AP = C::AP, KCA = C::KCA;
+  // 16x16x32 MFMAs in the ping-pong loop (see Cfg::M16_OK)
+  constexpr bool M16 = C::M16_OK && PINGPONG && C::THREADS == 512;
   constexpr int ST = AP == 1 ? C::A_STAGE + C::B_STAGE : C::B_STAGE;  // bytes of st0..st3
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -297,7 +299,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 #pragma unroll
   for (int i = 0; i < C::A_INST; ++i) {
     const int slot = i * C::THREADS + tid;
-    const int r = slot / KCA, c = (slot % KCA) ^ swz_act<C>(r);
+    const int r = slot / KCA, c = (slot % KCA) ^ swz_act<KCA, M16>(r);
     if (p.gather) {
       // rows past the group read zeros: an offset past the descriptor's range
       const int grow = row_lo + r;
@@ -314,7 +316,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
       // reads of one pass cover 256 contiguous bytes: no swizzle needed)
       b_off[i] = (slot / C::B_CPR) * Ncols * 8 + (slot % C::B_CPR) * 16;
     } else {
-      const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_wt<C>(k);
+      const int k = slot / C::B_CPR, c = (slot % C::B_CPR) ^ swz_wt<ES, M16>(k);
       b_off[i] = (k * Ncols + c * CE) * ES;
     }
   }
@@ -354,7 +356,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     };
 
     f32x16 acc[C::FN][FM];
-    if constexpr (!C::M16) {
+    if constexpr (!M16) {
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -364,8 +366,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     }
     // M16: the K loop's accumulators, 16x16 sub-block Q = 2a + b of each
     // 32x32 block (copied into acc[.][.][4Q .. 4Q+3] after the loop)
-    f32x4 acq[C::M16 ? C::FN : 1][C::M16 ? FM : 1][4];
-    if constexpr (C::M16) {
+    f32x4 acq[M16 ? C::FN : 1][M16 ? FM : 1][4];
+    if constexpr (M16) {
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -408,7 +410,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     int fa_off[KC / 2];
 #pragma unroll
     for (int ss = 0; ss < KC / 2; ++ss)
-      fa_off[ss] = (wm * WTM + lrow) * KCA * 16 + (((2 * ss + lhalf) ^ swz_act<C>(lrow)) * 16);
+      fa_off[ss] = (wm * WTM + lrow) * KCA * 16 + (((2 * ss + lhalf) ^ swz_act<KCA, M16>(lrow)) * 16);
     // 16x16x32 (M16): the activation fragment of m-half b of 32-row block j
     // is row wm*WTM + 32j + 16b + lane%16, chunk lane/16 (8 consecutive K),
     // at fa16 + (32j + 16b) rows; the weight fragment of n-half a of 32-column
@@ -416,16 +418,16 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
     // two transposing reads of 4 K-rows each from fw16[i][a] (in each 16-lane
     // group, lane 4q + r reads K-row q, columns 4r .. 4r+3 of the group's 16)
     const int l16 = lane & 15, g16 = lane >> 4;
-    const int fa16 = (wm * WTM + l16) * KCA * 16 + ((g16 ^ swz_act<C>(l16)) * 16);
-    int fw16[C::M16 ? C::FN : 1][2];
-    if constexpr (C::M16) {
+    const int fa16 = (wm * WTM + l16) * KCA * 16 + ((g16 ^ swz_act<KCA, M16>(l16)) * 16);
+    int fw16[M16 ? C::FN : 1][2];
+    if constexpr (M16) {
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
           const int k = 8 * g16 + (l16 >> 2);
           const int chunk = wn * C::WTN / 8 + 4 * i + 2 * a + ((l16 & 3) >> 1);
-          fw16[i][a] = k * C::B_CPR * 16 + ((chunk ^ swz_wt<C>(k)) * 16) + 8 * (l16 & 1);
+          fw16[i][a] = k * C::B_CPR * 16 + ((chunk ^ swz_wt<ES, M16>(k)) * 16) + 8 * (l16 & 1);
         }
     }
     // weight fragment, bf16: 16-lane group q, lane r in it: rows 16s + 8(q/2) + 4p + r/4,
@@ -445,7 +447,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 
     u32x4 fa[2][C::FN], fb[2][FM];
     auto load_frags = [&](const char* sa, const char* sb, int ss, int buf, int hi) {
-      if constexpr (C::M16) {
+      if constexpr (M16) {
         // half ss of the K-step's fragments: m-half ss of every row block,
         // n-half ss of every column block
 #pragma unroll
@@ -515,7 +517,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         for (int j = 0; j < FM; ++j) mfma16(acq[i][j][3], fa[1][i], fb[1][j]);
     };
     auto compute = [&](const char* sa, const char* sb, int hi) {
-      if constexpr (C::M16) {
+      if constexpr (M16) {
         load_frags(sa, sb, 0, 0, hi);
         load_frags(sa, sb, 1, 1, hi);
         mma16();
@@ -598,9 +600,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
               }
         }
       }
-      // (M16 takes the compiler's order: with these hints its fragments of
-      // both halves stayed live across the step and spilled)
-      if constexpr (ES == 2 && C::THREADS == 512 && !C::M16) {
+      if constexpr (ES == 2 && C::THREADS == 512 && !M16) {
         // (8-wave tiles) instruction order for the step: the first substep's LDS reads, then
         // each MFMA followed by one of the next substep's LDS reads and, after
         // every second MFMA, one of the step's global->LDS loads, so that the
@@ -671,7 +671,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
         __builtin_amdgcn_sched_barrier(0);
       };
       auto mma = [&]() {
-        if constexpr (C::M16) {
+        if constexpr (M16) {
           mma16();
         } else {
 #pragma unroll
@@ -749,7 +749,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = acc8[i][j];
     }
-    if constexpr (C::M16) {
+    if constexpr (M16) {
 #pragma unroll
       for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -777,8 +777,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           // M16: the lane's columns are 32i + 16q + 4(lane/16) .. +3 (q < 2)
-          if (C::M16 && q >= 2) continue;
-          const int off = (ccol0 + i * 32 + (C::M16 ? 16 * q + 4 * g16 : 8 * q + 4 * lhalf)) * ES;
+          if (M16 && q >= 2) continue;
+          const int off = (ccol0 + i * 32 + (M16 ? 16 * q + 4 * g16 : 8 * q + 4 * lhalf)) * ES;
           if constexpr (ES == 2) {
             const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0);
             bv[i][q] = u32x4{w[0], w[1], 0u, 0u};
@@ -829,8 +829,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
             // slice row and byte offset in it of acc[i][j][4q .. 4q+3]: M32
             // row lane%32, columns 32i + 8q + 4(lane/32); M16 (sub-block q =
             // 2a + b) row 16b + lane%16, columns 32i + 16a + 4(lane/16)
-            const int srow = C::M16 ? 16 * (q & 1) + l16 : lrow;
-            const int cb = (i * 32 + (C::M16 ? 16 * (q >> 1) + 4 * g16 : 8 * q + 4 * lhalf)) * OB;
+            const int srow = M16 ? 16 * (q & 1) + l16 : lrow;
+            const int cb = (i * 32 + (M16 ? 16 * (q >> 1) + 4 * g16 : 8 * q + 4 * lhalf)) * OB;
             float v[4];
   #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
@@ -870,7 +870,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
   #pragma unroll
             for (int q = 0; q < 4; ++q)
   #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][C::M16 ? q >> 1 : q], r);
+              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][M16 ? q >> 1 : q], r);
         }
         store_slice(static_cast<O*>(p.C2), j, frow);  // the pre-activation
         if (gelu) {
@@ -895,7 +895,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
   #pragma unroll
             for (int q = 0; q < 4; ++q)
   #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][C::M16 ? q >> 1 : q], r);
+              for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += chunk_elem<E>(bv[i][M16 ? q >> 1 : q], r);
         }
         if (gelu) {
   #pragma unroll
@@ -911,8 +911,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
             // slice row and byte offset in it of acc[i][j][4q .. 4q+3]: M32
             // row lane%32, columns 32i + 8q + 4(lane/32); M16 (sub-block q =
             // 2a + b) row 16b + lane%16, columns 32i + 16a + 4(lane/16)
-            const int srow = C::M16 ? 16 * (q & 1) + l16 : lrow;
-            const int cb = (i * 32 + (C::M16 ? 16 * (q >> 1) + 4 * g16 : 8 * q + 4 * lhalf)) * OB;
+            const int srow = M16 ? 16 * (q & 1) + l16 : lrow;
+            const int cb = (i * 32 + (M16 ? 16 * (q >> 1) + 4 * g16 : 8 * q + 4 * lhalf)) * OB;
             float v[4];
   #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
