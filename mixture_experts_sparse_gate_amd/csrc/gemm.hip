@@ -951,7 +951,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& p, bool gelu, char* 
   }
 }
 
-template <class C>
+template <class C, bool PINGPONG>
 __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p, const float* bscale) {
   constexpr int BM = C::BM, BN = C::BN;
   // one LDS object per stage, so that the compiler can tell a stage being
@@ -1049,7 +1049,7 @@ __global__ __launch_bounds__(C::THREADS) void grouped_gemm_kernel(GemmParams p, 
   const int row_hi = __builtin_amdgcn_readfirstlane(sched[2]);
   const int n0 = __builtin_amdgcn_readfirstlane(sched[3]);
   const bool tail_tile = __builtin_amdgcn_readfirstlane(sched[4]) != 0;
-  gemm_tile<C, false>(p, C::GELU, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0, tail_tile, bscale, [] {});
+  gemm_tile<C, PINGPONG>(p, C::GELU, st0, st1, st2, st3, sa0, sa1, g, row_lo, row_hi, n0, tail_tile, bscale, [] {});
 }
 
 // ---- the expert FFN (GEMM1 + GELU, then GEMM2) as one persistent launch.
@@ -1444,11 +1444,21 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s, LaunchEvents ev, const
   if (p.M <= 0 || ntiles <= 0) return hipSuccess;
   auto xcd_round = [](int64_t n) { return (n + kNumXcds - 1) / kNumXcds * kNumXcds; };
   const int64_t blocks = xcd_round(full_max * ntiles) + xcd_round(tail_max * ntiles);
-  if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, ev.start,
-                          ev.stop, 0, p, bscale);
-  else
-    hipLaunchKernelGGL(grouped_gemm_kernel<C>, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p, bscale);
+  auto launch = [&](auto kernel) {
+    if (ev.start || ev.stop)
+      hipExtLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, ev.start, ev.stop, 0, p, bscale);
+    else
+      hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(C::THREADS), 0, s, p, bscale);
+  };
+  // 256 x 256 bf16 tiles run the single-launch FFN's ping-pong K loop (with
+  // its 16x16x32 MFMAs) on long contractions, as that launch does
+  constexpr bool kCanPingPong = C::BM == 256 && C::ES == 2 && !C::W8 && C::THREADS == 512;
+  if constexpr (kCanPingPong) {
+    if ((p.K + C::BK - 1) / C::BK >= kPingPongMinSteps) launch(grouped_gemm_kernel<C, true>);
+    else launch(grouped_gemm_kernel<C, false>);
+  } else {
+    launch(grouped_gemm_kernel<C, false>);
+  }
   return hipGetLastError();
 }
 
