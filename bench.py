@@ -767,9 +767,14 @@ def _short(name: str) -> str:
     m = re.search(r"grouped_gemm_kernel.*?Cfg<([^>]*)>", name)
     if m:
         return "grouped_gemm_kernel<" + m.group(1) + ">"
+    m = re.search(r"CfgI(\w+?)EEELb([01])EEEvNS_10GemmParamsE", name)
+    if m:
+        # the Cfg's last flag: the dual (pre-activation and GELU) output; the
+        # kernel's flag: the ping-pong K loop
+        return ("grouped_gemm_kernel<" + m.group(1) + (", U and H" if m.group(1).endswith("Lb1") else "") +
+                (", ping-pong" if m.group(2) == "1" else "") + ">")
     m = re.search(r"CfgI(\w+?)EEEEEvNS_10GemmParamsE", name)
     if m:
-        # the Cfg's last flag: the dual (pre-activation and GELU) output
         return "grouped_gemm_kernel<" + m.group(1) + (", U and H" if m.group(1).endswith("Lb1") else "") + ">"
     m = re.search(r"fused_ffn_kernelINS0_3CfgI(\w+?)EEELb([01])ELb([01])EEEvNS0_8FusedFfnE", name)
     if m:
