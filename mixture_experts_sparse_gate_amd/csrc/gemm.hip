@@ -9,13 +9,14 @@
 // ("MoE稀疏计算加速技术解析与应用实践" §3.2).
 //
 // Design for gfx950:
-//  - The block computes a BM x BN tile of C. MFMA 16x16x32 (bf16 tiles with
-//    32-deep K-steps) or 32x32x16 (the others) is used in the transposed
-//    sense, D = B^T A^T: the weight tile is the MFMA's first operand and the
-//    activation rows its second, so each lane ends up with 4 consecutive
-//    output columns of one row (8- or 16-byte stores). Both shapes do the
-//    same flops per cycle; 16x16x32 spends less energy per flop, and the
-//    chip, held at its power cap by this loop, clocks higher with it.
+//  - The block computes a BM x BN tile of C. MFMA 16x16x32 (the ping-pong K
+//    loop of long bf16 contractions) or 32x32x16 (every other loop) is used
+//    in the transposed sense, D = B^T A^T: the weight tile is the MFMA's
+//    first operand and the activation rows its second, so each lane ends up
+//    with 4 consecutive output columns of one row (8- or 16-byte stores).
+//    Both shapes do the same flops per cycle; 16x16x32 spends less energy
+//    per flop, and the chip, held at its power cap by that loop, clocks
+//    higher with it.
 //  - Both tiles go global -> LDS with buffer_load_dwordx4 ... lds (no staging
 //    registers), as they lie in memory: activation rows K-contiguous, weight
 //    rows N-contiguous. The MFMA needs 8 consecutive K values of one weight
