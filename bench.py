@@ -561,10 +561,32 @@ def ffn_trace(args, dev, torch):
     buf = np.zeros(nbytes // 8, dtype=np.uint64)
     api._check(lib.moe_ffn_trace_read(buf.ctypes.data), "moe_ffn_trace_read", _lib.TRACE_LIB_PATH)
     rec = buf.reshape(-1, 8).astype(np.int64)
-    rec = rec[rec[:, 2] != 0]
-    if len(rec) == 0:
+    if not (rec[:, 2] != 0).any():
         print("no single-launch FFN ran (the layer takes the two grouped-GEMM launches)", file=sys.stderr)
         return 2
+    header = [f"command: {args.command}" if args.command else
+              f"command: python3 <repo>/bench.py --workload {spec.name} --ffn-trace --warmup {args.warmup} --steps {args.steps}",
+              "source: moe_ffn_trace_read on libmoe_gfx950_trace.so (MOE_FFN_TRACE), records of the last of "
+              f"{args.warmup + args.steps} back-to-back moe_forward calls"]
+    lines = summarize_ffn_trace(rec, spec, header)
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+    return 0
+
+
+def summarize_ffn_trace(rec, spec, header=()):
+    """Summary lines of the single-launch FFN's per-item trace records
+    (moe_ffn_trace_read layout, int64 [n, 8]; zero records unwritten): the
+    records of the highest launch number only, per XCD (items, mean duration
+    after the wait, mean clock, end of the last item), shader cycles per
+    K-step of full tiles, and the clock over the launch in 8 bins. Wall
+    clock: a 100 MHz counter; clock = shader cycles over wall time."""
+    import numpy as np
+
+    rec = rec[rec[:, 2] != 0]
     launch = rec[:, 5] >> 32
     rec = rec[launch == launch.max()]
     t0 = rec[:, 0].min()
@@ -575,10 +597,7 @@ def ffn_trace(args, dev, torch):
     span = end.max()
     busy = (end - wait_end).sum()
     nk = {1: (spec.d + 31) // 32, 2: (spec.h + 31) // 32}
-    lines = [f"command: {args.command}" if args.command else
-             f"command: python3 <repo>/bench.py --workload {spec.name} --ffn-trace --warmup {args.warmup} --steps {args.steps}",
-             "source: moe_ffn_trace_read on libmoe_gfx950_trace.so (MOE_FFN_TRACE), records of the last of "
-             f"{args.warmup + args.steps} back-to-back moe_forward calls",
+    lines = list(header) + [
              f"workload: {spec.name}",
              f"items: {len(rec)}; span {span:.1f} us; tile time / (256 CUs x span): {busy / (256 * span):.3f}",
              "per XCD: end of its last item (us); per kind: items x mean duration after the wait (us) @ mean clock (MHz)"]
@@ -607,12 +626,7 @@ def ffn_trace(args, dev, torch):
         if q.any():
             lines.append(f"  {a:7.0f}-{b:7.0f} us: {q.sum():4d} items, {mhz[q].mean():.0f} MHz, "
                          f"GEMM1 {(q & (kind == 1)).sum()}, GEMM2 {(q & (kind == 2)).sum()}")
-    text = "\n".join(lines) + "\n"
-    if args.out:
-        with open(args.out, "w") as f:
-            f.write(text)
-    print(text)
-    return 0
+    return lines
 
 
 def graph_ab(dev, torch):
